@@ -1,0 +1,324 @@
+"""Benchmark of the exact-attention hot path on one MI355X.
+
+One step runs every stage of the path once, on resident synthetic inputs:
+  * fa_fwd on the 2K-token causal bf16 workload (B=4, H=16, N=2048, d=128),
+  * fa_bwd on the same batch, consuming that forward's O and LSE,
+  * fa_decode on the KV-cache workload (B=64, H=32, L=8192, d=128).
+HIP events on the library's stream time each call inside the step.
+
+``value`` is the metric's first clause: attention forward+backward TFLOP/s on
+the 2K workload (4*B*H*N^2*d, halved for causal; backward 2.5x that), taken
+over the fwd and bwd calls inside the timed steps.  The decode leg of the same
+steps is reported as achieved HBM GB/s (K and V read once: 2*B*H*L*d*2 bytes).
+A sweep over N = 2K..16K (H=32, B=16384/N, causal) reports forward and
+backward TFLOP/s as the metric's range asks, and the oracle's CPU time on a
+bounded sample is reported as ``cpu_baseline``.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-sweep]
+                       [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 flop/clk)
+PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
+
+
+def fwd_flops(B, H, N, d, causal=True):
+    f = 4.0 * B * H * N * N * d
+    return f / 2 if causal else f
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+class Buffers:
+    """Resident inputs, outputs and workspaces for one step (raw pointers for the C ABI)."""
+
+    def __init__(self, torch, fa, W, dev):
+        self.w_tr = W.WORKLOADS["fwd_causal_bf16_b4h16n2048d128"]
+        self.w_dec = W.WORKLOADS["decode_bf16_b64h32l8192d128"]
+        t = self.w_tr
+        self.q, self.k, self.v, self.do = W.draw([(t.B, t.H, t.N, t.d)] * 4, t.seed, torch.bfloat16,
+                                                 device="cpu")
+        self.q, self.k, self.v, self.do = (x.to(dev) for x in (self.q, self.k, self.v, self.do))
+        self.o = torch.empty_like(self.q)
+        self.lse = torch.empty((t.B, t.H, t.N), dtype=torch.float32, device=dev)
+        self.dq = torch.empty_like(self.q)
+        self.dk = torch.empty_like(self.q)
+        self.dv = torch.empty_like(self.q)
+        self.bwd_ws_bytes = fa.fa_bwd_workspace_bytes(t.B, t.H, t.N, t.d)
+        self.bwd_ws = torch.empty((self.bwd_ws_bytes,), dtype=torch.uint8, device=dev)
+        dcfg = self.w_dec
+        self.dq_in, self.kc, self.vc = W.make_inputs(dcfg, dev)
+        self.do_out = torch.empty_like(self.dq_in)
+        self.dlse = torch.empty((dcfg.B, dcfg.H), dtype=torch.float32, device=dev)
+        self.splits = fa.fa_decode_num_splits(dcfg.B, dcfg.H, dcfg.N, dcfg.d)
+        self.dec_ws_bytes = fa.fa_decode_workspace_bytes(dcfg.B, dcfg.H, dcfg.N, dcfg.d, 0)
+        self.dec_ws = torch.empty((self.dec_ws_bytes,), dtype=torch.uint8, device=dev)
+
+
+def run_fwd(fa, b, stream):
+    t = b.w_tr
+    st = fa.fa_fwd(b.q.data_ptr(), b.k.data_ptr(), b.v.data_ptr(), b.o.data_ptr(), fa.FA_BF16,
+                   b.lse.data_ptr(), t.B, t.H, t.N, t.d, fa.FA_BF16, 1, t.scale, stream)
+    if st != fa.FA_OK:
+        raise RuntimeError(fa.fa_status_string(st))
+
+
+def run_bwd(fa, b, stream):
+    t = b.w_tr
+    st = fa.fa_bwd(b.q.data_ptr(), b.k.data_ptr(), b.v.data_ptr(), b.o.data_ptr(), fa.FA_BF16,
+                   b.lse.data_ptr(), b.do.data_ptr(), b.dq.data_ptr(), b.dk.data_ptr(), b.dv.data_ptr(),
+                   b.bwd_ws.data_ptr(), b.bwd_ws_bytes, t.B, t.H, t.N, t.d, fa.FA_BF16, 1, t.scale, stream)
+    if st != fa.FA_OK:
+        raise RuntimeError(fa.fa_status_string(st))
+
+
+def run_decode(fa, b, stream):
+    t = b.w_dec
+    st = fa.fa_decode(b.dq_in.data_ptr(), b.kc.data_ptr(), b.vc.data_ptr(), b.do_out.data_ptr(),
+                      b.dlse.data_ptr(), b.dec_ws.data_ptr(), b.dec_ws_bytes, t.B, t.H, t.N, t.d,
+                      fa.FA_BF16, 0, t.scale, stream)
+    if st != fa.FA_OK:
+        raise RuntimeError(fa.fa_status_string(st))
+
+
+def sweep(torch, fa, W, dev, iters=10):
+    """fwd and bwd TFLOP/s at N = 2K..16K, H = 32, B = 16384/N, causal bf16, d = 128."""
+    out = []
+    stream = torch.cuda.current_stream().cuda_stream
+    for N in (2048, 4096, 8192, 16384):
+        B, H, d = 16384 // N, 32, 128
+        scale = 1.0 / math.sqrt(d)
+        seed = 10 + int(math.log2(N // 1024))
+        q, k, v, do = W.draw([(B, H, N, d)] * 4, seed, torch.bfloat16, device=dev)
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+        nb = fa.fa_bwd_workspace_bytes(B, H, N, d)
+        ws = torch.empty((nb,), dtype=torch.uint8, device=dev)
+
+        def f():
+            fa.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), fa.FA_BF16, lse.data_ptr(),
+                      B, H, N, d, fa.FA_BF16, 1, scale, stream)
+
+        def g():
+            fa.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), fa.FA_BF16, lse.data_ptr(),
+                      do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr(), nb,
+                      B, H, N, d, fa.FA_BF16, 1, scale, stream)
+
+        res = {"N": N, "B": B, "H": H, "d": d}
+        for name, fn, mult in (("fwd", f, 1.0), ("bwd", g, 2.5)):
+            f()
+            fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(iters):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / iters
+            tf = mult * fwd_flops(B, H, N, d) / (ms * 1e-3) / 1e12
+            res[name] = {"ms": round(ms, 4), "tflops": round(tf, 1),
+                         "frac_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+        log(f"sweep N={N}: fwd {res['fwd']['tflops']} TFLOP/s, bwd {res['bwd']['tflops']} TFLOP/s")
+        out.append(res)
+        del q, k, v, do, o, lse, dq, dk, dv, ws
+        torch.cuda.empty_cache()
+    return out
+
+
+def cpu_baseline(W, heads=32):
+    """The fp64 oracle, as it stands, on a bounded sample of the 2K training workload."""
+    import numpy as np
+    import torch
+
+    from oracle import ref_bwd, ref_fwd
+    t = W.WORKLOADS["fwd_causal_bf16_b4h16n2048d128"]
+    q, k, v, do = W.draw([(t.B, t.H, t.N, t.d)] * 4, t.seed, torch.bfloat16, device="cpu")
+    # the first `heads` of the B*H heads, as a [1, heads, N, d] batch
+    q, k, v, do = (x.reshape(1, t.B * t.H, t.N, t.d)[:, :heads].float().numpy().astype(np.float64)
+                   for x in (q, k, v, do))
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+        info = threadpool_info()
+        threads = max((i.get("num_threads", 1) for i in info), default=None)
+    except Exception:
+        pass
+    t0 = time.perf_counter()
+    ref_fwd(q, k, v, True, t.scale)
+    ref_bwd(q, k, v, do, True, t.scale)
+    secs = time.perf_counter() - t0
+    flops = 3.5 * fwd_flops(1, heads, t.N, t.d)
+    return {
+        "value": round(flops / secs / 1e12, 5),
+        "unit": "TFLOP/s",
+        "cores": threads or os.cpu_count(),
+        "kind": "oracle",
+        "sample": f"oracle ref_fwd + ref_bwd (fp64, full N x N scores) on {heads} of the 64 heads of "
+                  f"B4 H16 N2048 d128 causal; {secs:.2f} s; rate uses the same causal flop count as the GPU",
+        "seconds": round(secs, 3),
+        "affinity_cores": len(os.sched_getaffinity(0)),
+    }
+
+
+def traffic_record(kernel_key):
+    """HBM bytes per launch measured with rocprofv3 counters, if still valid for this source."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except OSError:
+        return None
+    ent = rec.get(kernel_key)
+    if not ent:
+        return None
+    import hashlib
+    src = os.path.join(ROOT, "exact_io_aware_11_amd", "csrc", ent["source"])
+    try:
+        h = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    return ent["bytes_per_launch"] if h == ent.get("source_sha256") else None
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(every (batch, head) is independent; see the sharding notes in DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import exact_io_aware_11_amd as fa
+    import fa_workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    b = Buffers(torch, fa, W, dev)
+    stream = torch.cuda.current_stream().cuda_stream
+    stages = {"fwd": run_fwd, "bwd": run_bwd, "decode": run_decode}
+    active = list(stages)
+
+    log(f"warmup {args.warmup} steps ({', '.join(active)})")
+    for _ in range(args.warmup):
+        for name in active:
+            stages[name](fa, b, stream)
+    torch.cuda.synchronize()
+
+    ev = {n: [] for n in active}
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        for name in active:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            stages[name](fa, b, stream)
+            e1.record()
+            ev[name].append((e0, e1))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = {n: sum(a.elapsed_time(c) for a, c in ev[n]) / args.steps for n in active}
+    log("per-call ms: " + ", ".join(f"{n} {ms[n]:.4f}" for n in active))
+
+    t, dc = b.w_tr, b.w_dec
+    f_fwd = fwd_flops(t.B, t.H, t.N, t.d)
+    f_bwd = 2.5 * f_fwd
+    dec_bytes = 2.0 * dc.B * dc.H * dc.N * dc.d * 2
+    parts = {}
+    roofs = []
+    if "fwd" in ms:
+        tf = f_fwd / (ms["fwd"] * 1e-3) / 1e12
+        parts["fwd"] = {"ms": round(ms["fwd"], 4), "tflops": round(tf, 1)}
+        roofs.append({"kernel": "fwd_bf16_kernel<128,causal>", "bound": "mfma", "achieved": round(tf, 1),
+                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                      "traffic": traffic_record("fwd"), "ms": ms["fwd"],
+                      "per_launch": f"{f_fwd:.4g} flop (4*B*H*N^2*d/2 at B4 H16 N2048 d128)"})
+    if "bwd" in ms:
+        tf = f_bwd / (ms["bwd"] * 1e-3) / 1e12
+        parts["bwd"] = {"ms": round(ms["bwd"], 4), "tflops": round(tf, 1)}
+        roofs.append({"kernel": "fa_bwd (prep + bwd_main_kernel<128,causal> + dq convert)", "bound": "mfma",
+                      "achieved": round(tf, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                      "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": traffic_record("bwd"),
+                      "ms": ms["bwd"], "per_launch": f"{f_bwd:.4g} flop (2.5x forward)"})
+    if "decode" in ms:
+        gbs = dec_bytes / (ms["decode"] * 1e-3) / 1e9
+        parts["decode"] = {"ms": round(ms["decode"], 4), "GBps": round(gbs, 1), "splits": b.splits}
+        roofs.append({"kernel": "fa_decode (decode_split_kernel<128> + merge)", "bound": "hbm",
+                      "achieved": round(gbs, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                      "frac": round(gbs / PEAK_HBM_GBPS, 4), "traffic": traffic_record("decode"),
+                      "ms": ms["decode"], "per_launch": f"{dec_bytes:.4g} B (K and V caches read once)"})
+    dominant = max(roofs, key=lambda r: r["ms"])
+
+    tr_ms = ms.get("fwd", 0.0) + ms.get("bwd", 0.0)
+    tr_flops = (f_fwd if "fwd" in ms else 0.0) + (f_bwd if "bwd" in ms else 0.0)
+    value = tr_flops / (tr_ms * 1e-3) / 1e12 if tr_ms > 0 else 0.0
+
+    sweep_res = None
+    if not args.no_sweep:
+        log("sweep N=2K..16K")
+        sweep_res = sweep(torch, fa, W, dev)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        cpu = cpu_baseline(W)
+
+    line = {
+        "metric": "attn fwd/bwd TFLOP/s bf16 causal (N=2K–16K) + % MFMA peak; decode HBM GB/s",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "attention step: fa_fwd + fa_bwd on causal B4 H16 N2048 d128, "
+                               "then fa_decode on B64 H32 L8192 d128",
+                   "B": t.B, "H": t.H, "N": t.N, "d": t.d, "causal": True,
+                   "decode": {"B": dc.B, "H": dc.H, "L": dc.N, "d": dc.d, "splits": b.splits}},
+        "value_basis": "fwd+bwd flops / fwd+bwd event time inside the timed steps",
+        "frac_mfma_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "parts": parts,
+        "roofline": {k: dominant[k] for k in ("bound", "achieved", "peak", "unit", "frac", "traffic")}
+                    | {"kernel": dominant["kernel"]},
+        "rooflines": roofs,
+        "sweep": sweep_res,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

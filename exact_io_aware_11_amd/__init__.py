@@ -1,0 +1,213 @@
+"""Python binding of the exact IO-aware attention library (``libfa.so``).
+
+Argument marshalling only: every step of forward, backward and decode runs in
+the HIP kernels behind the C ABI of ``include/fa.h``.  PyTorch is used for two
+things, device memory (``torch.empty``) and the current HIP stream.  There is
+no fallback: if the library is missing, importing this package fails.
+
+Entry points with the C names (raw pointers, sizes, stream handle):
+``fa_fwd``, ``fa_bwd``, ``fa_bwd_workspace_bytes``, ``fa_decode``,
+``fa_decode_workspace_bytes``, ``fa_decode_num_splits``, ``fa_status_string``.
+
+Tensor-level helpers with the same semantics:
+``attention(q, k, v, is_causal=False, scale=None, out_dtype=None) -> (o, lse)``
+(the call shape of PyTorch's scaled_dot_product_attention that the pages show),
+``attention_backward(q, k, v, o, lse, do, is_causal=False, scale=None)``
+``-> (dq, dk, dv)`` and ``decode(q, k_cache, v_cache, scale=None,
+num_splits=0) -> (o, lse)``.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+__all__ = [
+    "LIB_PATH", "FA_OK", "FA_ERR_NULL", "FA_ERR_ARG", "FA_ERR_UNSUPPORTED", "FA_ERR_ALIGN",
+    "FA_ERR_WORKSPACE", "FA_ERR_HIP", "FA_FP32", "FA_BF16", "FaError",
+    "fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_decode", "fa_decode_workspace_bytes",
+    "fa_decode_num_splits", "fa_status_string",
+    "attention", "attention_backward", "decode", "lib",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
+
+FA_OK, FA_ERR_NULL, FA_ERR_ARG, FA_ERR_UNSUPPORTED, FA_ERR_ALIGN, FA_ERR_WORKSPACE, FA_ERR_HIP = range(7)
+FA_FP32, FA_BF16 = 0, 1
+
+
+class FaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {fa_status_string(status)}")
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it first (python -m exact_io_aware_11_amd.build). "
+            "There is no fallback implementation.")
+    lib_ = ctypes.CDLL(LIB_PATH)
+    P, I, F, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib_.fa_fwd.argtypes = [P, P, P, P, I, P, I, I, I, I, I, I, F, P]
+    lib_.fa_fwd.restype = I
+    lib_.fa_bwd_workspace_bytes.argtypes = [I, I, I, I]
+    lib_.fa_bwd_workspace_bytes.restype = Z
+    lib_.fa_bwd.argtypes = [P, P, P, P, I, P, P, P, P, P, P, Z, I, I, I, I, I, I, F, P]
+    lib_.fa_bwd.restype = I
+    lib_.fa_decode_num_splits.argtypes = [I, I, I, I]
+    lib_.fa_decode_num_splits.restype = I
+    lib_.fa_decode_workspace_bytes.argtypes = [I, I, I, I, I]
+    lib_.fa_decode_workspace_bytes.restype = Z
+    lib_.fa_decode.argtypes = [P, P, P, P, P, P, Z, I, I, I, I, I, I, F, P]
+    lib_.fa_decode.restype = I
+    lib_.fa_status_string.argtypes = [I]
+    lib_.fa_status_string.restype = ctypes.c_char_p
+    return lib_
+
+
+lib = _load()
+
+# ----------------------------------------------------------------------------
+# C-named entry points (plain integers for pointers and the stream)
+# ----------------------------------------------------------------------------
+
+
+def fa_status_string(status: int) -> str:
+    return lib.fa_status_string(int(status)).decode()
+
+
+def fa_fwd(q, k, v, o, o_dtype, lse, B, H, N, d, in_dtype, causal, scale, stream=0) -> int:
+    return lib.fa_fwd(q, k, v, o, o_dtype, lse, B, H, N, d, in_dtype, int(causal), scale, stream)
+
+
+def fa_bwd_workspace_bytes(B, H, N, d) -> int:
+    return lib.fa_bwd_workspace_bytes(B, H, N, d)
+
+
+def fa_bwd(q, k, v, o, o_dtype, lse, dout, dq, dk, dv, workspace, workspace_bytes,
+           B, H, N, d, in_dtype, causal, scale, stream=0) -> int:
+    return lib.fa_bwd(q, k, v, o, o_dtype, lse, dout, dq, dk, dv, workspace, workspace_bytes,
+                      B, H, N, d, in_dtype, int(causal), scale, stream)
+
+
+def fa_decode_num_splits(B, H, L, d) -> int:
+    return lib.fa_decode_num_splits(B, H, L, d)
+
+
+def fa_decode_workspace_bytes(B, H, L, d, num_splits=0) -> int:
+    return lib.fa_decode_workspace_bytes(B, H, L, d, num_splits)
+
+
+def fa_decode(q, k_cache, v_cache, o, lse, workspace, workspace_bytes, B, H, L, d, dtype,
+              num_splits, scale, stream=0) -> int:
+    return lib.fa_decode(q, k_cache, v_cache, o, lse, workspace, workspace_bytes, B, H, L, d,
+                         dtype, num_splits, scale, stream)
+
+
+# ----------------------------------------------------------------------------
+# tensor helpers (torch: allocation and stream only)
+# ----------------------------------------------------------------------------
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return FA_BF16
+    if t.dtype == torch.float32:
+        return FA_FP32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _check(t, name, shape=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _stream(t) -> int:
+    torch = _torch()
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _raise(status: int, where: str):
+    if status != FA_OK:
+        raise FaError(status, where)
+
+
+def attention(q, k, v, is_causal: bool = False, scale: float | None = None, out_dtype=None):
+    """O = softmax(scale Q K^T [causal]) V and the per-row LSE, via ``fa_fwd``.
+
+    q, k, v: contiguous [B,H,N,d] bf16 or fp32 GPU tensors.  Returns
+    (o [B,H,N,d] of ``out_dtype`` (default: q's dtype), lse [B,H,N] fp32).
+    """
+    torch = _torch()
+    _check(q, "q")
+    B, H, N, d = q.shape
+    _check(k, "k", q.shape)
+    _check(v, "v", q.shape)
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k and v must share a dtype")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    o = torch.empty((B, H, N, d), dtype=out_dtype, device=q.device)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    st = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), _dtype_code(o), lse.data_ptr(),
+                B, H, N, d, _dtype_code(q), is_causal, scale, _stream(q))
+    _raise(st, "fa_fwd")
+    return o, lse
+
+
+def attention_backward(q, k, v, o, lse, do, is_causal: bool = False, scale: float | None = None):
+    """dQ, dK, dV of ``attention`` by recomputation from (q, k, v, o, lse), via ``fa_bwd``."""
+    torch = _torch()
+    _check(q, "q")
+    B, H, N, d = q.shape
+    for t, n in ((k, "k"), (v, "v"), (o, "o"), (do, "do")):
+        _check(t, n, q.shape)
+    _check(lse, "lse", (B, H, N))
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    nbytes = fa_bwd_workspace_bytes(B, H, N, d)
+    ws = torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=q.device)
+    st = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), _dtype_code(o), lse.data_ptr(),
+                do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr(), nbytes,
+                B, H, N, d, _dtype_code(q), is_causal, scale, _stream(q))
+    _raise(st, "fa_bwd")
+    return dq, dk, dv
+
+
+def decode(q, k_cache, v_cache, scale: float | None = None, num_splits: int = 0):
+    """One decode step: q [B,H,1,d] against caches [B,H,L,d] (bf16), via ``fa_decode``.
+
+    Returns (o [B,H,1,d] bf16, lse [B,H] fp32).
+    """
+    torch = _torch()
+    _check(q, "q")
+    B, H, one, d = q.shape
+    if one != 1:
+        raise ValueError("decode takes one query token per (batch, head)")
+    _check(k_cache, "k_cache")
+    L = k_cache.shape[2]
+    _check(k_cache, "k_cache", (B, H, L, d))
+    _check(v_cache, "v_cache", (B, H, L, d))
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    o = torch.empty((B, H, 1, d), dtype=q.dtype, device=q.device)
+    lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    nbytes = fa_decode_workspace_bytes(B, H, L, d, num_splits)
+    ws = torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=q.device)
+    st = fa_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                   ws.data_ptr(), nbytes, B, H, L, d, _dtype_code(q), num_splits, scale, _stream(q))
+    _raise(st, "fa_decode")
+    return o, lse

@@ -1,0 +1,152 @@
+// fa_api.cpp -- the C ABI declared in include/fa.h: argument validation,
+// workspace sizing and dispatch to the kernel launchers.  Nothing is enqueued
+// unless every check passes.
+#include "fa.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "fa_internal.hpp"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool dims_ok(int B, int H, int N) { return B >= 1 && H >= 1 && N >= 1; }
+
+bool head_dim_ok(int d) { return d == 64 || d == 128; }
+
+bool scale_ok(float s) { return std::isfinite(s) && s > 0.f; }
+
+// B*H*N*d must fit the 64-bit byte arithmetic used everywhere, and B*H*N the
+// 32-bit row indices of the kernels.
+bool total_ok(int B, int H, int N, int d) {
+    const long long rows = (long long)B * H * N;
+    return rows <= 0x7fffffffLL && rows * d <= (1LL << 50);
+}
+
+fa_status_t from_hip(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
+
+constexpr int kMaxSplits = 256;
+
+int auto_splits(int B, int H, int L) {
+    // Aim for at least ~4096 workgroups so every CU holds several, but keep
+    // each split at 512 keys or more so the merge stays negligible.
+    const long long bh = (long long)B * H;
+    long long s = (4096 + bh - 1) / bh;
+    const long long max_by_len = (L + 511) / 512;
+    if (s > max_by_len) s = max_by_len;
+    if (s > kMaxSplits) s = kMaxSplits;
+    if (s < 1) s = 1;
+    return (int)s;
+}
+
+// Effective split count: chunks of ceil(L/S) keys, with no empty chunk.
+void split_plan(int L, int requested, int& splits, int& chunk) {
+    chunk = (L + requested - 1) / requested;
+    splits = (L + chunk - 1) / chunk;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fa_status_string(fa_status_t s) {
+    switch (s) {
+        case FA_OK: return "FA_OK";
+        case FA_ERR_NULL: return "FA_ERR_NULL: a required pointer is NULL";
+        case FA_ERR_ARG: return "FA_ERR_ARG: a size is < 1, too large, or scale is not finite and positive";
+        case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: dtype / head-dim combination not built";
+        case FA_ERR_ALIGN: return "FA_ERR_ALIGN: a pointer is not 16-byte aligned";
+        case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace missing or too small";
+        case FA_ERR_HIP: return "FA_ERR_HIP: the HIP runtime reported an error";
+    }
+    return "unknown fa_status_t";
+}
+
+fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, fa_dtype_t o_dtype, float* lse,
+                   int B, int H, int N, int d, fa_dtype_t in_dtype, int causal, float scale, void* stream) {
+    if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+    if (!dims_ok(B, H, N) || !scale_ok(scale) || !total_ok(B, H, N, d)) return FA_ERR_ARG;
+    if (!head_dim_ok(d)) return FA_ERR_UNSUPPORTED;
+    if (in_dtype != FA_BF16 && in_dtype != FA_FP32) return FA_ERR_UNSUPPORTED;
+    if (o_dtype != FA_BF16 && o_dtype != FA_FP32) return FA_ERR_UNSUPPORTED;
+    if (in_dtype == FA_FP32 && o_dtype != FA_FP32) return FA_ERR_UNSUPPORTED;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return FA_ERR_ALIGN;
+    fa::FwdArgs a{q, k, v, o, lse, B, H, N, d, in_dtype == FA_BF16, o_dtype == FA_BF16, causal != 0, scale, stream};
+    return from_hip(fa::launch_fwd(a));
+}
+
+size_t fa_bwd_workspace_bytes(int B, int H, int N, int d) {
+    if (!dims_ok(B, H, N) || d < 1 || !total_ok(B, H, N, d)) return 0;
+    const size_t rows = (size_t)B * H * N;
+    const size_t acc = rows * (size_t)d * sizeof(float);
+    const size_t delta = rows * sizeof(float);
+    return ((acc + 255) & ~(size_t)255) + delta;
+}
+
+fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, fa_dtype_t o_dtype,
+                   const float* lse, const void* dout, void* dq, void* dk, void* dv, void* workspace,
+                   size_t workspace_bytes, int B, int H, int N, int d, fa_dtype_t in_dtype, int causal,
+                   float scale, void* stream) {
+    if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_NULL;
+    if (!dims_ok(B, H, N) || !scale_ok(scale) || !total_ok(B, H, N, d)) return FA_ERR_ARG;
+    if (!head_dim_ok(d) || in_dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+    if (o_dtype != FA_BF16 && o_dtype != FA_FP32) return FA_ERR_UNSUPPORTED;
+    const void* ptrs[] = {q, k, v, o, lse, dout, dq, dk, dv};
+    for (const void* p : ptrs)
+        if (!aligned16(p)) return FA_ERR_ALIGN;
+    const size_t need = fa_bwd_workspace_bytes(B, H, N, d);
+    if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return FA_ERR_ALIGN;
+    const size_t rows = (size_t)B * H * N;
+    float* acc = static_cast<float*>(workspace);
+    float* delta = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                            (((rows * (size_t)d * sizeof(float)) + 255) & ~(size_t)255));
+    fa::BwdArgs a{q, k, v, o, lse, dout, dq, dk, dv, acc, delta, B, H, N, d, o_dtype == FA_BF16, causal != 0,
+                  scale, stream};
+    return from_hip(fa::launch_bwd(a));
+}
+
+int fa_decode_num_splits(int B, int H, int L, int d) {
+    (void)d;
+    if (!dims_ok(B, H, L)) return 1;
+    int splits, chunk;
+    split_plan(L, auto_splits(B, H, L), splits, chunk);
+    return splits;
+}
+
+size_t fa_decode_workspace_bytes(int B, int H, int L, int d, int num_splits) {
+    if (!dims_ok(B, H, L) || d < 1 || num_splits < 0 || !total_ok(B, H, L, d)) return 0;
+    int splits, chunk;
+    split_plan(L, num_splits == 0 ? auto_splits(B, H, L) : (num_splits > L ? L : num_splits), splits, chunk);
+    const size_t parts = (size_t)B * H * splits;
+    const size_t o_bytes = parts * (size_t)d * sizeof(float);
+    return ((o_bytes + 255) & ~(size_t)255) + parts * sizeof(float);
+}
+
+fa_status_t fa_decode(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                      void* workspace, size_t workspace_bytes, int B, int H, int L, int d, fa_dtype_t dtype,
+                      int num_splits, float scale, void* stream) {
+    if (!q || !k_cache || !v_cache || !o) return FA_ERR_NULL;
+    if (!dims_ok(B, H, L) || !scale_ok(scale) || num_splits < 0 || num_splits > L || !total_ok(B, H, L, d))
+        return FA_ERR_ARG;
+    if (!head_dim_ok(d) || dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o)) return FA_ERR_ALIGN;
+    if (lse && !aligned16(lse)) return FA_ERR_ALIGN;
+    const size_t need = fa_decode_workspace_bytes(B, H, L, d, num_splits);
+    if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return FA_ERR_ALIGN;
+    int splits, chunk;
+    split_plan(L, num_splits == 0 ? auto_splits(B, H, L) : num_splits, splits, chunk);
+    const size_t parts = (size_t)B * H * splits;
+    float* o_part = static_cast<float*>(workspace);
+    float* lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                               (((parts * (size_t)d * sizeof(float)) + 255) & ~(size_t)255));
+    fa::DecodeArgs a{q, k_cache, v_cache, o, lse, o_part, lse_part, B, H, L, d, splits, chunk, scale, stream};
+    return from_hip(fa::launch_decode(a));
+}
+
+}  // extern "C"

@@ -1,0 +1,114 @@
+// fa_common.hpp -- gfx950 building blocks shared by the attention kernels.
+//
+// MFMA operand conventions used throughout (wave64, v_mfma_f32_32x32x16_bf16
+// and v_mfma_f32_32x32x2_f32):
+//   lane l, i32 = l % 32, g = l / 32
+//   A operand (M x K):  lane l holds row i32 and K-slots (g, j), j < 8 (bf16)
+//                       or the single K-slot g (fp32).
+//   B operand (K x N):  lane l holds column i32 and the same K-slots.
+//   C/D (32 x 32 fp32): lane l, register r holds C[8*(r/4) + 4*g + r%4][i32].
+// A contraction is correct for any assignment of real indices to K-slots as
+// long as the A and B operands use the same one; the kernels exploit that to
+// feed a C accumulator straight back in as a B operand without shuffles.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ f32x16 mfma_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 mfma_f32(float a, float b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+// 2^x on the transcendental unit (v_exp_f32); exp2(-inf) = 0.
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ f32x16 zero16() {
+    f32x16 z;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) z[i] = 0.f;
+    return z;
+}
+
+// Round-to-nearest-even fp32 -> bf16 pair (v_cvt_pk_bf16_f32), packed in 32 bits.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    bf16x2 v = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte streaming load (nontemporal: the data is used once).
+__device__ __forceinline__ uint4 load_stream16(const void* p) {
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+// Eight packed bf16 (one 16-byte chunk) -> one MFMA operand.
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
+
+// Element c (0..7) of four 16-byte rows r0..r3, packed as 4 x bf16 (one 8-byte
+// store of a transposed tile row).
+__device__ __forceinline__ uint2 column4(const uint4& r0, const uint4& r1, const uint4& r2,
+                                         const uint4& r3, int c) {
+    const uint32_t* a = reinterpret_cast<const uint32_t*>(&r0);
+    const uint32_t* b = reinterpret_cast<const uint32_t*>(&r1);
+    const uint32_t* e = reinterpret_cast<const uint32_t*>(&r2);
+    const uint32_t* f = reinterpret_cast<const uint32_t*>(&r3);
+    const int wi = c >> 1;
+    uint32_t lo, hi;
+    if (c & 1) {
+        lo = (a[wi] >> 16) | (b[wi] & 0xffff0000u);
+        hi = (e[wi] >> 16) | (f[wi] & 0xffff0000u);
+    } else {
+        lo = (a[wi] & 0xffffu) | (b[wi] << 16);
+        hi = (e[wi] & 0xffffu) | (f[wi] << 16);
+    }
+    return make_uint2(lo, hi);
+}
+
+// Position of key (or query) k inside a transposed tile row, for the
+// permutation that lets a 32x32 C accumulator be used directly as a
+// K-slot-ordered B operand: within each group of 16, the 4-element quads are
+// stored in the order 0, 2, 1, 3.
+__device__ __forceinline__ int perm16(int k) {
+    const int quad = (k >> 2) & 3;
+    const int pq = (quad == 1) ? 2 : (quad == 2 ? 1 : quad);
+    return (k & ~15) | (pq << 2) | (k & 3);
+}
+
+// Full-wave butterfly over lanes l and l ^ 32 (ds_bpermute).
+__device__ __forceinline__ float xor32_max(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
+__device__ __forceinline__ float xor32_sum(float x) { return x + __shfl_xor(x, 32); }
+
+// DPP sums inside a row of 16 lanes (quad_perm, half-mirror, mirror).
+__device__ __forceinline__ float dpp_sum8(float v) {
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));  // [1,0,3,2]
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true));  // [2,3,0,1]
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, true)); // half mirror
+    return v;
+}
+__device__ __forceinline__ float dpp_sum16(float v) {
+    v = dpp_sum8(v);
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, true)); // row mirror
+    return v;
+}
+
+}  // namespace fa

@@ -1,0 +1,62 @@
+// fa_internal.hpp -- host-side launch interface between the C ABI layer and
+// the kernel translation units.  Arguments here are already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace fa {
+
+struct FwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    float* lse;
+    int B, H, N, d;
+    bool in_bf16;    // false: fp32 inputs
+    bool out_bf16;   // O element type
+    bool causal;
+    float scale;
+    void* stream;
+};
+
+struct BwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* o;
+    const float* lse;
+    const void* dout;
+    void* dq;
+    void* dk;
+    void* dv;
+    float* dq_acc;   // workspace: [B,H,N,d] fp32
+    float* delta;    // workspace: [B,H,N] fp32, rowsum(dO * O)
+    int B, H, N, d;
+    bool o_bf16;
+    bool causal;
+    float scale;
+    void* stream;
+};
+
+struct DecodeArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    float* lse;      // may be null
+    float* o_part;   // workspace: [B,H,S,d] fp32
+    float* lse_part; // workspace: [B,H,S] fp32
+    int B, H, L, d;
+    int splits;      // S >= 1, every split non-empty
+    int chunk;       // keys per split
+    float scale;
+    void* stream;
+};
+
+hipError_t launch_fwd(const FwdArgs& a);
+hipError_t launch_bwd(const BwdArgs& a);
+hipError_t launch_decode(const DecodeArgs& a);
+
+}  // namespace fa

@@ -1,0 +1,152 @@
+/*
+ * fa.h -- C ABI of the exact IO-aware attention library for MI355X (gfx950).
+ *
+ * The operation is exact scaled-dot-product attention,
+ *     O = softmax(scale * Q K^T [+ causal mask]) V,
+ * the formula displayed in the problem section of the page "FlashAttention
+ * (EL)".  It is computed tile by tile with an online softmax (running maximum
+ * and running sum of exponentials: same page, section on online softmax;
+ * "Flash Attention: Ako transformery zvladaju miliony tokenov", section 2), so
+ * the N x N score matrix never reaches device memory.  The backward pass
+ * recomputes the scores from a saved per-row log-sum-exp instead of storing
+ * them ("Flash Attention uitgelegd", section "Recomputation").
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every tensor pointer is a DEVICE pointer owned by the caller.  The
+ *    library never allocates, frees or synchronises, and keeps no per-call
+ *    state; it enqueues kernels on `stream` (a hipStream_t, NULL = the
+ *    default stream) and returns at once.
+ *  - Tensors are dense, row-major, [B, H, N, d] (d fastest).  LSE tensors
+ *    are [B, H, N] float32 and hold the natural-log log-sum-exp of the
+ *    scaled, masked scores of each query row.
+ *  - `scale` multiplies Q K^T; the pages' value is 1/sqrt(d).  It must be
+ *    finite and > 0 (FA_ERR_ARG otherwise).
+ *  - Causal masking (the decoder-only variant: Slovak page, section 5, and
+ *    its is_causal usage example in section 6): key j is visible to query i
+ *    iff j <= i (top-left aligned).
+ *  - Supported: head dimension d in {64, 128}; any N >= 1 (ragged tails are
+ *    masked inside the kernels); all offsets are 64-bit.
+ *  - Every pointer must be 16-byte aligned.
+ *  - Errors: arguments are validated before anything is enqueued; on error
+ *    nothing is launched and the status says why.  A failed launch returns
+ *    FA_ERR_HIP.  Kernel faults surface at the caller's next synchronisation,
+ *    as for any asynchronous HIP call.
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    FA_OK = 0,
+    FA_ERR_NULL = 1,        /* a required pointer is NULL                      */
+    FA_ERR_ARG = 2,         /* a size is < 1, or scale is not finite           */
+    FA_ERR_UNSUPPORTED = 3, /* a dtype / head-dim combination not built        */
+    FA_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned                */
+    FA_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required      */
+    FA_ERR_HIP = 6          /* the HIP runtime reported an error at launch     */
+} fa_status_t;
+
+typedef enum {
+    FA_FP32 = 0,            /* IEEE binary32                                   */
+    FA_BF16 = 1             /* bfloat16 (rounded to nearest even on output)    */
+} fa_dtype_t;
+
+/*
+ * fa_fwd -- forward pass: O and the per-row LSE.
+ *
+ * Computes O = softmax(scale Q K^T [causal]) V and LSE_i = ln sum_j
+ * exp(scale q_i.k_j) over visible j ("FlashAttention (EL)", displayed formula
+ * of the problem section; all operations fused in one kernel as its section
+ * on fusing operations describes).  Uses no workspace: memory beyond the
+ * outputs is O(1) in N.
+ *
+ *   q, k, v   [B,H,N,d] of in_dtype (FA_BF16: bf16 MFMA with fp32
+ *             accumulation; FA_FP32: fp32 MFMA).
+ *   o         [B,H,N,d] of o_dtype.  in_dtype FA_BF16 allows o_dtype FA_BF16
+ *             or FA_FP32; in_dtype FA_FP32 requires o_dtype FA_FP32.
+ *   lse       [B,H,N] float32, natural log; never NULL (backward needs it).
+ */
+fa_status_t fa_fwd(const void* q, const void* k, const void* v,
+                   void* o, fa_dtype_t o_dtype, float* lse,
+                   int B, int H, int N, int d, fa_dtype_t in_dtype,
+                   int causal, float scale, void* stream);
+
+/*
+ * fa_bwd_workspace_bytes -- bytes of workspace fa_bwd needs: an fp32 dQ
+ * accumulator [B,H,N,d] plus the fp32 row statistic D = rowsum(dO * O)
+ * [B,H,N].  Returns 0 if a size is < 1 or the total overflows.
+ */
+size_t fa_bwd_workspace_bytes(int B, int H, int N, int d);
+
+/*
+ * fa_bwd -- backward pass with recomputation ("Flash Attention uitgelegd",
+ * section "Recomputation"; Slovak page, section 2): the scores and
+ * probabilities are recomputed tile by tile from Q, K and the saved LSE; the
+ * gradients are the chain rule through the forward definition:
+ *     dV = P^T dO,  dP = dO V^T,  D_i = sum_k dO_ik O_ik,
+ *     dS = P * (dP - D),  dQ = scale dS K,  dK = scale dS^T Q.
+ *
+ *   q, k, v, dout  [B,H,N,d] bf16 (in_dtype must be FA_BF16).
+ *   o              [B,H,N,d] of o_dtype (FA_BF16 or FA_FP32), from fa_fwd.
+ *   lse            [B,H,N] float32, from fa_fwd with the same causal/scale.
+ *   dq, dk, dv     [B,H,N,d] bf16 outputs (fp32 accumulation inside).
+ *   workspace      device memory of at least fa_bwd_workspace_bytes(); its
+ *                  contents on entry do not matter and are clobbered.
+ */
+fa_status_t fa_bwd(const void* q, const void* k, const void* v,
+                   const void* o, fa_dtype_t o_dtype, const float* lse,
+                   const void* dout, void* dq, void* dk, void* dv,
+                   void* workspace, size_t workspace_bytes,
+                   int B, int H, int N, int d, fa_dtype_t in_dtype,
+                   int causal, float scale, void* stream);
+
+/*
+ * fa_decode_num_splits -- the split count fa_decode uses when called with
+ * num_splits = 0 for this shape (always >= 1 and <= L).
+ */
+int fa_decode_num_splits(int B, int H, int L, int d);
+
+/*
+ * fa_decode_workspace_bytes -- workspace of fa_decode: fp32 partial outputs
+ * [B,H,S,d] and partial LSEs [B,H,S] for S splits (num_splits = 0 means the
+ * library's choice).  Returns 0 if a size is < 1.
+ */
+size_t fa_decode_workspace_bytes(int B, int H, int L, int d, int num_splits);
+
+/*
+ * fa_decode -- one generation step against a KV cache (the cache the
+ * attention-backend page describes): one query token per (b, h) attends to
+ * all L cached keys, no mask.  The cache is cut into S contiguous chunks;
+ * each chunk's (o_s, lse_s) is computed with the online softmax and the
+ * chunks are merged with the same max-and-rescale rule applied to whole
+ * chunks:  M = max_s lse_s,  lse = M + ln sum_s exp(lse_s - M),
+ *          O = sum_s exp(lse_s - lse) o_s.
+ *
+ *   q                 [B,H,1,d] bf16 (dtype must be FA_BF16).
+ *   k_cache, v_cache  [B,H,L,d] bf16, contiguous.
+ *   o                 [B,H,1,d] bf16 output.
+ *   lse               [B,H] float32 output, or NULL if not wanted.
+ *   workspace         at least fa_decode_workspace_bytes(B,H,L,d,num_splits).
+ *   num_splits        0 = library's choice, else 1..L.
+ */
+fa_status_t fa_decode(const void* q, const void* k_cache, const void* v_cache,
+                      void* o, float* lse,
+                      void* workspace, size_t workspace_bytes,
+                      int B, int H, int L, int d, fa_dtype_t dtype,
+                      int num_splits, float scale, void* stream);
+
+/* fa_status_string -- a static, human-readable name for a status code. */
+const char* fa_status_string(fa_status_t s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

@@ -1,0 +1,172 @@
+"""Host-only checks of the C ABI: the library loads, exports every function
+``include/fa.h`` declares, sizes workspaces, and rejects every invalid call
+with its status code before anything is enqueued.
+
+No kernel is launched here.  The fake device "pointers" are plain integers
+that every tested call rejects during validation, so they are never touched.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import exact_io_aware_11_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+A = 1 << 20          # an aligned fake address (never dereferenced)
+MIS = A + 4          # a misaligned one
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == sorted([
+        "fa_bwd", "fa_bwd_workspace_bytes", "fa_decode", "fa_decode_num_splits",
+        "fa_decode_workspace_bytes", "fa_fwd", "fa_status_string"])
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(fa.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    for s in range(7):
+        assert fa.fa_status_string(s).startswith("FA_")
+    assert "unknown" in fa.fa_status_string(99)
+
+
+def fwd(**kw):
+    args = dict(q=A, k=A, v=A, o=A, o_dtype=fa.FA_BF16, lse=A, B=1, H=1, N=16, d=64,
+                in_dtype=fa.FA_BF16, causal=0, scale=0.125)
+    args.update(kw)
+    return fa.fa_fwd(args["q"], args["k"], args["v"], args["o"], args["o_dtype"], args["lse"],
+                     args["B"], args["H"], args["N"], args["d"], args["in_dtype"], args["causal"],
+                     args["scale"], 0)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=0), fa.FA_ERR_NULL),
+    (dict(k=0), fa.FA_ERR_NULL),
+    (dict(v=0), fa.FA_ERR_NULL),
+    (dict(o=0), fa.FA_ERR_NULL),
+    (dict(lse=0), fa.FA_ERR_NULL),
+    (dict(B=0), fa.FA_ERR_ARG),
+    (dict(H=-1), fa.FA_ERR_ARG),
+    (dict(N=0), fa.FA_ERR_ARG),
+    (dict(scale=float("nan")), fa.FA_ERR_ARG),
+    (dict(scale=float("inf")), fa.FA_ERR_ARG),
+    (dict(scale=0.0), fa.FA_ERR_ARG),
+    (dict(scale=-0.5), fa.FA_ERR_ARG),
+    (dict(B=1 << 16, H=1 << 16, N=16), fa.FA_ERR_ARG),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=256), fa.FA_ERR_UNSUPPORTED),
+    (dict(in_dtype=7), fa.FA_ERR_UNSUPPORTED),
+    (dict(o_dtype=5), fa.FA_ERR_UNSUPPORTED),
+    (dict(in_dtype=fa.FA_FP32, o_dtype=fa.FA_BF16), fa.FA_ERR_UNSUPPORTED),
+    (dict(q=MIS), fa.FA_ERR_ALIGN),
+    (dict(o=MIS), fa.FA_ERR_ALIGN),
+    (dict(lse=MIS), fa.FA_ERR_ALIGN),
+])
+def test_fwd_rejects(kw, status):
+    assert fwd(**kw) == status
+
+
+def bwd(ws_bytes=None, **kw):
+    B, H, N, d = kw.get("B", 1), kw.get("H", 1), kw.get("N", 16), kw.get("d", 64)
+    need = fa.fa_bwd_workspace_bytes(B, H, N, d)
+    args = dict(q=A, k=A, v=A, o=A, o_dtype=fa.FA_BF16, lse=A, dout=A, dq=A, dk=A, dv=A, ws=A,
+                B=B, H=H, N=N, d=d, in_dtype=fa.FA_BF16, causal=1, scale=0.125)
+    args.update(kw)
+    return fa.fa_bwd(args["q"], args["k"], args["v"], args["o"], args["o_dtype"], args["lse"],
+                     args["dout"], args["dq"], args["dk"], args["dv"], args["ws"],
+                     need if ws_bytes is None else ws_bytes, args["B"], args["H"], args["N"], args["d"],
+                     args["in_dtype"], args["causal"], args["scale"], 0)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dout=0), fa.FA_ERR_NULL),
+    (dict(dq=0), fa.FA_ERR_NULL),
+    (dict(lse=0), fa.FA_ERR_NULL),
+    (dict(N=0), fa.FA_ERR_ARG),
+    (dict(scale=float("nan")), fa.FA_ERR_ARG),
+    (dict(in_dtype=fa.FA_FP32), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=32), fa.FA_ERR_UNSUPPORTED),
+    (dict(o_dtype=3), fa.FA_ERR_UNSUPPORTED),
+    (dict(dk=MIS), fa.FA_ERR_ALIGN),
+    (dict(ws=0), fa.FA_ERR_WORKSPACE),
+    (dict(ws=MIS), fa.FA_ERR_ALIGN),
+])
+def test_bwd_rejects(kw, status):
+    assert bwd(**kw) == status
+
+
+def test_bwd_rejects_small_workspace():
+    need = fa.fa_bwd_workspace_bytes(1, 1, 16, 64)
+    assert bwd(ws_bytes=need - 1) == fa.FA_ERR_WORKSPACE
+
+
+def test_bwd_workspace_size():
+    # fp32 accumulator (256-byte aligned) + fp32 row statistic
+    B, H, N, d = 2, 16, 4096, 128
+    acc = B * H * N * d * 4
+    assert fa.fa_bwd_workspace_bytes(B, H, N, d) == ((acc + 255) // 256) * 256 + B * H * N * 4
+    assert fa.fa_bwd_workspace_bytes(0, 1, 1, 64) == 0
+
+
+def dec(ws_bytes=None, **kw):
+    B, H, L, d, s = kw.get("B", 2), kw.get("H", 2), kw.get("L", 100), kw.get("d", 128), kw.get("splits", 0)
+    need = fa.fa_decode_workspace_bytes(B, H, L, d, max(s, 0))
+    args = dict(q=A, k=A, v=A, o=A, lse=A, ws=A, B=B, H=H, L=L, d=d, dtype=fa.FA_BF16,
+                splits=s, scale=0.1)
+    args.update(kw)
+    return fa.fa_decode(args["q"], args["k"], args["v"], args["o"], args["lse"], args["ws"],
+                        need if ws_bytes is None else ws_bytes, args["B"], args["H"], args["L"],
+                        args["d"], args["dtype"], args["splits"], args["scale"], 0)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=0), fa.FA_ERR_NULL),
+    (dict(k=0), fa.FA_ERR_NULL),
+    (dict(o=0), fa.FA_ERR_NULL),
+    (dict(L=0), fa.FA_ERR_ARG),
+    (dict(splits=-1), fa.FA_ERR_ARG),
+    (dict(splits=101), fa.FA_ERR_ARG),
+    (dict(scale=-1.0), fa.FA_ERR_ARG),
+    (dict(dtype=fa.FA_FP32), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=80), fa.FA_ERR_UNSUPPORTED),
+    (dict(v=MIS), fa.FA_ERR_ALIGN),
+    (dict(lse=MIS), fa.FA_ERR_ALIGN),
+    (dict(ws=0), fa.FA_ERR_WORKSPACE),
+])
+def test_decode_rejects(kw, status):
+    assert dec(**kw) == status
+
+
+def test_decode_rejects_small_workspace():
+    need = fa.fa_decode_workspace_bytes(2, 2, 100, 128, 4)
+    assert dec(ws_bytes=need - 1, splits=4) == fa.FA_ERR_WORKSPACE
+
+
+def test_decode_split_plan():
+    # the automatic split count never exceeds L and never leaves a chunk empty
+    for (B, H, L) in [(64, 32, 8192), (1, 1, 1), (1, 32, 16384), (2, 3, 700), (1, 1, 513)]:
+        s = fa.fa_decode_num_splits(B, H, L, 128)
+        assert 1 <= s <= L
+        chunk = -(-L // s)
+        assert (s - 1) * chunk < L
+    # a workspace holds d + 1 floats per (b, h, split)
+    s = fa.fa_decode_num_splits(64, 32, 8192, 128)
+    parts = 64 * 32 * s
+    assert fa.fa_decode_workspace_bytes(64, 32, 8192, 128, 0) == ((parts * 128 * 4 + 255) // 256) * 256 + parts * 4

@@ -1,0 +1,289 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Every case draws seeded inputs, runs the library on the GPU, widens exactly
+the values the GPU received to fp64 and compares element by element with the
+oracle under the tolerances of ``parity_util``.  Full-size workloads that the
+oracle cannot finish in seconds are checked on sampled rows / heads / batches
+that the oracle computes one by one, at the same launch configuration the
+benchmark times.
+"""
+
+from __future__ import annotations
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import fa_workloads as W
+from oracle import ref_bwd, ref_decode, ref_fwd, ref_fwd_rows
+from parity_util import (assert_bf16_close, assert_fp32_close, assert_grad_close, to64)
+
+pytestmark = pytest.mark.gpu
+
+
+def _fa():
+    import exact_io_aware_11_amd as fa
+    return fa
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+DEV = "cuda:0"
+
+
+# ----------------------------------------------------------------------------
+# forward: the five workloads' forward parts
+# ----------------------------------------------------------------------------
+
+def test_fwd_fp32_b1h1n128d64():
+    fa = _fa()
+    w = W.WORKLOADS["fwd_fp32_b1h1n128d64"]
+    q, k, v = W.make_inputs(w, DEV)
+    say(f"fa_fwd fp32 {tuple(q.shape)} causal={w.causal}")
+    o, lse = fa.attention(q, k, v, is_causal=w.causal, scale=w.scale)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = ref_fwd(to64(q), to64(k), to64(v), w.causal, w.scale)
+    assert_fp32_close(to64(o), o_ref, "O")
+    assert_fp32_close(to64(lse), lse_ref, "LSE")
+
+
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32], ids=["o_bf16", "o_fp32"])
+def test_fwd_causal_bf16_b4h16n2048d128(out_dtype):
+    fa = _fa()
+    w = W.WORKLOADS["fwd_causal_bf16_b4h16n2048d128"]
+    q, k, v = W.make_inputs(w, DEV)
+    say(f"fa_fwd bf16 {tuple(q.shape)} causal out={out_dtype}")
+    o, lse = fa.attention(q, k, v, is_causal=True, scale=w.scale, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = ref_fwd(to64(q), to64(k), to64(v), True, w.scale)
+    assert_bf16_close(to64(o), o_ref, "O")
+    assert_bf16_close(to64(lse), lse_ref, "LSE")
+
+
+def test_fwd_causal_bf16_b1h32n16384d128_sampled_rows():
+    fa = _fa()
+    w = W.WORKLOADS["fwd_causal_bf16_b1h32n16384d128"]
+    q, k, v = W.make_inputs(w, DEV)
+    say(f"fa_fwd bf16 {tuple(q.shape)} causal (64 sampled rows per head + edge rows)")
+    o, lse = fa.attention(q, k, v, is_causal=True, scale=w.scale)
+    torch.cuda.synchronize()
+    rows = W.sample_rows(w.N, w.extra["sample_rows"], w.extra["row_seed"])
+    edge = [0, 1, 127, 128, w.N - 1]
+    for name, rr in (("sampled", rows), ("edge", edge)):
+        o_ref, lse_ref = ref_fwd_rows(to64(q), to64(k), to64(v), True, w.scale, rr)
+        assert_bf16_close(to64(o[:, :, rr]), o_ref, f"O {name}")
+        assert_bf16_close(to64(lse[:, :, rr]), lse_ref, f"LSE {name}")
+
+
+# ----------------------------------------------------------------------------
+# forward: ragged and small shapes against the full oracle
+# ----------------------------------------------------------------------------
+
+SMALL = [
+    # (B, H, N, d, dtype, causal)
+    (1, 1, 1, 64, "bf16", False),
+    (1, 1, 1, 128, "bf16", True),
+    (1, 2, 17, 64, "bf16", True),
+    (2, 1, 63, 128, "bf16", False),
+    (1, 2, 127, 128, "bf16", True),
+    (1, 1, 128, 128, "bf16", True),
+    (2, 2, 129, 64, "bf16", True),
+    (1, 3, 200, 128, "bf16", False),
+    (1, 2, 1000, 128, "bf16", True),
+    (1, 1, 1000, 64, "bf16", False),
+    (1, 1, 1, 64, "fp32", False),
+    (1, 2, 33, 128, "fp32", True),
+    (2, 1, 129, 64, "fp32", True),
+    (1, 1, 300, 128, "fp32", False),
+]
+
+
+@pytest.mark.parametrize("B,H,N,d,dtype,causal", SMALL)
+def test_fwd_small_shapes(B, H, N, d, dtype, causal):
+    fa = _fa()
+    q, k, v = W.make_custom(B, H, N, d, dtype, seed=1000 + N + d, device=DEV)
+    scale = 1.0 / math.sqrt(d)
+    say(f"fa_fwd {dtype} {(B, H, N, d)} causal={causal}")
+    o, lse = fa.attention(q, k, v, is_causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = ref_fwd(to64(q), to64(k), to64(v), causal, scale)
+    check = assert_fp32_close if dtype == "fp32" else assert_bf16_close
+    check(to64(o), o_ref, "O")
+    check(to64(lse), lse_ref, "LSE")
+
+
+def test_fwd_closed_form_uniform_scores():
+    # Q = 0: row i of a causal head is the mean of V_0..V_i and LSE_i = ln(i+1)
+    fa = _fa()
+    B, H, N, d = 1, 2, 300, 128
+    _, k, v = W.make_custom(B, H, N, d, "bf16", seed=77, device=DEV)
+    q = torch.zeros_like(k)
+    say("fa_fwd closed form Q=0 causal")
+    o, lse = fa.attention(q, k, v, is_causal=True, scale=0.125)
+    torch.cuda.synchronize()
+    vv = to64(v)
+    counts = np.arange(1, N + 1, dtype=np.float64)
+    expect = np.cumsum(vv, axis=2) / counts[None, None, :, None]
+    assert_bf16_close(to64(o), expect, "O")
+    assert_bf16_close(to64(lse), np.broadcast_to(np.log(counts), (B, H, N)), "LSE")
+
+
+def test_fwd_large_scores_stay_finite():
+    # Q and K scaled x8 make scores of O(100): the running max must keep exp
+    # finite.  V stays N(0, 1) so that O's own bf16 rounding stays below the
+    # absolute tolerance.
+    fa = _fa()
+    q, k = W.make_custom(1, 2, 257, 128, "bf16", seed=78, sigma=8.0, n_tensors=2, device=DEV)
+    (v,) = W.make_custom(1, 2, 257, 128, "bf16", seed=178, n_tensors=1, device=DEV)
+    say("fa_fwd large logits")
+    o, lse = fa.attention(q, k, v, is_causal=True)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+    o_ref, lse_ref = ref_fwd(to64(q), to64(k), to64(v), True, 1 / math.sqrt(128))
+    # scores of magnitude ~100 amplify fp32 accumulation order; LSE is checked relative
+    assert_bf16_close(to64(o), o_ref, "O")
+    assert np.max(np.abs(to64(lse) - lse_ref) / np.maximum(1.0, np.abs(lse_ref))) <= 2e-3
+
+
+def test_fwd_deterministic_and_allocation_free():
+    fa = _fa()
+    q, k, v = W.make_custom(2, 4, 1000, 128, "bf16", seed=79, device=DEV)
+    o1 = torch.empty_like(q)
+    o2 = torch.empty_like(q)
+    l1 = torch.empty((2, 4, 1000), dtype=torch.float32, device=DEV)
+    l2 = torch.empty_like(l1)
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+    before = torch.cuda.memory_allocated()
+    stream = torch.cuda.current_stream().cuda_stream
+    say("fa_fwd determinism / no allocation")
+    for o, l in ((o1, l1), (o2, l2)):
+        st = fa.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), fa.FA_BF16, l.data_ptr(),
+                       2, 4, 1000, 128, fa.FA_BF16, 1, 1 / math.sqrt(128), stream)
+        assert st == fa.FA_OK
+    torch.cuda.synchronize()
+    assert torch.cuda.max_memory_allocated() == before
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+# ----------------------------------------------------------------------------
+# backward
+# ----------------------------------------------------------------------------
+
+BWD_SMALL = [
+    # (B, H, N, d, causal, o_dtype)
+    (1, 1, 1, 64, True, "bf16"),
+    (1, 2, 17, 128, True, "bf16"),
+    (1, 1, 64, 64, False, "bf16"),
+    (2, 1, 127, 128, True, "fp32"),
+    (1, 2, 128, 128, False, "bf16"),
+    (1, 1, 129, 64, True, "bf16"),
+    (1, 2, 300, 128, True, "bf16"),
+    (1, 1, 515, 128, False, "fp32"),
+]
+
+
+def _bwd_case(B, H, N, d, causal, o_dtype, seed, sigma=1.0):
+    fa = _fa()
+    q, k, v, do = W.make_custom(B, H, N, d, "bf16", seed=seed, sigma=sigma, n_tensors=4, device=DEV)
+    scale = 1.0 / math.sqrt(d)
+    odt = torch.bfloat16 if o_dtype == "bf16" else torch.float32
+    o, lse = fa.attention(q, k, v, is_causal=causal, scale=scale, out_dtype=odt)
+    dq, dk, dv = fa.attention_backward(q, k, v, o, lse, do, is_causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return (q, k, v, do), (dq, dk, dv)
+
+
+@pytest.mark.parametrize("B,H,N,d,causal,o_dtype", BWD_SMALL)
+def test_bwd_small_shapes(B, H, N, d, causal, o_dtype):
+    say(f"fa_bwd {(B, H, N, d)} causal={causal} o={o_dtype}")
+    (q, k, v, do), (dq, dk, dv) = _bwd_case(B, H, N, d, causal, o_dtype, seed=2000 + N + d)
+    rq, rk, rv = ref_bwd(to64(q), to64(k), to64(v), to64(do), causal, 1 / math.sqrt(d))
+    assert_grad_close(to64(dq), rq, "dQ")
+    assert_grad_close(to64(dk), rk, "dK")
+    assert_grad_close(to64(dv), rv, "dV")
+
+
+def test_bwd_causal_bf16_b2h16n4096d128_sampled_heads():
+    fa = _fa()
+    w = W.WORKLOADS["bwd_causal_bf16_b2h16n4096d128"]
+    q, k, v, do = W.make_inputs(w, DEV)
+    say(f"fa_fwd+fa_bwd bf16 {tuple(q.shape)} causal")
+    o, lse = fa.attention(q, k, v, is_causal=True, scale=w.scale)
+    dq, dk, dv = fa.attention_backward(q, k, v, o, lse, do, is_causal=True, scale=w.scale)
+    torch.cuda.synchronize()
+    heads = [(0, 0), (0, 9), (1, 4), (1, 15)]
+    for b, h in heads:
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        rq, rk, rv = ref_bwd(to64(q[sl]), to64(k[sl]), to64(v[sl]), to64(do[sl]), True, w.scale)
+        assert_grad_close(to64(dq[sl]), rq, f"dQ head {(b, h)}")
+        assert_grad_close(to64(dk[sl]), rk, f"dK head {(b, h)}")
+        assert_grad_close(to64(dv[sl]), rv, f"dV head {(b, h)}")
+    # invariants over every head: sum_j dV_j = sum_i dO_i, sum_j dK_j = 0
+    dv_sum = dv.float().sum(dim=2)
+    do_sum = do.float().sum(dim=2)
+    scale_v = dv.float().abs().amax().item()
+    assert (dv_sum - do_sum).abs().max().item() <= 2e-2 * scale_v * math.sqrt(w.N)
+    scale_k = dk.float().abs().amax().item()
+    assert dk.float().sum(dim=2).abs().max().item() <= 2e-2 * scale_k * math.sqrt(w.N)
+
+
+# ----------------------------------------------------------------------------
+# decode
+# ----------------------------------------------------------------------------
+
+def test_decode_bf16_b64h32l8192d128_sampled_batches():
+    fa = _fa()
+    w = W.WORKLOADS["decode_bf16_b64h32l8192d128"]
+    q, kc, vc = W.make_inputs(w, DEV)
+    say(f"fa_decode bf16 q{tuple(q.shape)} cache{tuple(kc.shape)} splits=auto")
+    o, lse = fa.decode(q, kc, vc, scale=w.scale)
+    torch.cuda.synchronize()
+    g = torch.Generator().manual_seed(505)
+    batches = torch.randperm(w.B, generator=g)[:6].tolist() + [0, w.B - 1]
+    for b in sorted(set(batches)):
+        o_ref, lse_ref = ref_decode(to64(q[b:b + 1]), to64(kc[b:b + 1]), to64(vc[b:b + 1]), w.scale)
+        assert_bf16_close(to64(o[b:b + 1]), o_ref, f"O batch {b}")
+        assert_bf16_close(to64(lse[b:b + 1]), lse_ref, f"LSE batch {b}")
+
+
+@pytest.mark.parametrize("L", [1, 7, 100, 1000, 4097])
+@pytest.mark.parametrize("d", [64, 128])
+def test_decode_split_counts_agree(L, d):
+    fa = _fa()
+    B, H = 3, 5
+    q, kc, vc = W.make_custom(B, H, 1, d, "bf16", seed=3000 + L + d, Nk=L, device=DEV)
+    scale = 1 / math.sqrt(d)
+    o_ref, lse_ref = ref_decode(to64(q), to64(kc), to64(vc), scale)
+    outs = []
+    for s in (0, 1, 2, 4, 8, 16):
+        if s > L:
+            continue
+        say(f"fa_decode {(B, H, L, d)} splits={s}")
+        o, lse = fa.decode(q, kc, vc, scale=scale, num_splits=s)
+        torch.cuda.synchronize()
+        assert_bf16_close(to64(o), o_ref, f"O splits={s}")
+        assert_bf16_close(to64(lse), lse_ref, f"LSE splits={s}")
+        outs.append((to64(o), to64(lse)))
+    o0, l0 = outs[0]
+    for o, lse in outs[1:]:
+        # split counts change only the fp32 summation order: LSEs agree to fp32
+        # level, bf16 outputs at most one rounding step apart
+        assert np.max(np.abs(lse - l0)) <= 1e-4
+        assert np.all(np.abs(o - o0) <= np.maximum(np.abs(o), np.abs(o0)) * 2.0 ** -7 + 1e-6)
+
+
+def test_decode_deterministic():
+    fa = _fa()
+    q, kc, vc = W.make_custom(4, 8, 1, 128, "bf16", seed=3100, Nk=3000, device=DEV)
+    say("fa_decode determinism")
+    a = fa.decode(q, kc, vc)
+    b = fa.decode(q, kc, vc)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
