@@ -61,6 +61,26 @@ __device__ __forceinline__ uint4 load_stream16(const void* p) {
     return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// 16-byte global -> LDS copy that bypasses registers (global_load_lds_dwordx4).
+// Lane l's 16 bytes land at lds_base + 16*l; lds_base must be wave-uniform.
+__device__ __forceinline__ void g2lds16(const void* gsrc, void* lds_base) {
+    __builtin_amdgcn_global_load_lds(gsrc, (lds_void*)lds_base, 16, 0, 0);
+}
+
+// Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
+// local lane j supplies the address of 4 consecutive 16-bit elements; local
+// lane i receives element i%4 of the rows supplied by local lanes 4e + i/4,
+// e = 0..3.  With lane j pointing at row r0 + j/4, columns c0 + 4*(j%4) .. +3
+// of a row-major tile, lane i receives column c0 + i of rows r0 .. r0+3.
+__device__ __forceinline__ uint2 lds_read_tr16x4(const void* p) {
+    const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p);
+    return __builtin_bit_cast(uint2, r);
+}
+
 // Eight packed bf16 (one 16-byte chunk) -> one MFMA operand.
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
 

@@ -48,22 +48,39 @@ __device__ __forceinline__ void fwd_tile_of(int bid, int BH, int nqt, bool causa
     qt = causal ? (nqt - 1 - t) : t;
 }
 
+// K and V tiles live in LDS row-major without padding (2*D bytes per row) and
+// are filled by direct global->LDS copies; bank conflicts are avoided by
+// permuting the 16-byte chunks of each row with an XOR of the row index.
+// K is read one 16-byte chunk per lane by 32 consecutive rows: XOR with
+// row % (chunks per row).  V is read with the transposing 8-byte read, whose
+// 16-lane groups touch 4 consecutive rows x 32 bytes: XOR of chunk bits 2..3
+// spreads those rows over all banks.
+template <int D>
+__device__ __forceinline__ int k_swz(int row) { return row & (D / 8 - 1); }
+template <int D>
+__device__ __forceinline__ int v_swz(int row) {
+    return D == 128 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2);
+}
+
 template <int D, bool CAUSAL, bool OUT_BF16>
-__global__ void __launch_bounds__(FWD_THREADS)
+__global__ void __launch_bounds__(FWD_THREADS) __attribute__((amdgpu_waves_per_eu(2)))
 fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                 const __bf16* __restrict__ V, void* __restrict__ O, float* __restrict__ LSE,
                 int BH, int N, int nqt, float c /* scale * log2(e) */) {
     constexpr int BR = FWD_BR, BC = FWD_BC;
-    constexpr int KS = D + 8;      // LDS row stride (bf16) of the K tile
-    constexpr int VS = BC + 8;     // LDS row stride (bf16) of the V^T tile
-    constexpr int KCH = BC * D / 8;                // 16-byte chunks in a K tile
-    constexpr int KPT = KCH / FWD_THREADS;         // chunks per thread
-    constexpr int VBLK = (BC / 4) * (D / 8);       // 4-key x 8-dim blocks in a V tile
-    constexpr int VPT = (VBLK + FWD_THREADS - 1) / FWD_THREADS;
-    static_assert(KCH % FWD_THREADS == 0, "K tile must split evenly");
+    constexpr int ROWB = 2 * D;              // bytes per K/V row in LDS
+    constexpr int CPR = D / 8;               // 16-byte chunks per row
+    constexpr int TILEB = BC * ROWB;         // bytes per K (or V) tile
+    constexpr int RPS = 1024 / ROWB;         // rows per 1 KiB copy segment
+    constexpr int SPW = TILEB / 1024 / 4;    // copy segments per wave per tile
+    constexpr float TAU = 8.f;               // lazy-rescale threshold, log2 units
+    static_assert(SPW >= 1, "tile too small for four waves");
 
-    __shared__ __attribute__((aligned(16))) __bf16 Ks[BC * KS];
-    __shared__ __attribute__((aligned(16))) __bf16 Vt[D * VS];
+    // Two buffers, each a K tile followed by a V tile.  They are separate
+    // objects so that the compiler can tell that the copies into one buffer do
+    // not alias the reads of the other, and need not wait for them.
+    __shared__ __attribute__((aligned(1024))) char smem0[2 * TILEB];
+    __shared__ __attribute__((aligned(1024))) char smem1[2 * TILEB];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
@@ -90,82 +107,62 @@ fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     f32x16 oacc[D / 32];
 #pragma unroll
     for (int mb = 0; mb < D / 32; ++mb) oacc[mb] = zero16();
-    float m_run = -INFINITY;   // running max of scale*log2(e)*s over the row
+    float m_ref = -INFINITY;   // reference max (log2 units) the exponentials use
     float l_run = 0.f;         // this lane's share of the running sum
 
     const int kv_end = CAUSAL ? min(N, q0 + BR) : N;
     const int nkt = (kv_end + BC - 1) / BC;
 
-    uint4 kreg[KPT];
-    uint4 vreg[VPT][4];
-
-    auto load_tile = [&](int kt) {
-        const int kv0 = kt * BC;
+    // Copy the K/V tile starting at key kv0 into buffer buf.  Rows past the
+    // end are clamped to row N-1: they are masked (K) or weighted by 0 (V).
+    auto issue = [&](int kv0, char* buf) {
+        char* kdst = buf;
+        char* vdst = buf + TILEB;
 #pragma unroll
-        for (int i = 0; i < KPT; ++i) {
-            const int ch = tid + FWD_THREADS * i;
-            const int row = ch / (D / 8), c8 = ch % (D / 8);
-            uint4 u = make_uint4(0, 0, 0, 0);
-            if (kv0 + row < N) u = *reinterpret_cast<const uint4*>(Kh + (size_t)(kv0 + row) * D + 8 * c8);
-            kreg[i] = u;
-        }
-#pragma unroll
-        for (int i = 0; i < VPT; ++i) {
-            const int blk = tid + FWD_THREADS * i;
-            const int kq = blk % (BC / 4), dc = blk / (BC / 4);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int key = kv0 + 4 * kq + r;
-                uint4 u = make_uint4(0, 0, 0, 0);
-                if (blk < VBLK && key < N) u = *reinterpret_cast<const uint4*>(Vh + (size_t)key * D + 8 * dc);
-                vreg[i][r] = u;
-            }
-        }
-    };
-    auto store_tile = [&]() {
-#pragma unroll
-        for (int i = 0; i < KPT; ++i) {
-            const int ch = tid + FWD_THREADS * i;
-            const int row = ch / (D / 8), c8 = ch % (D / 8);
-            *reinterpret_cast<uint4*>(Ks + row * KS + 8 * c8) = kreg[i];
-        }
-#pragma unroll
-        for (int i = 0; i < VPT; ++i) {
-            const int blk = tid + FWD_THREADS * i;
-            if (blk < VBLK) {
-                const int kq = blk % (BC / 4), dc = blk / (BC / 4);
-                const int pos = perm16(4 * kq);
-#pragma unroll
-                for (int cc = 0; cc < 8; ++cc)
-                    *reinterpret_cast<uint2*>(Vt + (8 * dc + cc) * VS + pos) =
-                        column4(vreg[i][0], vreg[i][1], vreg[i][2], vreg[i][3], cc);
-            }
+        for (int i = 0; i < SPW; ++i) {
+            const int seg = w * SPW + i;
+            const int row = seg * RPS + lane / CPR;
+            const int pc = lane % CPR;
+            const size_t grow = (size_t)min(kv0 + row, N - 1) * D;
+            g2lds16(Kh + grow + 8 * (pc ^ k_swz<D>(row)), kdst + seg * 1024);
+            g2lds16(Vh + grow + 8 * (pc ^ v_swz<D>(row)), vdst + seg * 1024);
         }
     };
 
-    if (nkt > 0) load_tile(0);
+    // per-lane constant parts of the LDS addresses
+    const int gq = lane >> 4, li = lane & 15;
+    const int k_rd_row0 = l32;                        // + 32*kb
+    const int v_rd_row = 4 * g + (li >> 2);           // + 16*ks + 8*h
+    const int v_rd_col = 16 * (gq & 1) + 4 * (li & 3);  // + 32*mb (elements)
+
     const int wrow0 = q0 + 32 * w;
-    for (int kt = 0; kt < nkt; ++kt) {
+    // One step: wait for tile kt (in `cur`), start copying tile kt+1 into
+    // `nxt`, then compute on `cur`.  Called with the buffers swapped on odd
+    // steps so that both are compile-time distinct objects.
+    auto step = [&](int kt, const char* cur, char* nxt) {
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        store_tile();
-        __syncthreads();
-        if (kt + 1 < nkt) load_tile(kt + 1);
+        if (kt + 1 < nkt) issue((kt + 1) * BC, nxt);
 
         const int kv0 = kt * BC;
-        if (wrow0 >= N) continue;                       // padding wave
-        if (CAUSAL && kv0 > wrow0 + 31) continue;       // tile entirely above the diagonal
+        if (wrow0 >= N) return;                         // padding wave
+        if (CAUSAL && kv0 > wrow0 + 31) return;         // tile entirely above the diagonal
+        const char* Ks = cur;
+        const char* Vs = cur + TILEB;
 
-        // S^T = K Q^T : two 32-key blocks
+        // S^T = K Q^T : BC/32 blocks of 32 keys
         f32x16 s[BC / 32];
 #pragma unroll
-        for (int kb = 0; kb < BC / 32; ++kb) {
-            s[kb] = zero16();
+        for (int kb = 0; kb < BC / 32; ++kb) s[kb] = zero16();
 #pragma unroll
-            for (int ks = 0; ks < D / 16; ++ks) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8*>(Ks + (32 * kb + l32) * KS + 16 * ks + 8 * g);
+        for (int ks = 0; ks < D / 16; ++ks)
+#pragma unroll
+            for (int kb = 0; kb < BC / 32; ++kb) {
+                const int row = 32 * kb + k_rd_row0;
+                const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+                    Ks + row * ROWB + 16 * ((2 * ks + g) ^ k_swz<D>(row)));
                 s[kb] = mfma_bf16(a, qf[ks], s[kb]);
             }
-        }
 
         const bool need_mask = (kv0 + BC > N) || (CAUSAL && kv0 + BC - 1 > wrow0);
         if (need_mask) {
@@ -183,11 +180,20 @@ fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
         for (int kb = 0; kb < BC / 32; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-        mx = xor32_max(mx);
-        const float m_new = fmaxf(m_run, mx * c);
-        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-        const float alpha = exp2_fast(m_run - m_use);
-        m_run = m_new;
+        mx = xor32_max(mx) * c;
+        // Lazy rescaling: the exponentials use a reference max that is only
+        // raised when the row max exceeds it by more than TAU (p <= 2^TAU).
+        if (__any(mx > m_ref + TAU)) {
+            const float m_new = fmaxf(m_ref, mx);
+            const float alpha = exp2_fast(m_ref - m_new);   // 0 on the first tile
+            m_ref = m_new;
+            l_run *= alpha;
+#pragma unroll
+            for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[mb][r] *= alpha;
+        }
+        const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
 
         // P (bf16) laid out as the B operand of O^T += V^T P^T
         bf16x8 pb[BC / 16];
@@ -206,20 +212,29 @@ fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                 }
                 pb[2 * kb + h] = as_bf16x8(make_uint4(pk[0], pk[1], pk[2], pk[3]));
             }
-        l_run = l_run * alpha + psum;
-#pragma unroll
-        for (int mb = 0; mb < D / 32; ++mb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) oacc[mb][r] *= alpha;
+        l_run += psum;
 
-        // O^T += V^T P^T
+        // O^T += V^T P^T ; V^T operand read transposed from the row-major tile
 #pragma unroll
-        for (int mb = 0; mb < D / 32; ++mb)
+        for (int ks = 0; ks < BC / 16; ++ks)
 #pragma unroll
-            for (int ks = 0; ks < BC / 16; ++ks) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8*>(Vt + (32 * mb + l32) * VS + 16 * ks + 8 * g);
+            for (int mb = 0; mb < D / 32; ++mb) {
+                uint2 part[2];
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int row = 16 * ks + 8 * h + v_rd_row;
+                    const int col = 32 * mb + v_rd_col;
+                    part[h] = lds_read_tr16x4(Vs + row * ROWB + 16 * ((col >> 3) ^ v_swz<D>(row)) + 2 * (col & 7));
+                }
+                const bf16x8 a = as_bf16x8(make_uint4(part[0].x, part[0].y, part[1].x, part[1].y));
                 oacc[mb] = mfma_bf16(a, pb[ks], oacc[mb]);
             }
+    };
+
+    if (nkt > 0) issue(0, smem0);
+    for (int kt = 0; kt < nkt; kt += 2) {
+        step(kt, smem0, smem1);
+        if (kt + 1 < nkt) step(kt + 1, smem1, smem0);
     }
 
     const float l_tot = xor32_sum(l_run);
@@ -241,7 +256,7 @@ fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                 }
             }
         if (g == 0)
-            LSE[(size_t)bh * N + qrow] = (l_tot > 0.f) ? m_run * kLn2 + __logf(l_tot) : -INFINITY;
+            LSE[(size_t)bh * N + qrow] = (l_tot > 0.f) ? m_ref * kLn2 + __logf(l_tot) : -INFINITY;
     }
 }
 
