@@ -12,20 +12,21 @@
 //   1. bwd_prep:  D = rowsum(dO * O) in fp32, and the fp32 dQ accumulator
 //                 cleared to zero.
 //   2. bwd_main:  one workgroup per tile of BC = 128 keys of one head (4 waves,
-//                 32 keys each).  K and V of the tile stay in registers; the
-//                 workgroup walks the query tiles (BR = 64 rows) that can see
-//                 its keys, staging Q and dO in LDS both row-major and
-//                 transposed.  dK^T and dV^T accumulate in registers; dS goes
+//                 32 keys each).  K and V of the tile stay in registers (and K
+//                 also in LDS); the workgroup walks the query tiles (BR = 64
+//                 rows) that can see its keys.  Q, dO, LSE and D of the next
+//                 query tile are copied global -> LDS while the current one is
+//                 computed.  dK^T and dV^T accumulate in registers; dS goes
 //                 through LDS so that all four waves contribute to
 //                 dQ_i += dS K_j, which is added into the fp32 accumulator with
-//                 global atomics.
+//                 global atomics that stay in flight across the barriers.
 //   3. bwd_dq:    dQ = scale * accumulator, rounded to bf16.
 //
 // Layout trick (as in the forward): S is computed with queries as MFMA rows
 // and keys as columns, so each lane holds one key and 16 queries; those
 // registers are directly the K-slot-ordered B operands of dV^T = dO^T P and
-// dK^T = Q^T dS when Q^T and dO^T are staged with the matching query
-// permutation.
+// dK^T = Q^T dS, whose Q^T / dO^T operands are read with the transposing LDS
+// read in the matching query order.
 #include "fa_common.hpp"
 #include "fa_internal.hpp"
 
@@ -85,21 +86,21 @@ bwd_prep_kernel(const void* __restrict__ O, const __bf16* __restrict__ dO, float
 // ---------------------------------------------------------------------------
 // 2. main kernel
 // ---------------------------------------------------------------------------
+// Q, dO and K tiles live in LDS row-major (2*D bytes per row, no padding),
+// filled by direct global -> LDS copies.  Each is read two ways: 16-byte
+// chunks by 32 consecutive rows (A operands of S = Q K^T and dP = dO V^T) and
+// with the transposing 8-byte read (Q^T, dO^T and K^T operands, 4 rows x 32
+// bytes per 16-lane group).  The XOR of the 16-byte chunk index with
+// 4*(row%4) + (row/4)%4 keeps both patterns free of bank conflicts.
 template <int D>
-struct BwdSmem {
-    static constexpr int RS = D + 8;          // row-major [BR][D] stride
-    static constexpr int TS = BWD_BR + 8;     // transposed [D][BR] stride
-    static constexpr int KTS = BWD_BC + 8;    // K^T [D][BC] stride
-    static constexpr int DSS = BWD_BC + 8;    // dS [BR][BC] stride
-    __bf16 q[BWD_BR * RS];
-    __bf16 qt[D * TS];
-    __bf16 dO[BWD_BR * RS];
-    __bf16 dOt[D * TS];
-    __bf16 kt[D * KTS];
-    __bf16 ds[BWD_BR * DSS];
-    float lse[BWD_BR];
-    float dd[BWD_BR];
-};
+__device__ __forceinline__ int bwd_swz(int row) {
+    return (4 * (row & 3) + ((row >> 2) & 3)) & (D / 8 - 1);
+}
+
+// s_waitcnt with only vmcnt constrained (expcnt / lgkmcnt left at their max).
+#define FA_WAIT_VMCNT(n) \
+    __builtin_amdgcn_s_waitcnt((((n) & 15) | (((n) >> 4) << 14)) | (7 << 4) | (15 << 8))
+#define FA_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4))
 
 template <int D, bool CAUSAL>
 __global__ void __launch_bounds__(BWD_THREADS)
@@ -107,11 +108,31 @@ bwd_main_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, cons
                 const __bf16* __restrict__ dO, const float* __restrict__ LSE,
                 const float* __restrict__ delta, float* __restrict__ dq_acc, __bf16* __restrict__ dK,
                 __bf16* __restrict__ dV, int BH, int N, float c /* scale*log2e */, float scale) {
-    using SM = BwdSmem<D>;
     constexpr int BR = BWD_BR, BC = BWD_BC;
-    constexpr int RS = SM::RS, TS = SM::TS, KTS = SM::KTS, DSS = SM::DSS;
-    extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
-    SM& sm = *reinterpret_cast<SM*>(smem_raw);
+    constexpr int ROWB = 2 * D;                  // bytes per row of a Q/dO/K tile
+    constexpr int CPR = D / 8;
+    constexpr int QTB = BR * ROWB;               // bytes of a Q (or dO) tile
+    constexpr int KTB = BC * ROWB;               // bytes of the K tile
+    constexpr int RPS = 1024 / ROWB;             // rows per 1 KiB copy segment
+    constexpr int QSPW = QTB / 1024 / 4;         // Q segments per wave
+    constexpr int KSPW = KTB / 1024 / 4;         // K segments per wave
+    constexpr int DSS = BC + 8;                  // dS row stride (bf16)
+    constexpr int NQB = BR / 32;
+    constexpr int DQ_UNITS = NQB * (D / 32);     // 32x32 output blocks of dQ per tile
+    constexpr int DQ_PER_WAVE = DQ_UNITS / 4;
+    constexpr int ATOMICS = DQ_PER_WAVE * 16;    // VMEM atomics a wave issues per tile
+    static_assert(QSPW >= 1 && DQ_UNITS % 4 == 0, "tile shapes");
+
+    // Two buffers, each holding a query tile's Q, dO, LSE and D, plus the K
+    // tile and dS.  The buffers are separate LDS objects, so the compiler can
+    // tell that the copies into one do not alias the reads of the other and
+    // need not wait for them.
+    constexpr int BUFB = 2 * QTB + 2 * BR * 4;
+    __shared__ __attribute__((aligned(1024))) char buf0[BUFB];
+    __shared__ __attribute__((aligned(1024))) char buf1[BUFB];
+    __shared__ __attribute__((aligned(1024))) char kbuf[KTB];
+    __shared__ __attribute__((aligned(16))) __bf16 dss[BR * DSS];
+    static_assert(BR == 64, "one wave copies a row statistic of the tile");
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
@@ -130,6 +151,19 @@ bwd_main_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, cons
     const float* Dh = delta + (size_t)bh * N;
     float* dQh = dq_acc + hoff;
 
+    // copy rows [r0, r0 + rows) of a [N, D] tensor into an LDS tile
+    // (segments seg0 .. seg0+nseg-1); rows past the end are clamped to N-1
+    auto issue = [&](const __bf16* src, int r0, char* dst, int seg0, int nseg) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < nseg; ++i) {
+            const int seg = seg0 + i;
+            const int row = seg * RPS + lane / CPR;
+            const int pc = lane % CPR;
+            const size_t grow = (size_t)min(r0 + row, N - 1) * D;
+            g2lds16(src + grow + 8 * (pc ^ bwd_swz<D>(row)), dst + seg * 1024);
+        }
+    };
+
     // this lane's key, and K/V as B operands (column = key, K-slots = dims)
     const int wk0 = k0 + 32 * w;
     const int key = wk0 + l32;
@@ -146,27 +180,18 @@ bwd_main_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, cons
         vf[ks] = as_bf16x8(vu);
     }
 
-    // K^T of the whole tile in LDS (natural key order), B operand of dQ = dS K
-    {
-        constexpr int NBLK = (BC / 4) * (D / 8);
+    // per-lane LDS offsets.  Row-major chunk reads: row 32*b + l32, chunk 2*ks + g.
+    int rd_off[D / 16];
 #pragma unroll
-        for (int i = 0; i < (NBLK + BWD_THREADS - 1) / BWD_THREADS; ++i) {
-            const int blk = tid + BWD_THREADS * i;
-            if (blk < NBLK) {
-                const int kq = blk % (BC / 4), dc = blk / (BC / 4);
-                uint4 r[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int kk = k0 + 4 * kq + j;
-                    r[j] = make_uint4(0, 0, 0, 0);
-                    if (kk < N) r[j] = *reinterpret_cast<const uint4*>(Kh + (size_t)kk * D + 8 * dc);
-                }
-#pragma unroll
-                for (int cc = 0; cc < 8; ++cc)
-                    *reinterpret_cast<uint2*>(sm.kt + (8 * dc + cc) * KTS + 4 * kq) = column4(r[0], r[1], r[2], r[3], cc);
-            }
-        }
-    }
+    for (int ks = 0; ks < D / 16; ++ks) rd_off[ks] = l32 * ROWB + 16 * ((2 * ks + g) ^ bwd_swz<D>(l32));
+    // Transposed reads: rows rt + 4*u (u selects the 4-row group), columns
+    // 32*mb + ct .. +3.  The swizzle depends on (row % 16), i.e. on rt and on
+    // the 4-row group index modulo 4.
+    const int rt = (lane & 15) >> 2;
+    const int ct = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    auto tr_off = [&](int row, int col) __attribute__((always_inline)) -> int {
+        return row * ROWB + 16 * ((col >> 3) ^ bwd_swz<D>(row)) + 2 * (col & 7);
+    };
 
     f32x16 dvt[D / 32], dkt[D / 32];
 #pragma unroll
@@ -177,90 +202,94 @@ bwd_main_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, cons
 
     const int nqt = (N + BR - 1) / BR;
     const int qt_begin = CAUSAL ? (k0 / BR) : 0;
-    for (int qt = qt_begin; qt < nqt; ++qt) {
-        const int q0 = qt * BR;
-        __syncthreads();
-        // stage Q and dO: 4-row x 8-dim blocks, row-major and transposed (query-permuted)
-        {
-            constexpr int NBLK = (BR / 4) * (D / 8);
-#pragma unroll
-            for (int i = 0; i < (NBLK + BWD_THREADS - 1) / BWD_THREADS; ++i) {
-                const int blk = tid + BWD_THREADS * i;
-                if (blk < NBLK) {
-                    const int rq = blk % (BR / 4), dc = blk / (BR / 4);
-                    uint4 qr[4], dr[4];
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const int row = q0 + 4 * rq + j;
-                        qr[j] = make_uint4(0, 0, 0, 0);
-                        dr[j] = qr[j];
-                        if (row < N) {
-                            qr[j] = *reinterpret_cast<const uint4*>(Qh + (size_t)row * D + 8 * dc);
-                            dr[j] = *reinterpret_cast<const uint4*>(dOh + (size_t)row * D + 8 * dc);
-                        }
-                        *reinterpret_cast<uint4*>(sm.q + (4 * rq + j) * RS + 8 * dc) = qr[j];
-                        *reinterpret_cast<uint4*>(sm.dO + (4 * rq + j) * RS + 8 * dc) = dr[j];
-                    }
-                    const int pos = perm16(4 * rq);
-#pragma unroll
-                    for (int cc = 0; cc < 8; ++cc) {
-                        *reinterpret_cast<uint2*>(sm.qt + (8 * dc + cc) * TS + pos) = column4(qr[0], qr[1], qr[2], qr[3], cc);
-                        *reinterpret_cast<uint2*>(sm.dOt + (8 * dc + cc) * TS + pos) = column4(dr[0], dr[1], dr[2], dr[3], cc);
-                    }
-                }
-            }
-            if (tid < BR) {
-                const int row = q0 + tid;
-                // rows past the end get LSE = +inf, so their P is exactly 0
-                sm.lse[tid] = (row < N) ? LSEh[row] * kLog2e : INFINITY;
-                sm.dd[tid] = (row < N) ? Dh[row] : 0.f;
-            }
-        }
-        __syncthreads();
 
-        const bool wave_dead = (!CAUSAL ? false : (wk0 > q0 + BR - 1)) || wk0 >= N;
+    // LSE (wave 0) and D (wave 1) of the query tile starting at row r0, one
+    // row per lane; rows past the end are clamped (and masked later)
+    auto issue_stats = [&](int r0, float* ldst, float* ddst) __attribute__((always_inline)) {
+        const int row = min(r0 + lane, N - 1);
+        if (w == 0) g2lds4(LSEh + row, ldst);
+        if (w == 1) g2lds4(Dh + row, ddst);
+    };
+
+    // buffer layout: Q tile | dO tile | LSE[BR] | D[BR]
+    auto fill = [&](int r0, char* b) __attribute__((always_inline)) {
+        issue(Qh, r0, b, w * QSPW, QSPW);
+        issue(dOh, r0, b + QTB, w * QSPW, QSPW);
+        issue_stats(r0, reinterpret_cast<float*>(b + 2 * QTB), reinterpret_cast<float*>(b + 2 * QTB + 4 * BR));
+    };
+
+    // prologue: K tile (once) and the first query tile
+    issue(Kh, k0, kbuf, w * KSPW, KSPW);
+    if (qt_begin < nqt) fill(qt_begin * BR, buf0);
+    FA_WAIT_VMCNT(0);
+
+    auto tile = [&](int qt, const char* cur, char* nxt) __attribute__((always_inline)) {
+        const char* qs = cur;
+        const char* os = cur + QTB;
+        const float* ls = reinterpret_cast<const float*>(cur + 2 * QTB);
+        const float* ds_ = reinterpret_cast<const float*>(cur + 2 * QTB + 4 * BR);
+        const int q0 = qt * BR;
+        // copies of this tile have landed (the atomics of the previous tile,
+        // issued after them, may still be in flight); every wave is done with
+        // the previous tile, so its buffers may be refilled
+        FA_WAIT_VMCNT(ATOMICS);
+        __builtin_amdgcn_s_barrier();
+        if (qt + 1 < nqt) fill(q0 + BR, nxt);
+
+        const bool wave_dead = (CAUSAL && wk0 > q0 + BR - 1) || wk0 >= N;
         if (wave_dead) {
             // this wave's keys see none of the tile's queries: dS = 0
 #pragma unroll
-            for (int qb = 0; qb < BR / 32; ++qb)
+            for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
-                    sm.ds[(32 * qb + 8 * (r >> 2) + 4 * g + (r & 3)) * DSS + 32 * w + l32] = (__bf16)0.f;
+                    dss[(32 * qb + 8 * (r >> 2) + 4 * g + (r & 3)) * DSS + 32 * w + l32] = (__bf16)0.f;
         } else {
-            f32x16 sP[BR / 32], dP[BR / 32];
+            // LSE and D of this lane's 16 query rows per block (runs of 4)
+            float4 lse4[NQB][4], dd4[NQB][4];
 #pragma unroll
-            for (int qb = 0; qb < BR / 32; ++qb) {
-                sP[qb] = zero16();
-                dP[qb] = zero16();
-#pragma unroll
-                for (int ks = 0; ks < D / 16; ++ks) {
-                    const bf16x8 aq = *reinterpret_cast<const bf16x8*>(sm.q + (32 * qb + l32) * RS + 16 * ks + 8 * g);
-                    sP[qb] = mfma_bf16(aq, kf[ks], sP[qb]);
-                    const bf16x8 ad = *reinterpret_cast<const bf16x8*>(sm.dO + (32 * qb + l32) * RS + 16 * ks + 8 * g);
-                    dP[qb] = mfma_bf16(ad, vf[ks], dP[qb]);
-                }
-            }
-            // P = 2^(c S - LSE*log2e), masked; dS = P (dP - D)
-            const bool need_mask = (k0 + BC > N) || (CAUSAL && wk0 + 31 > q0);
-#pragma unroll
-            for (int qb = 0; qb < BR / 32; ++qb)
+            for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
                 for (int rb = 0; rb < 4; ++rb) {
-                    const int qi = 32 * qb + 8 * rb + 4 * g;
-                    const float4 lse4 = *reinterpret_cast<const float4*>(sm.lse + qi);
-                    const float4 dd4 = *reinterpret_cast<const float4*>(sm.dd + qi);
-                    const float lv[4] = {lse4.x, lse4.y, lse4.z, lse4.w};
-                    const float dv[4] = {dd4.x, dd4.y, dd4.z, dd4.w};
+                    lse4[qb][rb] = *reinterpret_cast<const float4*>(ls + 32 * qb + 8 * rb + 4 * g);
+                    dd4[qb][rb] = *reinterpret_cast<const float4*>(ds_ + 32 * qb + 8 * rb + 4 * g);
+                }
+
+            f32x16 sP[NQB], dP[NQB];
+#pragma unroll
+            for (int qb = 0; qb < NQB; ++qb) {
+                sP[qb] = zero16();
+                dP[qb] = zero16();
+            }
+#pragma unroll
+            for (int ks = 0; ks < D / 16; ++ks)
+#pragma unroll
+                for (int qb = 0; qb < NQB; ++qb) {
+                    const bf16x8 aq = *reinterpret_cast<const bf16x8*>(qs + 32 * qb * ROWB + rd_off[ks]);
+                    sP[qb] = mfma_bf16(aq, kf[ks], sP[qb]);
+                    const bf16x8 ad = *reinterpret_cast<const bf16x8*>(os + 32 * qb * ROWB + rd_off[ks]);
+                    dP[qb] = mfma_bf16(ad, vf[ks], dP[qb]);
+                }
+            // P = 2^(c S - LSE log2 e), masked; dS = P (dP - D)
+            const bool need_mask = (k0 + BC > N) || (q0 + BR > N) || (CAUSAL && wk0 + 31 > q0);
+#pragma unroll
+            for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+                for (int rb = 0; rb < 4; ++rb) {
+                    const float lv[4] = {lse4[qb][rb].x, lse4[qb][rb].y, lse4[qb][rb].z, lse4[qb][rb].w};
+                    const float dv[4] = {dd4[qb][rb].x, dd4[qb][rb].y, dd4[qb][rb].z, dd4[qb][rb].w};
 #pragma unroll
                     for (int t = 0; t < 4; ++t) {
                         const int r = 4 * rb + t;
-                        float p = exp2_fast(fmaf(sP[qb][r], c, -lv[t]));
-                        if (need_mask && (!key_live || (CAUSAL && key > q0 + qi + t))) p = 0.f;
+                        const int qrow = q0 + 32 * qb + 8 * rb + 4 * g + t;
+                        float p = exp2_fast(fmaf(sP[qb][r], c, -lv[t] * kLog2e));
+                        if (need_mask && (!key_live || qrow >= N || (CAUSAL && key > qrow))) p = 0.f;
                         sP[qb][r] = p;
                         dP[qb][r] = p * (dP[qb][r] - dv[t]);
                     }
                 }
-            // dV^T += dO^T P ; dK^T += Q^T dS  (K-slots = queries, permuted)
+            // dV^T += dO^T P ; dK^T += Q^T dS  (K-slots = queries, permuted as
+            // in the C layout; the transposed reads follow the same order)
 #pragma unroll
             for (int ks = 0; ks < BR / 16; ++ks) {
                 const int qb = ks >> 1, h = ks & 1;
@@ -272,44 +301,56 @@ bwd_main_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, cons
                 }
                 const bf16x8 pb = as_bf16x8(make_uint4(pk[0], pk[1], pk[2], pk[3]));
                 const bf16x8 sb = as_bf16x8(make_uint4(sk[0], sk[1], sk[2], sk[3]));
+                const int row_lo = 16 * ks + 4 * g + rt;       // queries of K-slots j = 0..3
 #pragma unroll
                 for (int mb = 0; mb < D / 32; ++mb) {
-                    const bf16x8 ad = *reinterpret_cast<const bf16x8*>(sm.dOt + (32 * mb + l32) * TS + 16 * ks + 8 * g);
-                    dvt[mb] = mfma_bf16(ad, pb, dvt[mb]);
-                    const bf16x8 aq = *reinterpret_cast<const bf16x8*>(sm.qt + (32 * mb + l32) * TS + 16 * ks + 8 * g);
-                    dkt[mb] = mfma_bf16(aq, sb, dkt[mb]);
+                    const int col = 32 * mb + ct;
+                    const uint2 dlo = lds_read_tr16x4(os + tr_off(row_lo, col));
+                    const uint2 dhi = lds_read_tr16x4(os + tr_off(row_lo + 8, col));
+                    dvt[mb] = mfma_bf16(as_bf16x8(make_uint4(dlo.x, dlo.y, dhi.x, dhi.y)), pb, dvt[mb]);
+                    const uint2 qlo = lds_read_tr16x4(qs + tr_off(row_lo, col));
+                    const uint2 qhi = lds_read_tr16x4(qs + tr_off(row_lo + 8, col));
+                    dkt[mb] = mfma_bf16(as_bf16x8(make_uint4(qlo.x, qlo.y, qhi.x, qhi.y)), sb, dkt[mb]);
                 }
             }
             // dS -> LDS as [query][key] bf16 for dQ
 #pragma unroll
-            for (int qb = 0; qb < BR / 32; ++qb)
+            for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
-                    sm.ds[(32 * qb + 8 * (r >> 2) + 4 * g + (r & 3)) * DSS + 32 * w + l32] = (__bf16)dP[qb][r];
+                    dss[(32 * qb + 8 * (r >> 2) + 4 * g + (r & 3)) * DSS + 32 * w + l32] = (__bf16)dP[qb][r];
         }
-        __syncthreads();
+        FA_WAIT_LGKM0();
+        __builtin_amdgcn_s_barrier();
 
-        // dQ_tile += dS K : (BR/32) x (D/32) output blocks shared by the waves
-        constexpr int UNITS = (BR / 32) * (D / 32);
+        // dQ_tile += dS K : DQ_UNITS 32x32 output blocks shared by the waves.
+        // K-slots are keys in natural order; the K^T operand is read
+        // transposed from the row-major K tile.
 #pragma unroll
-        for (int u0 = 0; u0 < UNITS; u0 += BWD_THREADS / 64) {
-            const int u = u0 + w;
-            if (u < UNITS) {
-                const int qb = u / (D / 32), nb = u % (D / 32);
-                f32x16 acc = zero16();
+        for (int u0 = 0; u0 < DQ_PER_WAVE; ++u0) {
+            const int u = u0 * 4 + w;
+            const int qb = u / (D / 32), nb = u % (D / 32);
+            f32x16 acc = zero16();
 #pragma unroll
-                for (int ks = 0; ks < BC / 16; ++ks) {
-                    const bf16x8 a = *reinterpret_cast<const bf16x8*>(sm.ds + (32 * qb + l32) * DSS + 16 * ks + 8 * g);
-                    const bf16x8 b = *reinterpret_cast<const bf16x8*>(sm.kt + (32 * nb + l32) * KTS + 16 * ks + 8 * g);
-                    acc = mfma_bf16(a, b, acc);
-                }
+            for (int ks = 0; ks < BC / 16; ++ks) {
+                const bf16x8 a = *reinterpret_cast<const bf16x8*>(dss + (32 * qb + l32) * DSS + 16 * ks + 8 * g);
+                const int row = 16 * ks + 8 * g + rt;
+                const int col = 32 * nb + ct;
+                const uint2 lo = lds_read_tr16x4(kbuf + tr_off(row, col));
+                const uint2 hi = lds_read_tr16x4(kbuf + tr_off(row + 4, col));
+                acc = mfma_bf16(a, as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)), acc);
+            }
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int row = q0 + 32 * qb + 8 * (r >> 2) + 4 * g + (r & 3);
-                    if (row < N) unsafeAtomicAdd(dQh + (size_t)row * D + 32 * nb + l32, acc[r]);
-                }
+            for (int r = 0; r < 16; ++r) {
+                const int row = q0 + 32 * qb + 8 * (r >> 2) + 4 * g + (r & 3);
+                if (row < N) unsafeAtomicAdd(dQh + (size_t)row * D + 32 * nb + l32, acc[r]);
             }
         }
+    };
+
+    for (int qt = qt_begin; qt < nqt; qt += 2) {
+        tile(qt, buf0, buf1);
+        if (qt + 1 < nqt) tile(qt + 1, buf1, buf0);
     }
 
     // dV = (dV^T)^T, dK = scale (dK^T)^T: lane holds key `key`, dims in runs of 4
@@ -349,13 +390,10 @@ template <int D, bool CAUSAL>
 hipError_t launch_main(const BwdArgs& a) {
     const int BH = a.B * a.H;
     const int nkt = (a.N + BWD_BC - 1) / BWD_BC;
-    const size_t smem = sizeof(BwdSmem<D>);
-    auto kern = bwd_main_kernel<D, CAUSAL>;
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3((unsigned)(nkt * BH)), dim3(BWD_THREADS), smem, (hipStream_t)a.stream,
-                       (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (const __bf16*)a.dout, a.lse,
-                       a.delta, a.dq_acc, (__bf16*)a.dk, (__bf16*)a.dv, BH, a.N, a.scale * kLog2e, a.scale);
+    hipLaunchKernelGGL((bwd_main_kernel<D, CAUSAL>), dim3((unsigned)(nkt * BH)), dim3(BWD_THREADS), 0,
+                       (hipStream_t)a.stream, (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v,
+                       (const __bf16*)a.dout, a.lse, a.delta, a.dq_acc, (__bf16*)a.dk, (__bf16*)a.dv, BH, a.N,
+                       a.scale * kLog2e, a.scale);
     return hipGetLastError();
 }
 

@@ -50,6 +50,12 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
     return __builtin_bit_cast(uint32_t, v);
 }
 
+// acc + lo + hi of a packed bf16 pair (v_dot2c_f32_bf16 against (1, 1)).
+__device__ __forceinline__ float sum_bf16x2(uint32_t packed, float acc) {
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, packed), one, acc, false);
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
 
@@ -69,6 +75,12 @@ typedef __attribute__((address_space(3))) void lds_void;
 // Lane l's 16 bytes land at lds_base + 16*l; lds_base must be wave-uniform.
 __device__ __forceinline__ void g2lds16(const void* gsrc, void* lds_base) {
     __builtin_amdgcn_global_load_lds(gsrc, (lds_void*)lds_base, 16, 0, 0);
+}
+
+// 4-byte global -> LDS copy (global_load_lds_dword): lane l's word lands at
+// lds_base + 4*l.
+__device__ __forceinline__ void g2lds4(const void* gsrc, void* lds_base) {
+    __builtin_amdgcn_global_load_lds(gsrc, (lds_void*)lds_base, 4, 0, 0);
 }
 
 // Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,

@@ -11,16 +11,20 @@
 // sequences fill the chip ("Flash Attention uitgelegd", FA2 section on
 // parallelism over the sequence length).
 //
-// bf16 path (d = 64 or 128): four waves, 32 query rows each.  Per key tile
-// of BC = 64 keys a wave computes S^T = K Q^T (keys x queries) with
-// v_mfma_f32_32x32x16_bf16: K comes from LDS, Q^T stays in registers for the
-// whole kernel.  In the C layout each lane then holds one query row and 16 of
-// the tile's keys, so row max and row sum are in-lane work plus one exchange
-// with lane ^ 32.  The probabilities, rounded to bf16, are already a valid B
-// operand of O^T += V^T P^T, given V^T staged in LDS with the matching key
-// permutation; O^T again gives each lane one query row.  The scale is folded
-// into the exp2 argument and O is normalised once at the end (the FA2 point
-// about minimising non-matmul work).
+// bf16 path (d = 64 or 128): four waves, 32 query rows each, two
+// workgroups per CU.  Per key tile of BC = 64 keys a wave computes
+// S^T = K Q^T (keys x queries) with v_mfma_f32_32x32x16_bf16: K comes from
+// LDS, Q^T stays in registers for the whole kernel.  In the C layout each lane
+// then holds one query row and 16 of the tile's keys, so row max and row sum
+// are in-lane work plus one exchange with lane ^ 32.  The probabilities,
+// rounded to bf16, are already a valid B operand of O^T += V^T P^T; the V^T A
+// operand is read from the row-major V tile with the transposing LDS read.
+// O^T again gives each lane one query row.  K and V tiles are copied
+// global -> LDS without passing through registers, double-buffered.  The scale
+// is folded into the exp2 argument, the running max is only raised when it
+// grows by more than 2^8 (exact: the same reference max is used for the
+// numerator and the denominator), and O is normalised once at the end (the
+// FA2 point about minimising non-matmul work).
 //
 // fp32 path: same structure on v_mfma_f32_32x32x2_f32 with BC = 32; V needs no
 // transpose because each fp32 K-slot holds a single key.
@@ -73,14 +77,18 @@ fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     constexpr int TILEB = BC * ROWB;         // bytes per K (or V) tile
     constexpr int RPS = 1024 / ROWB;         // rows per 1 KiB copy segment
     constexpr int SPW = TILEB / 1024 / 4;    // copy segments per wave per tile
+    constexpr int NKB = BC / 32;             // 32-key blocks per tile
     constexpr float TAU = 8.f;               // lazy-rescale threshold, log2 units
     static_assert(SPW >= 1, "tile too small for four waves");
 
-    // Two buffers, each a K tile followed by a V tile.  They are separate
-    // objects so that the compiler can tell that the copies into one buffer do
-    // not alias the reads of the other, and need not wait for them.
-    __shared__ __attribute__((aligned(1024))) char smem0[2 * TILEB];
-    __shared__ __attribute__((aligned(1024))) char smem1[2 * TILEB];
+    // Two buffer pairs (K tile, V tile): the copies of tile kt+1 run while
+    // tile kt is computed.  Four separate LDS objects let the compiler see
+    // that the copies into one pair never alias the reads of the other, so it
+    // does not wait for them before reading.
+    __shared__ __attribute__((aligned(1024))) char kb0[TILEB];
+    __shared__ __attribute__((aligned(1024))) char kb1[TILEB];
+    __shared__ __attribute__((aligned(1024))) char vb0[TILEB];
+    __shared__ __attribute__((aligned(1024))) char vb1[TILEB];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
@@ -104,85 +112,77 @@ fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
         qf[ks] = as_bf16x8(u);
     }
 
+    const int kv_end = CAUSAL ? min(N, q0 + BR) : N;
+    const int nkt = (kv_end + BC - 1) / BC;                 // tiles the workgroup streams
+    const int wrow0 = q0 + 32 * w;
+    // tiles this wave computes on (a causal wave stops at its diagonal)
+    const int nkt_w = (wrow0 >= N) ? 0 : (CAUSAL ? min(nkt, (wrow0 + 31) / BC + 1) : nkt);
+
+    // Copy K or V tile kt into an LDS buffer.  Rows past the end are clamped
+    // to row N-1: they are masked (K) or weighted by 0 (V).
+    auto issue = [&](const __bf16* src, int kt, char* dst, bool is_v) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < SPW; ++i) {
+            const int seg = w * SPW + i;
+            const int row = seg * RPS + lane / CPR;
+            const int pc = lane % CPR;
+            const size_t grow = (size_t)min(kt * BC + row, N - 1) * D;
+            const int lc = pc ^ (is_v ? v_swz<D>(row) : k_swz<D>(row));
+            g2lds16(src + grow + 8 * lc, dst + seg * 1024);
+        }
+    };
+
+    // Per-lane LDS byte offsets, fixed for the whole kernel (the swizzles only
+    // depend on the low bits of the row, which the tile loops do not change).
+    //  K: A operand of S^T, row 32*kb + l32, logical chunk 2*ks + g.
+    int k_off[D / 16];
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) k_off[ks] = l32 * ROWB + 16 * ((2 * ks + g) ^ k_swz<D>(l32));
+    //  V: transposed read of rows 16*ks + 8*h + vr, columns 32*mb + vc .. +3.
+    const int vr = 4 * g + ((lane & 15) >> 2);
+    const int vc = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    const int vsw = v_swz<D>(vr) >> 2;   // XOR on the chunk bits above the 4-chunk group
+    int v_off[D / 32];
+#pragma unroll
+    for (int mb = 0; mb < D / 32; ++mb) v_off[mb] = vr * ROWB + 16 * (4 * (mb ^ vsw) + (vc >> 3)) + 2 * (vc & 7);
+
+    // key kv0 + 32*kb + 8*(r/4) + 4*g + r%4 is hidden iff 32*kb + 8*(r/4) + r%4 > lim
+    const int last_visible = CAUSAL ? min(qrow, N - 1) : N - 1;
+
     f32x16 oacc[D / 32];
 #pragma unroll
     for (int mb = 0; mb < D / 32; ++mb) oacc[mb] = zero16();
     float m_ref = -INFINITY;   // reference max (log2 units) the exponentials use
     float l_run = 0.f;         // this lane's share of the running sum
 
-    const int kv_end = CAUSAL ? min(N, q0 + BR) : N;
-    const int nkt = (kv_end + BC - 1) / BC;
-
-    // Copy the K/V tile starting at key kv0 into buffer buf.  Rows past the
-    // end are clamped to row N-1: they are masked (K) or weighted by 0 (V).
-    auto issue = [&](int kv0, char* buf) {
-        char* kdst = buf;
-        char* vdst = buf + TILEB;
+    auto qk = [&](const char* Ks, f32x16* s) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < SPW; ++i) {
-            const int seg = w * SPW + i;
-            const int row = seg * RPS + lane / CPR;
-            const int pc = lane % CPR;
-            const size_t grow = (size_t)min(kv0 + row, N - 1) * D;
-            g2lds16(Kh + grow + 8 * (pc ^ k_swz<D>(row)), kdst + seg * 1024);
-            g2lds16(Vh + grow + 8 * (pc ^ v_swz<D>(row)), vdst + seg * 1024);
-        }
-    };
-
-    // per-lane constant parts of the LDS addresses
-    const int gq = lane >> 4, li = lane & 15;
-    const int k_rd_row0 = l32;                        // + 32*kb
-    const int v_rd_row = 4 * g + (li >> 2);           // + 16*ks + 8*h
-    const int v_rd_col = 16 * (gq & 1) + 4 * (li & 3);  // + 32*mb (elements)
-
-    const int wrow0 = q0 + 32 * w;
-    // One step: wait for tile kt (in `cur`), start copying tile kt+1 into
-    // `nxt`, then compute on `cur`.  Called with the buffers swapped on odd
-    // steps so that both are compile-time distinct objects.
-    auto step = [&](int kt, const char* cur, char* nxt) {
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        if (kt + 1 < nkt) issue((kt + 1) * BC, nxt);
-
-        const int kv0 = kt * BC;
-        if (wrow0 >= N) return;                         // padding wave
-        if (CAUSAL && kv0 > wrow0 + 31) return;         // tile entirely above the diagonal
-        const char* Ks = cur;
-        const char* Vs = cur + TILEB;
-
-        // S^T = K Q^T : BC/32 blocks of 32 keys
-        f32x16 s[BC / 32];
-#pragma unroll
-        for (int kb = 0; kb < BC / 32; ++kb) s[kb] = zero16();
+        for (int kb = 0; kb < NKB; ++kb) s[kb] = zero16();
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks)
 #pragma unroll
-            for (int kb = 0; kb < BC / 32; ++kb) {
-                const int row = 32 * kb + k_rd_row0;
-                const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-                    Ks + row * ROWB + 16 * ((2 * ks + g) ^ k_swz<D>(row)));
+            for (int kb = 0; kb < NKB; ++kb) {
+                const bf16x8 a = *reinterpret_cast<const bf16x8*>(Ks + 32 * kb * ROWB + k_off[ks]);
                 s[kb] = mfma_bf16(a, qf[ks], s[kb]);
             }
-
-        const bool need_mask = (kv0 + BC > N) || (CAUSAL && kv0 + BC - 1 > wrow0);
-        if (need_mask) {
-#pragma unroll
-            for (int kb = 0; kb < BC / 32; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = kv0 + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
-                    if (key >= N || (CAUSAL && key > qrow)) s[kb][r] = -INFINITY;
-                }
-        }
-
+    };
+    // mask tile kt of S (branch-free; lim is large when nothing is hidden) and
+    // return the row max in log2 units
+    auto mask_max = [&](int kt, f32x16* s) __attribute__((always_inline)) -> float {
+        const int lim = last_visible - kt * BC - 4 * g;
         float mx = -INFINITY;
 #pragma unroll
-        for (int kb = 0; kb < BC / 32; ++kb)
+        for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-        mx = xor32_max(mx) * c;
-        // Lazy rescaling: the exponentials use a reference max that is only
-        // raised when the row max exceeds it by more than TAU (p <= 2^TAU).
+            for (int r = 0; r < 16; ++r) {
+                s[kb][r] = (32 * kb + 8 * (r >> 2) + (r & 3) > lim) ? -INFINITY : s[kb][r];
+                mx = fmaxf(mx, s[kb][r]);
+            }
+        return xor32_max(mx) * c;
+    };
+    // Lazy rescaling: the exponentials use a reference max that is only raised
+    // when the row max exceeds it by more than TAU (so p <= 2^TAU).
+    auto rescale = [&](float mx) __attribute__((always_inline)) {
         if (__any(mx > m_ref + TAU)) {
             const float m_new = fmaxf(m_ref, mx);
             const float alpha = exp2_fast(m_ref - m_new);   // 0 on the first tile
@@ -193,13 +193,14 @@ fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 #pragma unroll
                 for (int r = 0; r < 16; ++r) oacc[mb][r] *= alpha;
         }
+    };
+    // P (bf16) laid out as the B operand of O^T += V^T P^T.  The row sum adds
+    // the same bf16-rounded values the PV product uses (dot2 against 1).
+    auto probs = [&](const f32x16* s, bf16x8* pb) __attribute__((always_inline)) {
         const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
-
-        // P (bf16) laid out as the B operand of O^T += V^T P^T
-        bf16x8 pb[BC / 16];
-        float psum = 0.f;
+        float psum[2] = {0.f, 0.f};
 #pragma unroll
-        for (int kb = 0; kb < BC / 32; ++kb)
+        for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 uint32_t pk[4];
@@ -207,34 +208,62 @@ fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                 for (int j = 0; j < 8; j += 2) {
                     const float p0 = exp2_fast(fmaf(s[kb][8 * h + j], c, -m_use));
                     const float p1 = exp2_fast(fmaf(s[kb][8 * h + j + 1], c, -m_use));
-                    psum += p0 + p1;
                     pk[j / 2] = pack_bf16x2(p0, p1);
+                    psum[h] = sum_bf16x2(pk[j / 2], psum[h]);
                 }
                 pb[2 * kb + h] = as_bf16x8(make_uint4(pk[0], pk[1], pk[2], pk[3]));
             }
-        l_run += psum;
-
-        // O^T += V^T P^T ; V^T operand read transposed from the row-major tile
+        l_run += psum[0] + psum[1];
+    };
+    // O^T += V^T P^T ; V^T operand read transposed from the row-major tile
+    auto pv = [&](const char* Vs, const bf16x8* pb) __attribute__((always_inline)) {
 #pragma unroll
         for (int ks = 0; ks < BC / 16; ++ks)
 #pragma unroll
             for (int mb = 0; mb < D / 32; ++mb) {
-                uint2 part[2];
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const int row = 16 * ks + 8 * h + v_rd_row;
-                    const int col = 32 * mb + v_rd_col;
-                    part[h] = lds_read_tr16x4(Vs + row * ROWB + 16 * ((col >> 3) ^ v_swz<D>(row)) + 2 * (col & 7));
-                }
-                const bf16x8 a = as_bf16x8(make_uint4(part[0].x, part[0].y, part[1].x, part[1].y));
+                const uint2 lo = lds_read_tr16x4(Vs + (16 * ks) * ROWB + v_off[mb]);
+                const uint2 hi = lds_read_tr16x4(Vs + (16 * ks + 8) * ROWB + v_off[mb]);
+                const bf16x8 a = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
                 oacc[mb] = mfma_bf16(a, pb[ks], oacc[mb]);
             }
     };
 
-    if (nkt > 0) issue(0, smem0);
+    // One tile: wait for its copies, start the next tile's copies into the
+    // other buffer pair, then S = K Q^T, mask, softmax and O += V^T P.
+    auto step = [&](int kt, const char* kc, const char* vcb, char* kn, char* vn) __attribute__((always_inline)) {
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (kt + 1 < nkt) {
+            issue(Kh, kt + 1, kn, false);
+            issue(Vh, kt + 1, vn, true);
+        }
+        if (kt >= nkt_w) return;
+        f32x16 s[NKB];
+        qk(kc, s);
+        float mx;
+        const bool need_mask = (kt * BC + BC > N) || (CAUSAL && kt * BC + BC - 1 > wrow0);
+        if (need_mask) {
+            mx = mask_max(kt, s);
+        } else {
+            mx = -INFINITY;
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+            mx = xor32_max(mx) * c;
+        }
+        rescale(mx);
+        bf16x8 pb[BC / 16];
+        probs(s, pb);
+        pv(vcb, pb);
+    };
+    if (nkt > 0) {
+        issue(Kh, 0, kb0, false);
+        issue(Vh, 0, vb0, true);
+    }
     for (int kt = 0; kt < nkt; kt += 2) {
-        step(kt, smem0, smem1);
-        if (kt + 1 < nkt) step(kt + 1, smem1, smem0);
+        step(kt, kb0, vb0, kb1, vb1);
+        if (kt + 1 < nkt) step(kt + 1, kb1, vb1, kb0, vb0);
     }
 
     const float l_tot = xor32_sum(l_run);
