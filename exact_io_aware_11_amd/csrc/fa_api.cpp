@@ -81,10 +81,7 @@ fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, fa_dtyp
 
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d) {
     if (!dims_ok(B, H, N) || d < 1 || !total_ok(B, H, N, d)) return 0;
-    const size_t rows = (size_t)B * H * N;
-    const size_t acc = rows * (size_t)d * sizeof(float);
-    const size_t delta = rows * sizeof(float);
-    return ((acc + 255) & ~(size_t)255) + delta;
+    return (size_t)B * H * N * sizeof(float);
 }
 
 fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, fa_dtype_t o_dtype,
@@ -101,11 +98,8 @@ fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, f
     const size_t need = fa_bwd_workspace_bytes(B, H, N, d);
     if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
     if (!aligned16(workspace)) return FA_ERR_ALIGN;
-    const size_t rows = (size_t)B * H * N;
-    float* acc = static_cast<float*>(workspace);
-    float* delta = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                            (((rows * (size_t)d * sizeof(float)) + 255) & ~(size_t)255));
-    fa::BwdArgs a{q, k, v, o, lse, dout, dq, dk, dv, acc, delta, B, H, N, d, o_dtype == FA_BF16, causal != 0,
+    float* delta = static_cast<float*>(workspace);
+    fa::BwdArgs a{q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d, o_dtype == FA_BF16, causal != 0,
                   scale, stream};
     return from_hip(fa::launch_bwd(a));
 }

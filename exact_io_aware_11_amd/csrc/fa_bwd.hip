@@ -9,24 +9,29 @@
 //     dS = P * (dP - D),  dK = scale dS^T Q,  dQ = scale dS K.
 //
 // Three launches on the caller's stream:
-//   1. bwd_prep:  D = rowsum(dO * O) in fp32, and the fp32 dQ accumulator
-//                 cleared to zero.
-//   2. bwd_main:  one workgroup per tile of BC = 128 keys of one head (4 waves,
-//                 32 keys each).  K and V of the tile stay in registers (and K
-//                 also in LDS); the workgroup walks the query tiles (BR = 64
-//                 rows) that can see its keys.  Q, dO, LSE and D of the next
-//                 query tile are copied global -> LDS while the current one is
-//                 computed.  dK^T and dV^T accumulate in registers; dS goes
-//                 through LDS so that all four waves contribute to
-//                 dQ_i += dS K_j, which is added into the fp32 accumulator with
-//                 global atomics that stay in flight across the barriers.
-//   3. bwd_dq:    dQ = scale * accumulator, rounded to bf16.
+//   1. bwd_prep:  D = rowsum(dO * O) in fp32.
+//   2. bwd_dkdv:  one workgroup per tile of BC = 128 keys of one head (4 waves,
+//                 32 keys each), walking the query tiles (BR = 64 rows) that can
+//                 see its keys.  K and V of the tile stay in registers; Q, dO,
+//                 LSE and D of the next query tile are copied global -> LDS
+//                 while the current one is computed.  dK^T and dV^T accumulate
+//                 in registers and are stored once.
+//   3. bwd_dq:    one workgroup per tile of 128 query rows, streaming the K/V
+//                 tiles of its head like the forward pass: it recomputes S, P
+//                 and dP, forms dS and accumulates dQ^T = K^T dS^T in
+//                 registers.  Recomputing S and dP a second time costs three
+//                 more matrix products than accumulating dQ with atomics from
+//                 the key-tile kernel, but those atomics measured slower than
+//                 the products, and this way dQ needs no fp32 accumulator, no
+//                 extra pass and is deterministic.
 //
-// Layout trick (as in the forward): S is computed with queries as MFMA rows
-// and keys as columns, so each lane holds one key and 16 queries; those
-// registers are directly the K-slot-ordered B operands of dV^T = dO^T P and
-// dK^T = Q^T dS, whose Q^T / dO^T operands are read with the transposing LDS
-// read in the matching query order.
+// Layout trick (as in the forward): with queries as MFMA rows and keys as
+// columns, each lane holds one key and 16 queries, and those registers are
+// directly the K-slot-ordered B operands of dV^T = dO^T P and dK^T = Q^T dS;
+// with keys as rows and queries as columns (dQ kernel) each lane holds one
+// query and 16 keys, the B operand of dQ^T = K^T dS^T.  The transposed A
+// operands (Q^T, dO^T, K^T) are read with the transposing LDS read in the
+// matching order.
 #include "fa_common.hpp"
 #include "fa_internal.hpp"
 
@@ -34,17 +39,23 @@ namespace fa {
 
 namespace {
 
-constexpr int BWD_BR = 64;       // query rows per inner step
+#ifndef FA_BWD_BR
+#define FA_BWD_BR 64
+#endif
+#ifndef FA_BWD_WAVES
+#define FA_BWD_WAVES 1
+#endif
+constexpr int BWD_BR = FA_BWD_BR;       // query rows per inner step
 constexpr int BWD_BC = 128;      // keys per workgroup (4 waves x 32)
 constexpr int BWD_THREADS = 256;
 
 // ---------------------------------------------------------------------------
-// 1. D = rowsum(dO * O); zero the dQ accumulator.  d/8 lanes per row.
+// 1. D = rowsum(dO * O).  d/8 lanes per row.
 // ---------------------------------------------------------------------------
 template <int D, bool O_BF16>
 __global__ void __launch_bounds__(256)
 bwd_prep_kernel(const void* __restrict__ O, const __bf16* __restrict__ dO, float* __restrict__ delta,
-                float* __restrict__ dq_acc, long long rows) {
+                long long rows) {
     constexpr int LPR = D / 8;
     const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
     const long long row = gid / LPR;
@@ -75,9 +86,6 @@ bwd_prep_kernel(const void* __restrict__ O, const __bf16* __restrict__ dO, float
             acc = fmaf(bf16_lo(dp[j]), ov[2 * j], acc);
             acc = fmaf(bf16_hi(dp[j]), ov[2 * j + 1], acc);
         }
-        const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
-        *reinterpret_cast<float4*>(dq_acc + base) = z;
-        *reinterpret_cast<float4*>(dq_acc + base + 4) = z;
     }
     acc = (LPR == 16) ? dpp_sum16(acc) : dpp_sum8(acc);
     if (live && part == 0) delta[row] = acc;
@@ -86,53 +94,38 @@ bwd_prep_kernel(const void* __restrict__ O, const __bf16* __restrict__ dO, float
 // ---------------------------------------------------------------------------
 // 2. main kernel
 // ---------------------------------------------------------------------------
-// Q, dO and K tiles live in LDS row-major (2*D bytes per row, no padding),
+// Q and dO tiles live in LDS row-major (2*D bytes per row, no padding),
 // filled by direct global -> LDS copies.  Each is read two ways: 16-byte
 // chunks by 32 consecutive rows (A operands of S = Q K^T and dP = dO V^T) and
-// with the transposing 8-byte read (Q^T, dO^T and K^T operands, 4 rows x 32
-// bytes per 16-lane group).  The XOR of the 16-byte chunk index with
-// 4*(row%4) + (row/4)%4 keeps both patterns free of bank conflicts.
-template <int D>
-__device__ __forceinline__ int bwd_swz(int row) {
-    return (4 * (row & 3) + ((row >> 2) & 3)) & (D / 8 - 1);
-}
-
+// with the transposing 8-byte read (Q^T and dO^T operands); rt_swz keeps both
+// patterns free of bank conflicts.
 // s_waitcnt with only vmcnt constrained (expcnt / lgkmcnt left at their max).
 #define FA_WAIT_VMCNT(n) \
     __builtin_amdgcn_s_waitcnt((((n) & 15) | (((n) >> 4) << 14)) | (7 << 4) | (15 << 8))
 #define FA_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4))
 
 template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(BWD_THREADS)
-bwd_main_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
+__global__ void __launch_bounds__(BWD_THREADS) __attribute__((amdgpu_waves_per_eu(FA_BWD_WAVES)))
+bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
                 const __bf16* __restrict__ dO, const float* __restrict__ LSE,
-                const float* __restrict__ delta, float* __restrict__ dq_acc, __bf16* __restrict__ dK,
+                const float* __restrict__ delta, __bf16* __restrict__ dK,
                 __bf16* __restrict__ dV, int BH, int N, float c /* scale*log2e */, float scale) {
     constexpr int BR = BWD_BR, BC = BWD_BC;
     constexpr int ROWB = 2 * D;                  // bytes per row of a Q/dO/K tile
     constexpr int CPR = D / 8;
     constexpr int QTB = BR * ROWB;               // bytes of a Q (or dO) tile
-    constexpr int KTB = BC * ROWB;               // bytes of the K tile
     constexpr int RPS = 1024 / ROWB;             // rows per 1 KiB copy segment
     constexpr int QSPW = QTB / 1024 / 4;         // Q segments per wave
-    constexpr int KSPW = KTB / 1024 / 4;         // K segments per wave
-    constexpr int DSS = BC + 8;                  // dS row stride (bf16)
     constexpr int NQB = BR / 32;
-    constexpr int DQ_UNITS = NQB * (D / 32);     // 32x32 output blocks of dQ per tile
-    constexpr int DQ_PER_WAVE = DQ_UNITS / 4;
-    constexpr int ATOMICS = DQ_PER_WAVE * 16;    // VMEM atomics a wave issues per tile
-    static_assert(QSPW >= 1 && DQ_UNITS % 4 == 0, "tile shapes");
+    static_assert(QSPW >= 1, "tile shapes");
 
-    // Two buffers, each holding a query tile's Q, dO, LSE and D, plus the K
-    // tile and dS.  The buffers are separate LDS objects, so the compiler can
-    // tell that the copies into one do not alias the reads of the other and
-    // need not wait for them.
+    // Two buffers, each holding a query tile's Q, dO, LSE and D.  They are
+    // separate LDS objects, so the compiler can tell that the copies into one
+    // do not alias the reads of the other and need not wait for them.
     constexpr int BUFB = 2 * QTB + 2 * BR * 4;
     __shared__ __attribute__((aligned(1024))) char buf0[BUFB];
     __shared__ __attribute__((aligned(1024))) char buf1[BUFB];
-    __shared__ __attribute__((aligned(1024))) char kbuf[KTB];
-    __shared__ __attribute__((aligned(16))) __bf16 dss[BR * DSS];
-    static_assert(BR == 64, "one wave copies a row statistic of the tile");
+    static_assert(BR <= 64, "one wave copies a row statistic of the tile");
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
@@ -149,7 +142,6 @@ bwd_main_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, cons
     const __bf16* dOh = dO + hoff;
     const float* LSEh = LSE + (size_t)bh * N;
     const float* Dh = delta + (size_t)bh * N;
-    float* dQh = dq_acc + hoff;
 
     // copy rows [r0, r0 + rows) of a [N, D] tensor into an LDS tile
     // (segments seg0 .. seg0+nseg-1); rows past the end are clamped to N-1
@@ -160,7 +152,7 @@ bwd_main_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, cons
             const int row = seg * RPS + lane / CPR;
             const int pc = lane % CPR;
             const size_t grow = (size_t)min(r0 + row, N - 1) * D;
-            g2lds16(src + grow + 8 * (pc ^ bwd_swz<D>(row)), dst + seg * 1024);
+            g2lds16(src + grow + 8 * (pc ^ rt_swz<D>(row)), dst + seg * 1024);
         }
     };
 
@@ -183,15 +175,22 @@ bwd_main_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, cons
     // per-lane LDS offsets.  Row-major chunk reads: row 32*b + l32, chunk 2*ks + g.
     int rd_off[D / 16];
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) rd_off[ks] = l32 * ROWB + 16 * ((2 * ks + g) ^ bwd_swz<D>(l32));
-    // Transposed reads: rows rt + 4*u (u selects the 4-row group), columns
-    // 32*mb + ct .. +3.  The swizzle depends on (row % 16), i.e. on rt and on
-    // the 4-row group index modulo 4.
+    for (int ks = 0; ks < D / 16; ++ks) rd_off[ks] = l32 * ROWB + 16 * ((2 * ks + g) ^ rt_swz<D>(l32));
+    // Transposed reads: the 16-lane group of this lane reads rows r..r+3 and
+    // columns 32*mb + ct .. +15, lane (rt, ct): row r + rt, 4 columns at ct.
+    // Row offsets that are multiples of 16 leave the swizzle unchanged, so the
+    // Q^T / dO^T rows 16*ks + 4*g + 8*h + rt need one per-lane offset per
+    // (h, mb): qt_off[h][mb] + 16*ks*ROWB.
     const int rt = (lane & 15) >> 2;
     const int ct = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
     auto tr_off = [&](int row, int col) __attribute__((always_inline)) -> int {
-        return row * ROWB + 16 * ((col >> 3) ^ bwd_swz<D>(row)) + 2 * (col & 7);
+        return row * ROWB + 16 * ((col >> 3) ^ rt_swz<D>(row)) + 2 * (col & 7);
     };
+    int qt_off[2][D / 32];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int mb = 0; mb < D / 32; ++mb) qt_off[h][mb] = tr_off(4 * g + 8 * h + rt, 32 * mb + ct);
 
     f32x16 dvt[D / 32], dkt[D / 32];
 #pragma unroll
@@ -207,8 +206,8 @@ bwd_main_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, cons
     // row per lane; rows past the end are clamped (and masked later)
     auto issue_stats = [&](int r0, float* ldst, float* ddst) __attribute__((always_inline)) {
         const int row = min(r0 + lane, N - 1);
-        if (w == 0) g2lds4(LSEh + row, ldst);
-        if (w == 1) g2lds4(Dh + row, ddst);
+        if (w == 0 && lane < BR) g2lds4(LSEh + row, ldst);
+        if (w == 1 && lane < BR) g2lds4(Dh + row, ddst);
     };
 
     // buffer layout: Q tile | dO tile | LSE[BR] | D[BR]
@@ -218,8 +217,7 @@ bwd_main_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, cons
         issue_stats(r0, reinterpret_cast<float*>(b + 2 * QTB), reinterpret_cast<float*>(b + 2 * QTB + 4 * BR));
     };
 
-    // prologue: K tile (once) and the first query tile
-    issue(Kh, k0, kbuf, w * KSPW, KSPW);
+    // prologue: the first query tile
     if (qt_begin < nqt) fill(qt_begin * BR, buf0);
     FA_WAIT_VMCNT(0);
 
@@ -229,22 +227,15 @@ bwd_main_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, cons
         const float* ls = reinterpret_cast<const float*>(cur + 2 * QTB);
         const float* ds_ = reinterpret_cast<const float*>(cur + 2 * QTB + 4 * BR);
         const int q0 = qt * BR;
-        // copies of this tile have landed (the atomics of the previous tile,
-        // issued after them, may still be in flight); every wave is done with
-        // the previous tile, so its buffers may be refilled
-        FA_WAIT_VMCNT(ATOMICS);
+        // copies of this tile have landed, and every wave is done with the
+        // previous tile, so its buffers may be refilled
+        FA_WAIT_VMCNT(0);
         __builtin_amdgcn_s_barrier();
         if (qt + 1 < nqt) fill(q0 + BR, nxt);
 
+        // a wave whose keys see none of the tile's queries has nothing to add
         const bool wave_dead = (CAUSAL && wk0 > q0 + BR - 1) || wk0 >= N;
-        if (wave_dead) {
-            // this wave's keys see none of the tile's queries: dS = 0
-#pragma unroll
-            for (int qb = 0; qb < NQB; ++qb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    dss[(32 * qb + 8 * (r >> 2) + 4 * g + (r & 3)) * DSS + 32 * w + l32] = (__bf16)0.f;
-        } else {
+        if (!wave_dead) {
             // LSE and D of this lane's 16 query rows per block (runs of 4)
             float4 lse4[NQB][4], dd4[NQB][4];
 #pragma unroll
@@ -301,49 +292,17 @@ bwd_main_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, cons
                 }
                 const bf16x8 pb = as_bf16x8(make_uint4(pk[0], pk[1], pk[2], pk[3]));
                 const bf16x8 sb = as_bf16x8(make_uint4(sk[0], sk[1], sk[2], sk[3]));
-                const int row_lo = 16 * ks + 4 * g + rt;       // queries of K-slots j = 0..3
+                // queries of K-slots j = 0..3 and 4..7: 16*ks + 4*g + {0..3, 8..11}
+                const int rk = 16 * ks * ROWB;
 #pragma unroll
                 for (int mb = 0; mb < D / 32; ++mb) {
-                    const int col = 32 * mb + ct;
-                    const uint2 dlo = lds_read_tr16x4(os + tr_off(row_lo, col));
-                    const uint2 dhi = lds_read_tr16x4(os + tr_off(row_lo + 8, col));
+                    const uint2 dlo = lds_read_tr16x4(os + rk + qt_off[0][mb]);
+                    const uint2 dhi = lds_read_tr16x4(os + rk + qt_off[1][mb]);
                     dvt[mb] = mfma_bf16(as_bf16x8(make_uint4(dlo.x, dlo.y, dhi.x, dhi.y)), pb, dvt[mb]);
-                    const uint2 qlo = lds_read_tr16x4(qs + tr_off(row_lo, col));
-                    const uint2 qhi = lds_read_tr16x4(qs + tr_off(row_lo + 8, col));
+                    const uint2 qlo = lds_read_tr16x4(qs + rk + qt_off[0][mb]);
+                    const uint2 qhi = lds_read_tr16x4(qs + rk + qt_off[1][mb]);
                     dkt[mb] = mfma_bf16(as_bf16x8(make_uint4(qlo.x, qlo.y, qhi.x, qhi.y)), sb, dkt[mb]);
                 }
-            }
-            // dS -> LDS as [query][key] bf16 for dQ
-#pragma unroll
-            for (int qb = 0; qb < NQB; ++qb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    dss[(32 * qb + 8 * (r >> 2) + 4 * g + (r & 3)) * DSS + 32 * w + l32] = (__bf16)dP[qb][r];
-        }
-        FA_WAIT_LGKM0();
-        __builtin_amdgcn_s_barrier();
-
-        // dQ_tile += dS K : DQ_UNITS 32x32 output blocks shared by the waves.
-        // K-slots are keys in natural order; the K^T operand is read
-        // transposed from the row-major K tile.
-#pragma unroll
-        for (int u0 = 0; u0 < DQ_PER_WAVE; ++u0) {
-            const int u = u0 * 4 + w;
-            const int qb = u / (D / 32), nb = u % (D / 32);
-            f32x16 acc = zero16();
-#pragma unroll
-            for (int ks = 0; ks < BC / 16; ++ks) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8*>(dss + (32 * qb + l32) * DSS + 16 * ks + 8 * g);
-                const int row = 16 * ks + 8 * g + rt;
-                const int col = 32 * nb + ct;
-                const uint2 lo = lds_read_tr16x4(kbuf + tr_off(row, col));
-                const uint2 hi = lds_read_tr16x4(kbuf + tr_off(row + 4, col));
-                acc = mfma_bf16(a, as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)), acc);
-            }
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = q0 + 32 * qb + 8 * (r >> 2) + 4 * g + (r & 3);
-                if (row < N) unsafeAtomicAdd(dQh + (size_t)row * D + 32 * nb + l32, acc[r]);
             }
         }
     };
@@ -373,49 +332,204 @@ bwd_main_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, cons
 }
 
 // ---------------------------------------------------------------------------
-// 3. dQ = scale * accumulator -> bf16 (8 elements per thread)
+// 3. dQ kernel: query-tile outer, K/V tiles streamed through LDS.
 // ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(256)
-bwd_dq_kernel(const float* __restrict__ acc, __bf16* __restrict__ dq, long long n8, float scale) {
-    const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
-    if (i >= n8) return;
-    const float4 a = *reinterpret_cast<const float4*>(acc + 8 * i);
-    const float4 b = *reinterpret_cast<const float4*>(acc + 8 * i + 4);
-    *reinterpret_cast<uint4*>(dq + 8 * i) =
-        make_uint4(pack_bf16x2(scale * a.x, scale * a.y), pack_bf16x2(scale * a.z, scale * a.w),
-                   pack_bf16x2(scale * b.x, scale * b.y), pack_bf16x2(scale * b.z, scale * b.w));
+constexpr int DQ_BR = 128;       // query rows per workgroup (4 waves x 32)
+constexpr int DQ_BC = 64;        // keys per K/V tile
+
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
+              const __bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ delta,
+              __bf16* __restrict__ dQ, int BH, int N, int nqt, float c /* scale*log2e */, float scale) {
+    constexpr int BR = DQ_BR, BC = DQ_BC;
+    constexpr int ROWB = 2 * D;
+    constexpr int CPR = D / 8;
+    constexpr int TILEB = BC * ROWB;
+    constexpr int RPS = 1024 / ROWB;
+    constexpr int SPW = TILEB / 1024 / 4;
+    constexpr int NKB = BC / 32;
+    static_assert(SPW >= 1, "tile too small for four waves");
+
+    // two buffer pairs (K tile, V tile), separate LDS objects (see the forward)
+    __shared__ __attribute__((aligned(1024))) char kb0[TILEB];
+    __shared__ __attribute__((aligned(1024))) char kb1[TILEB];
+    __shared__ __attribute__((aligned(1024))) char vb0[TILEB];
+    __shared__ __attribute__((aligned(1024))) char vb1[TILEB];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, w = tid >> 6;
+    const int l32 = lane & 31, g = lane >> 5;
+
+    // heavy (late) query tiles first; consecutive blocks are different heads
+    const int bh = blockIdx.x % BH;
+    const int qt = CAUSAL ? (nqt - 1 - blockIdx.x / BH) : (blockIdx.x / BH);
+    const int q0 = qt * BR;
+    const size_t hoff = (size_t)bh * (size_t)N * D;
+    const __bf16* Qh = Q + hoff;
+    const __bf16* Kh = K + hoff;
+    const __bf16* Vh = V + hoff;
+    const __bf16* dOh = dO + hoff;
+
+    // Q^T and dO^T fragments: B operands of S^T = K Q^T and dP^T = V dO^T
+    const int wrow0 = q0 + 32 * w;
+    const int qrow = wrow0 + l32;
+    const bool row_live = qrow < N;
+    bf16x8 qf[D / 16], df[D / 16];
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+        uint4 uq = make_uint4(0, 0, 0, 0), ud = uq;
+        if (row_live) {
+            uq = *reinterpret_cast<const uint4*>(Qh + (size_t)qrow * D + 16 * ks + 8 * g);
+            ud = *reinterpret_cast<const uint4*>(dOh + (size_t)qrow * D + 16 * ks + 8 * g);
+        }
+        qf[ks] = as_bf16x8(uq);
+        df[ks] = as_bf16x8(ud);
+    }
+    // rows past the end get LSE = +inf (P = 0)
+    const float lse2 = row_live ? LSE[(size_t)bh * N + qrow] * kLog2e : INFINITY;
+    const float dd = row_live ? delta[(size_t)bh * N + qrow] : 0.f;
+
+    const int kv_end = CAUSAL ? min(N, q0 + BR) : N;
+    const int nkt = (kv_end + BC - 1) / BC;
+    const int nkt_w = (wrow0 >= N) ? 0 : (CAUSAL ? min(nkt, (wrow0 + 31) / BC + 1) : nkt);
+
+    // K is read both ways (rows for S^T, transposed for K^T): rt_swz.
+    // V is only read by rows (dP^T = V dO^T): k_swz.
+    auto issue = [&](int kt, char* kdst, char* vdst) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < SPW; ++i) {
+            const int seg = w * SPW + i;
+            const int row = seg * RPS + lane / CPR;
+            const int pc = lane % CPR;
+            const size_t grow = (size_t)min(kt * BC + row, N - 1) * D;
+            g2lds16(Kh + grow + 8 * (pc ^ rt_swz<D>(row)), kdst + seg * 1024);
+            g2lds16(Vh + grow + 8 * (pc ^ k_swz<D>(row)), vdst + seg * 1024);
+        }
+    };
+
+    int ko[D / 16], vo[D / 16];
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+        ko[ks] = l32 * ROWB + 16 * ((2 * ks + g) ^ rt_swz<D>(l32));
+        vo[ks] = l32 * ROWB + 16 * ((2 * ks + g) ^ k_swz<D>(l32));
+    }
+    // K^T: rows 16*ks + 4*g + 8*h + rt (keys in the C-layout order of dS^T),
+    // columns 32*mb + ct .. +3
+    const int rt = (lane & 15) >> 2;
+    const int ct = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    int kto[2][D / 32];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int mb = 0; mb < D / 32; ++mb) {
+            const int row = 4 * g + 8 * h + rt, col = 32 * mb + ct;
+            kto[h][mb] = row * ROWB + 16 * ((col >> 3) ^ rt_swz<D>(row)) + 2 * (col & 7);
+        }
+    const int last_visible = CAUSAL ? min(qrow, N - 1) : N - 1;
+
+    f32x16 dqt[D / 32];
+#pragma unroll
+    for (int mb = 0; mb < D / 32; ++mb) dqt[mb] = zero16();
+
+    auto step = [&](int kt, const char* Ks, const char* Vs, char* kn, char* vn) __attribute__((always_inline)) {
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (kt + 1 < nkt) issue(kt + 1, kn, vn);
+        if (kt >= nkt_w) return;
+        // S^T = K Q^T and dP^T = V dO^T (keys x queries)
+        f32x16 st[NKB], pt[NKB];
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+            st[kb] = zero16();
+            pt[kb] = zero16();
+        }
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks)
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                st[kb] = mfma_bf16(*reinterpret_cast<const bf16x8*>(Ks + 32 * kb * ROWB + ko[ks]), qf[ks], st[kb]);
+                pt[kb] = mfma_bf16(*reinterpret_cast<const bf16x8*>(Vs + 32 * kb * ROWB + vo[ks]), df[ks], pt[kb]);
+            }
+        // dS^T = P^T (dP^T - D), P^T = 2^(c S^T - LSE log2 e), masked
+        const bool need_mask = (kt * BC + BC > N) || (CAUSAL && kt * BC + BC - 1 > wrow0);
+        const int lim = last_visible - kt * BC - 4 * g;
+        bf16x8 sb[BC / 16];
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                uint32_t pk[4];
+#pragma unroll
+                for (int j = 0; j < 8; j += 2) {
+                    float v2[2];
+#pragma unroll
+                    for (int t = 0; t < 2; ++t) {
+                        const int r = 8 * h + j + t;
+                        float p = exp2_fast(fmaf(st[kb][r], c, -lse2));
+                        if (need_mask && 32 * kb + 8 * (r >> 2) + (r & 3) > lim) p = 0.f;
+                        v2[t] = p * (pt[kb][r] - dd);
+                    }
+                    pk[j / 2] = pack_bf16x2(v2[0], v2[1]);
+                }
+                sb[2 * kb + h] = as_bf16x8(make_uint4(pk[0], pk[1], pk[2], pk[3]));
+            }
+        // dQ^T += K^T dS^T
+#pragma unroll
+        for (int ks = 0; ks < BC / 16; ++ks)
+#pragma unroll
+            for (int mb = 0; mb < D / 32; ++mb) {
+                const uint2 lo = lds_read_tr16x4(Ks + 16 * ks * ROWB + kto[0][mb]);
+                const uint2 hi = lds_read_tr16x4(Ks + 16 * ks * ROWB + kto[1][mb]);
+                dqt[mb] = mfma_bf16(as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)), sb[ks], dqt[mb]);
+            }
+    };
+
+    if (nkt > 0) issue(0, kb0, vb0);
+    for (int kt = 0; kt < nkt; kt += 2) {
+        step(kt, kb0, vb0, kb1, vb1);
+        if (kt + 1 < nkt) step(kt + 1, kb1, vb1, kb0, vb0);
+    }
+
+    // dQ = scale * (dQ^T)^T: lane holds row qrow, dims in runs of 4
+    if (row_live) {
+        __bf16* drow = dQ + hoff + (size_t)qrow * D;
+#pragma unroll
+        for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb) {
+                const int d0 = 32 * mb + 8 * rb + 4 * g;
+                *reinterpret_cast<uint2*>(drow + d0) =
+                    make_uint2(pack_bf16x2(scale * dqt[mb][4 * rb], scale * dqt[mb][4 * rb + 1]),
+                               pack_bf16x2(scale * dqt[mb][4 * rb + 2], scale * dqt[mb][4 * rb + 3]));
+            }
+    }
 }
 
 template <int D, bool CAUSAL>
-hipError_t launch_main(const BwdArgs& a) {
-    const int BH = a.B * a.H;
-    const int nkt = (a.N + BWD_BC - 1) / BWD_BC;
-    hipLaunchKernelGGL((bwd_main_kernel<D, CAUSAL>), dim3((unsigned)(nkt * BH)), dim3(BWD_THREADS), 0,
-                       (hipStream_t)a.stream, (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v,
-                       (const __bf16*)a.dout, a.lse, a.delta, a.dq_acc, (__bf16*)a.dk, (__bf16*)a.dv, BH, a.N,
-                       a.scale * kLog2e, a.scale);
-    return hipGetLastError();
-}
-
-template <int D>
-hipError_t launch_d(const BwdArgs& a) {
+hipError_t launch_kernels(const BwdArgs& a) {
     hipStream_t st = (hipStream_t)a.stream;
-    const long long rows = (long long)a.B * a.H * a.N;
-    const long long prep_threads = rows * (D / 8);
-    const unsigned prep_blocks = (unsigned)((prep_threads + 255) / 256);
+    const int BH = a.B * a.H;
+    const long long rows = (long long)BH * a.N;
+    const unsigned prep_blocks = (unsigned)((rows * (D / 8) + 255) / 256);
     if (a.o_bf16)
         hipLaunchKernelGGL((bwd_prep_kernel<D, true>), dim3(prep_blocks), dim3(256), 0, st, a.o,
-                           (const __bf16*)a.dout, a.delta, a.dq_acc, rows);
+                           (const __bf16*)a.dout, a.delta, rows);
     else
         hipLaunchKernelGGL((bwd_prep_kernel<D, false>), dim3(prep_blocks), dim3(256), 0, st, a.o,
-                           (const __bf16*)a.dout, a.delta, a.dq_acc, rows);
+                           (const __bf16*)a.dout, a.delta, rows);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    e = a.causal ? launch_main<D, true>(a) : launch_main<D, false>(a);
+    const int nkt = (a.N + BWD_BC - 1) / BWD_BC;
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)(nkt * BH)), dim3(BWD_THREADS), 0, st,
+                       (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (const __bf16*)a.dout, a.lse,
+                       a.delta, (__bf16*)a.dk, (__bf16*)a.dv, BH, a.N, a.scale * kLog2e, a.scale);
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const long long n8 = rows * D / 8;
-    hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st, a.dq_acc,
-                       (__bf16*)a.dq, n8, a.scale);
+    const int nqt = (a.N + DQ_BR - 1) / DQ_BR;
+    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)(nqt * BH)), dim3(256), 0, st,
+                       (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (const __bf16*)a.dout, a.lse,
+                       a.delta, (__bf16*)a.dq, BH, a.N, nqt, a.scale * kLog2e, a.scale);
     return hipGetLastError();
 }
 
@@ -424,7 +538,8 @@ hipError_t launch_d(const BwdArgs& a) {
 hipError_t launch_bwd(const BwdArgs& a) {
     const long long rows = (long long)a.B * a.H * a.N;
     if (rows * (a.d / 8) / 256 + 1 > 0x7fffffffLL) return hipErrorInvalidValue;
-    return a.d == 64 ? launch_d<64>(a) : launch_d<128>(a);
+    if (a.d == 64) return a.causal ? launch_kernels<64, true>(a) : launch_kernels<64, false>(a);
+    return a.causal ? launch_kernels<128, true>(a) : launch_kernels<128, false>(a);
 }
 
 }  // namespace fa

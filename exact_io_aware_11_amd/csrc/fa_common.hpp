@@ -143,4 +143,21 @@ __device__ __forceinline__ float dpp_sum16(float v) {
     return v;
 }
 
+// XOR swizzles of the 16-byte chunks of an LDS tile row (2*D bytes, no
+// padding), applied when the tile is copied in and when it is read.
+//  k_swz: rows read one 16-byte chunk per lane by 32 consecutive rows.
+//  v_swz: rows read with the transposing 8-byte read (4 rows x 32 bytes per
+//         16-lane group).
+//  rt_swz: both patterns on the same tile (4*(row%4) + (row/4)%4).
+template <int D>
+__device__ __forceinline__ int k_swz(int row) { return row & (D / 8 - 1); }
+template <int D>
+__device__ __forceinline__ int v_swz(int row) {
+    return D == 128 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2);
+}
+template <int D>
+__device__ __forceinline__ int rt_swz(int row) {
+    return (4 * (row & 3) + ((row >> 2) & 3)) & (D / 8 - 1);
+}
+
 }  // namespace fa

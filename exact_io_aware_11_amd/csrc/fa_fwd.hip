@@ -54,18 +54,9 @@ __device__ __forceinline__ void fwd_tile_of(int bid, int BH, int nqt, bool causa
 
 // K and V tiles live in LDS row-major without padding (2*D bytes per row) and
 // are filled by direct global->LDS copies; bank conflicts are avoided by
-// permuting the 16-byte chunks of each row with an XOR of the row index.
-// K is read one 16-byte chunk per lane by 32 consecutive rows: XOR with
-// row % (chunks per row).  V is read with the transposing 8-byte read, whose
-// 16-lane groups touch 4 consecutive rows x 32 bytes: XOR of chunk bits 2..3
-// spreads those rows over all banks.
-template <int D>
-__device__ __forceinline__ int k_swz(int row) { return row & (D / 8 - 1); }
-template <int D>
-__device__ __forceinline__ int v_swz(int row) {
-    return D == 128 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2);
-}
-
+// permuting the 16-byte chunks of each row with an XOR of the row index
+// (k_swz for K, read one chunk per lane by 32 consecutive rows; v_swz for V,
+// read with the transposing 8-byte read).
 template <int D, bool CAUSAL, bool OUT_BF16>
 __global__ void __launch_bounds__(FWD_THREADS) __attribute__((amdgpu_waves_per_eu(2)))
 fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,

@@ -31,7 +31,6 @@ struct BwdArgs {
     void* dq;
     void* dk;
     void* dv;
-    float* dq_acc;   // workspace: [B,H,N,d] fp32
     float* delta;    // workspace: [B,H,N] fp32, rowsum(dO * O)
     int B, H, N, d;
     bool o_bf16;

@@ -79,9 +79,9 @@ fa_status_t fa_fwd(const void* q, const void* k, const void* v,
                    int causal, float scale, void* stream);
 
 /*
- * fa_bwd_workspace_bytes -- bytes of workspace fa_bwd needs: an fp32 dQ
- * accumulator [B,H,N,d] plus the fp32 row statistic D = rowsum(dO * O)
- * [B,H,N].  Returns 0 if a size is < 1 or the total overflows.
+ * fa_bwd_workspace_bytes -- bytes of workspace fa_bwd needs: the fp32 row
+ * statistic D = rowsum(dO * O), [B,H,N].  Returns 0 if a size is < 1 or the
+ * total overflows.
  */
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d);
 
@@ -96,7 +96,8 @@ size_t fa_bwd_workspace_bytes(int B, int H, int N, int d);
  *   q, k, v, dout  [B,H,N,d] bf16 (in_dtype must be FA_BF16).
  *   o              [B,H,N,d] of o_dtype (FA_BF16 or FA_FP32), from fa_fwd.
  *   lse            [B,H,N] float32, from fa_fwd with the same causal/scale.
- *   dq, dk, dv     [B,H,N,d] bf16 outputs (fp32 accumulation inside).
+ *   dq, dk, dv     [B,H,N,d] bf16 outputs (fp32 accumulation inside; no
+ *                  atomics, so the results are bitwise reproducible).
  *   workspace      device memory of at least fa_bwd_workspace_bytes(); its
  *                  contents on entry do not matter and are clobbered.
  */

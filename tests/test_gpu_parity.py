@@ -234,6 +234,19 @@ def test_bwd_causal_bf16_b2h16n4096d128_sampled_heads():
     assert dk.float().sum(dim=2).abs().max().item() <= 2e-2 * scale_k * math.sqrt(w.N)
 
 
+def test_bwd_deterministic():
+    # no atomics anywhere in the backward: two runs agree bit for bit
+    fa = _fa()
+    q, k, v, do = W.make_custom(2, 3, 700, 128, "bf16", seed=2100, n_tensors=4, device=DEV)
+    say("fa_bwd determinism")
+    o, lse = fa.attention(q, k, v, is_causal=True)
+    a = fa.attention_backward(q, k, v, o, lse, do, is_causal=True)
+    b = fa.attention_backward(q, k, v, o, lse, do, is_causal=True)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
 # ----------------------------------------------------------------------------
 # decode
 # ----------------------------------------------------------------------------
