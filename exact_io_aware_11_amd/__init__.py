@@ -44,6 +44,15 @@ class FaError(RuntimeError):
 
 
 def _load() -> ctypes.CDLL:
+    # libfa.so needs libamdhip64.so.7.  PyTorch ships its own copy under the
+    # same soname; if libfa.so were loaded first, the dynamic loader would map
+    # the system copy as well and the process would hold two HIP runtimes,
+    # whose streams and allocations the other cannot use.  Importing torch
+    # first makes the loader resolve libfa.so's dependency to torch's runtime.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     if not os.path.exists(LIB_PATH):
         raise ImportError(
             f"{LIB_PATH} is missing: build it first (python -m exact_io_aware_11_amd.build). "

@@ -3,6 +3,11 @@ import sys
 
 import pytest
 
+# The HIP runtime must be the one PyTorch loads (see exact_io_aware_11_amd's
+# loader); importing torch before any test module loads the library keeps a
+# single runtime in the test process.
+import torch  # noqa: F401
+
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)

@@ -41,6 +41,19 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(lib, name), name
 
 
+def test_single_hip_runtime_in_process():
+    # importing the binding must not map a second libamdhip64 next to torch's
+    import subprocess
+    import sys
+    code = ("import exact_io_aware_11_amd, torch; "
+            "print(sorted({l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l}))")
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT,
+                         timeout=300)
+    assert out.returncode == 0, out.stderr
+    libs = eval(out.stdout.strip().splitlines()[-1])
+    assert len(libs) == 1, libs
+
+
 def test_status_strings():
     for s in range(7):
         assert fa.fa_status_string(s).startswith("FA_")
