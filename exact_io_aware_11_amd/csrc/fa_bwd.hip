@@ -32,6 +32,8 @@
 // query and 16 keys, the B operand of dQ^T = K^T dS^T.  The transposed A
 // operands (Q^T, dO^T, K^T) are read with the transposing LDS read in the
 // matching order.
+#include <type_traits>
+
 #include "fa_common.hpp"
 #include "fa_internal.hpp"
 
@@ -39,13 +41,7 @@ namespace fa {
 
 namespace {
 
-#ifndef FA_BWD_BR
-#define FA_BWD_BR 64
-#endif
-#ifndef FA_BWD_WAVES
-#define FA_BWD_WAVES 1
-#endif
-constexpr int BWD_BR = FA_BWD_BR;       // query rows per inner step
+constexpr int BWD_BR = 64;       // query rows per inner step
 constexpr int BWD_BC = 128;      // keys per workgroup (4 waves x 32)
 constexpr int BWD_THREADS = 256;
 
@@ -99,13 +95,25 @@ bwd_prep_kernel(const void* __restrict__ O, const __bf16* __restrict__ dO, float
 // chunks by 32 consecutive rows (A operands of S = Q K^T and dP = dO V^T) and
 // with the transposing 8-byte read (Q^T and dO^T operands); rt_swz keeps both
 // patterns free of bank conflicts.
+// Ask the scheduler to interleave the current region as n groups of
+// (rd LDS reads, 1 MFMA, va VALU ops), so that vector work issues while the
+// matrix core is busy with the same wave's products.
+#define FA_INTERLEAVE(n, rd, va)                                   \
+    do {                                                           \
+        _Pragma("unroll") for (int _i = 0; _i < (n); ++_i) {       \
+            __builtin_amdgcn_sched_group_barrier(0x100, (rd), 0);  \
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     \
+            __builtin_amdgcn_sched_group_barrier(0x002, (va), 0);  \
+        }                                                          \
+    } while (0)
+
 // s_waitcnt with only vmcnt constrained (expcnt / lgkmcnt left at their max).
 #define FA_WAIT_VMCNT(n) \
     __builtin_amdgcn_s_waitcnt((((n) & 15) | (((n) >> 4) << 14)) | (7 << 4) | (15 << 8))
 #define FA_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4))
 
 template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(BWD_THREADS) __attribute__((amdgpu_waves_per_eu(FA_BWD_WAVES)))
+__global__ void __launch_bounds__(BWD_THREADS)
 bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
                 const __bf16* __restrict__ dO, const float* __restrict__ LSE,
                 const float* __restrict__ delta, __bf16* __restrict__ dK,
@@ -125,7 +133,7 @@ bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, cons
     constexpr int BUFB = 2 * QTB + 2 * BR * 4;
     __shared__ __attribute__((aligned(1024))) char buf0[BUFB];
     __shared__ __attribute__((aligned(1024))) char buf1[BUFB];
-    static_assert(BR <= 64, "one wave copies a row statistic of the tile");
+    static_assert(BR == 64, "two 32-row halves per query tile; one wave copies a row statistic");
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
@@ -246,63 +254,93 @@ bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, cons
                     dd4[qb][rb] = *reinterpret_cast<const float4*>(ds_ + 32 * qb + 8 * rb + 4 * g);
                 }
 
+            // The two 32-row halves of the tile are independent until they
+            // meet in dV^T and dK^T, which lets one half's exponentials run in
+            // the shadow of the other half's matrix products:
+            //   S,dP(0) | S,dP(1) + P,dS(0) | dV,dK(0) + P,dS(1) | dV,dK(1)
             f32x16 sP[NQB], dP[NQB];
-#pragma unroll
-            for (int qb = 0; qb < NQB; ++qb) {
+            bf16x8 pb[BR / 16], sb[BR / 16];
+            auto sdp = [&](int qb) __attribute__((always_inline)) {
                 sP[qb] = zero16();
                 dP[qb] = zero16();
-            }
 #pragma unroll
-            for (int ks = 0; ks < D / 16; ++ks)
-#pragma unroll
-                for (int qb = 0; qb < NQB; ++qb) {
+                for (int ks = 0; ks < D / 16; ++ks) {
                     const bf16x8 aq = *reinterpret_cast<const bf16x8*>(qs + 32 * qb * ROWB + rd_off[ks]);
                     sP[qb] = mfma_bf16(aq, kf[ks], sP[qb]);
                     const bf16x8 ad = *reinterpret_cast<const bf16x8*>(os + 32 * qb * ROWB + rd_off[ks]);
                     dP[qb] = mfma_bf16(ad, vf[ks], dP[qb]);
                 }
-            // P = 2^(c S - LSE log2 e), masked; dS = P (dP - D)
-            const bool need_mask = (k0 + BC > N) || (q0 + BR > N) || (CAUSAL && wk0 + 31 > q0);
+            };
+            // P = 2^(c S - LSE log2 e), masked; dS = P (dP - D); both packed to
+            // bf16 as the B operands of the two K-steps of this half
+            auto pds = [&](int qb, auto masked) __attribute__((always_inline)) {
 #pragma unroll
-            for (int qb = 0; qb < NQB; ++qb)
+                for (int h = 0; h < 2; ++h) {
+                    uint32_t pk[4], sk[4];
 #pragma unroll
-                for (int rb = 0; rb < 4; ++rb) {
-                    const float lv[4] = {lse4[qb][rb].x, lse4[qb][rb].y, lse4[qb][rb].z, lse4[qb][rb].w};
-                    const float dv[4] = {dd4[qb][rb].x, dd4[qb][rb].y, dd4[qb][rb].z, dd4[qb][rb].w};
+                    for (int j = 0; j < 8; j += 2) {
+                        float pv[2], sv[2];
 #pragma unroll
-                    for (int t = 0; t < 4; ++t) {
-                        const int r = 4 * rb + t;
-                        const int qrow = q0 + 32 * qb + 8 * rb + 4 * g + t;
-                        float p = exp2_fast(fmaf(sP[qb][r], c, -lv[t] * kLog2e));
-                        if (need_mask && (!key_live || qrow >= N || (CAUSAL && key > qrow))) p = 0.f;
-                        sP[qb][r] = p;
-                        dP[qb][r] = p * (dP[qb][r] - dv[t]);
+                        for (int u = 0; u < 2; ++u) {
+                            const int r = 8 * h + j + u, rb = r >> 2, t = r & 3;
+                            const float4 l4 = lse4[qb][rb], d4 = dd4[qb][rb];
+                            const float lv = t == 0 ? l4.x : t == 1 ? l4.y : t == 2 ? l4.z : l4.w;
+                            const float dv = t == 0 ? d4.x : t == 1 ? d4.y : t == 2 ? d4.z : d4.w;
+                            float p = exp2_fast(fmaf(sP[qb][r], c, -lv * kLog2e));
+                            if (decltype(masked)::value) {
+                                const int qrow = q0 + 32 * qb + 8 * rb + 4 * g + t;
+                                if (!key_live || qrow >= N || (CAUSAL && key > qrow)) p = 0.f;
+                            }
+                            pv[u] = p;
+                            sv[u] = p * (dP[qb][r] - dv);
+                        }
+                        pk[j / 2] = pack_bf16x2(pv[0], pv[1]);
+                        sk[j / 2] = pack_bf16x2(sv[0], sv[1]);
                     }
+                    pb[2 * qb + h] = as_bf16x8(make_uint4(pk[0], pk[1], pk[2], pk[3]));
+                    sb[2 * qb + h] = as_bf16x8(make_uint4(sk[0], sk[1], sk[2], sk[3]));
                 }
-            // dV^T += dO^T P ; dK^T += Q^T dS  (K-slots = queries, permuted as
-            // in the C layout; the transposed reads follow the same order)
-#pragma unroll
-            for (int ks = 0; ks < BR / 16; ++ks) {
-                const int qb = ks >> 1, h = ks & 1;
-                uint32_t pk[4], sk[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    pk[j] = pack_bf16x2(sP[qb][8 * h + 2 * j], sP[qb][8 * h + 2 * j + 1]);
-                    sk[j] = pack_bf16x2(dP[qb][8 * h + 2 * j], dP[qb][8 * h + 2 * j + 1]);
-                }
-                const bf16x8 pb = as_bf16x8(make_uint4(pk[0], pk[1], pk[2], pk[3]));
-                const bf16x8 sb = as_bf16x8(make_uint4(sk[0], sk[1], sk[2], sk[3]));
-                // queries of K-slots j = 0..3 and 4..7: 16*ks + 4*g + {0..3, 8..11}
+            };
+            // dV^T += dO^T P ; dK^T += Q^T dS for K-step ks (queries
+            // 16*ks + 4*g + {0..3, 8..11}, the C-layout order of P and dS)
+            auto dvdk = [&](int ks) __attribute__((always_inline)) {
                 const int rk = 16 * ks * ROWB;
 #pragma unroll
                 for (int mb = 0; mb < D / 32; ++mb) {
                     const uint2 dlo = lds_read_tr16x4(os + rk + qt_off[0][mb]);
                     const uint2 dhi = lds_read_tr16x4(os + rk + qt_off[1][mb]);
-                    dvt[mb] = mfma_bf16(as_bf16x8(make_uint4(dlo.x, dlo.y, dhi.x, dhi.y)), pb, dvt[mb]);
+                    dvt[mb] = mfma_bf16(as_bf16x8(make_uint4(dlo.x, dlo.y, dhi.x, dhi.y)), pb[ks], dvt[mb]);
                     const uint2 qlo = lds_read_tr16x4(qs + rk + qt_off[0][mb]);
                     const uint2 qhi = lds_read_tr16x4(qs + rk + qt_off[1][mb]);
-                    dkt[mb] = mfma_bf16(as_bf16x8(make_uint4(qlo.x, qlo.y, qhi.x, qhi.y)), sb, dkt[mb]);
+                    dkt[mb] = mfma_bf16(as_bf16x8(make_uint4(qlo.x, qlo.y, qhi.x, qhi.y)), sb[ks], dkt[mb]);
                 }
+            };
+            auto pipeline = [&](auto masked) __attribute__((always_inline)) {
+                sdp(0);
+                __builtin_amdgcn_sched_barrier(0);
+                sdp(1);
+                pds(0, masked);
+                FA_INTERLEAVE(2 * D / 16, 2, 4);
+                __builtin_amdgcn_sched_barrier(0);
+                dvdk(0);
+                dvdk(1);
+                pds(1, masked);
+                FA_INTERLEAVE(4 * D / 32, 4, 4);
+                __builtin_amdgcn_sched_barrier(0);
+                dvdk(2);
+                dvdk(3);
+            };
+            // Causal: the unmasked copy serves every tile off the diagonal.
+            // Without a causal mask only the ragged end needs masking, and a
+            // single (masked) copy keeps the register allocation within bounds.
+            if constexpr (CAUSAL) {
+                const bool need_mask = (k0 + BC > N) || (q0 + BR > N) || (wk0 + 31 > q0);
+                if (need_mask)
+                    pipeline(std::true_type{});
+                else
+                    pipeline(std::false_type{});
+            } else {
+                pipeline(std::true_type{});
             }
         }
     };
