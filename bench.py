@@ -47,6 +47,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--reduce-counters", nargs="+", metavar="DIR",
+                    help="host only: summarise rocprofv3 --pmc output of this script and exit")
+    ap.add_argument("--write-traffic", action="store_true",
+                    help="with --reduce-counters: write profiles/traffic.json")
     return ap.parse_args()
 
 
@@ -152,17 +156,20 @@ def sweep(torch, fa, W, dev, iters=10):
     return out
 
 
-def cpu_baseline(W, heads=32):
-    """The fp64 oracle, as it stands, on a bounded sample of the 2K training workload."""
+def cpu_baseline(W, min_seconds=10.0, max_passes=8):
+    """The fp64 oracle, as it stands, on the 2K training workload.
+
+    One pass is ref_fwd + ref_bwd over all B*H = 64 heads of B4 H16 N2048 d128
+    (causal); passes repeat until ``min_seconds`` have elapsed, and the rate is
+    the mean over them.
+    """
     import numpy as np
     import torch
 
     from oracle import ref_bwd, ref_fwd
     t = W.WORKLOADS["fwd_causal_bf16_b4h16n2048d128"]
     q, k, v, do = W.draw([(t.B, t.H, t.N, t.d)] * 4, t.seed, torch.bfloat16, device="cpu")
-    # the first `heads` of the B*H heads, as a [1, heads, N, d] batch
-    q, k, v, do = (x.reshape(1, t.B * t.H, t.N, t.d)[:, :heads].float().numpy().astype(np.float64)
-                   for x in (q, k, v, do))
+    q, k, v, do = (x.float().numpy().astype(np.float64) for x in (q, k, v, do))
     threads = None
     try:
         from threadpoolctl import threadpool_info
@@ -170,21 +177,146 @@ def cpu_baseline(W, heads=32):
         threads = max((i.get("num_threads", 1) for i in info), default=None)
     except Exception:
         pass
+    passes = 0
     t0 = time.perf_counter()
-    ref_fwd(q, k, v, True, t.scale)
-    ref_bwd(q, k, v, do, True, t.scale)
+    while passes < max_passes:
+        ref_fwd(q, k, v, True, t.scale)
+        ref_bwd(q, k, v, do, True, t.scale)
+        passes += 1
+        if time.perf_counter() - t0 >= min_seconds:
+            break
     secs = time.perf_counter() - t0
-    flops = 3.5 * fwd_flops(1, heads, t.N, t.d)
+    flops = passes * 3.5 * fwd_flops(t.B, t.H, t.N, t.d)
     return {
         "value": round(flops / secs / 1e12, 5),
         "unit": "TFLOP/s",
         "cores": threads or os.cpu_count(),
         "kind": "oracle",
-        "sample": f"oracle ref_fwd + ref_bwd (fp64, full N x N scores) on {heads} of the 64 heads of "
-                  f"B4 H16 N2048 d128 causal; {secs:.2f} s; rate uses the same causal flop count as the GPU",
+        "sample": f"oracle ref_fwd + ref_bwd (fp64, full N x N scores) on the whole B4 H16 N2048 d128 "
+                  f"causal workload, {passes} pass(es) in {secs:.2f} s; rate uses the same causal flop "
+                  "count as the GPU",
         "seconds": round(secs, 3),
         "affinity_cores": len(os.sched_getaffinity(0)),
     }
+
+
+# Kernels of one step as they appear in rocprofv3 output: key -> (name
+# substring, source file, algorithmic HBM bytes per launch on the step's
+# workloads).  Algorithmic bytes count each tensor the kernel must touch once:
+# bf16 [B,H,N,d] tensors at 2 bytes an element, fp32 row statistics at 4.
+def _step_kernels():
+    B, H, N, d = 4, 16, 2048, 128          # training workload
+    Bd, Hd, L = 64, 32, 8192                # decode workload
+    t, r = B * H * N * d * 2, B * H * N * 4
+    return {
+        "fwd": ("fwd_bf16_kernel", "fa_fwd.hip", "B4 H16 N2048 d128 causal", 4 * t + r,
+                "read Q, K, V; write O, LSE"),
+        "bwd_prep": ("bwd_prep_kernel", "fa_bwd.hip", "B4 H16 N2048 d128 causal", 2 * t + r,
+                     "read O, dO; write D"),
+        "bwd_dkdv": ("bwd_dkdv_kernel", "fa_bwd.hip", "B4 H16 N2048 d128 causal", 6 * t + 2 * r,
+                     "read Q, K, V, dO, LSE, D; write dK, dV"),
+        "bwd_dq": ("bwd_dq_kernel", "fa_bwd.hip", "B4 H16 N2048 d128 causal", 5 * t + 2 * r,
+                   "read Q, K, V, dO, LSE, D; write dQ"),
+        "decode": ("decode_split_kernel", "fa_decode.hip", "B64 H32 L8192 d128",
+                   2 * Bd * Hd * L * d * 2, "read the K and V caches"),
+        "decode_merge": ("decode_merge_kernel", "fa_decode.hip", "B64 H32 L8192 d128", None,
+                         "read the split partials; write O, LSE"),
+    }
+
+
+COPY_KERNEL = "copyBuffer"            # the 256 MiB device copy main() runs at set-up
+COPY_BYTES = 256 * 1024 * 1024
+
+
+def reduce_counters(dirs, write_traffic):
+    """Turn rocprofv3 ``--pmc`` CSV output of this script into per-kernel means.
+
+    Every ``*counter_collection.csv`` under ``dirs`` is read; each counter is
+    averaged per dispatch of a kernel, leaving out the first (cold) dispatch.
+    With FETCH_SIZE and WRITE_SIZE present, both are scaled by what they read
+    for the 256 MiB copy, and ``write_traffic`` writes profiles/traffic.json
+    with each kernel's HBM bytes per launch.  Prints a markdown summary.
+    """
+    import csv
+    import glob
+    import hashlib
+    from collections import defaultdict
+
+    kern = _step_kernels()
+    names = {k: v[0] for k, v in kern.items()} | {"copy": COPY_KERNEL}
+    vals = defaultdict(lambda: defaultdict(list))   # key -> counter -> [(dispatch, value)]
+    for d in dirs:
+        for f in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
+            with open(f) as fh:
+                for row in csv.DictReader(fh):
+                    for key, pat in names.items():
+                        if pat in row["Kernel_Name"]:
+                            vals[key][row["Counter_Name"]].append(
+                                (int(row["Dispatch_Id"]), float(row["Counter_Value"])))
+    mean = {}
+    for key, cs in vals.items():
+        mean[key] = {}
+        for c, xs in cs.items():
+            xs = [v for _, v in sorted(xs)]
+            xs = xs[1:] if len(xs) > 1 else xs
+            mean[key][c] = sum(xs) / len(xs)
+
+    print("| kernel | counter | mean per dispatch |\n|---|---|---:|")
+    for key in list(kern) + ["copy"]:
+        for c in sorted(mean.get(key, {})):
+            print(f"| {names[key]} | {c} | {mean[key][c]:.6g} |")
+
+    derived = []
+    for key in kern:
+        m = mean.get(key, {})
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in m and "GRBM_GUI_ACTIVE" in m:
+            # GRBM_GUI_ACTIVE sums the 8 XCDs' clocks; MFMA busy cycles sum the 1024 SIMDs
+            cyc = m["GRBM_GUI_ACTIVE"] / 8
+            derived.append(f"| {names[key]} | MFMA busy | {100 * m['SQ_VALU_MFMA_BUSY_CYCLES'] / 1024 / cyc:.1f}% "
+                           f"of {cyc:.4g} cycles |")
+        if "SQ_WAIT_ANY" in m and "SQ_WAVE_CYCLES" in m:
+            derived.append(f"| {names[key]} | waves waiting | {100 * m['SQ_WAIT_ANY'] / m['SQ_WAVE_CYCLES']:.0f}% "
+                           "of wave cycles |")
+        if "SQ_LDS_BANK_CONFLICT" in m and "SQ_LDS_IDX_ACTIVE" in m and m["SQ_LDS_IDX_ACTIVE"] > 0:
+            derived.append(f"| {names[key]} | LDS bank conflicts | "
+                           f"{100 * m['SQ_LDS_BANK_CONFLICT'] / m['SQ_LDS_IDX_ACTIVE']:.2f}% of LDS cycles |")
+    if derived:
+        print("\n| kernel | derived | value |\n|---|---|---|")
+        print("\n".join(derived))
+
+    cm = mean.get("copy", {})
+    if not ("FETCH_SIZE" in cm and "WRITE_SIZE" in cm):
+        if write_traffic:
+            raise SystemExit("no FETCH_SIZE and WRITE_SIZE for the calibration copy in the given runs")
+        return
+    ff = COPY_BYTES / 1024 / cm["FETCH_SIZE"]
+    wf = COPY_BYTES / 1024 / cm["WRITE_SIZE"]
+    rec = {"_about": "HBM bytes per launch from rocprofv3 FETCH_SIZE and WRITE_SIZE (separate passes "
+                     "over bench.py), each scaled by what the counter reads for bench.py's 256 MiB device "
+                     "copy; valid while the kernel source matches source_sha256",
+           "copy_calibration": {"bytes": COPY_BYTES, "fetch_kib": cm["FETCH_SIZE"], "write_kib": cm["WRITE_SIZE"],
+                                "fetch_factor": ff, "write_factor": wf}}
+    print(f"\nCalibration: the {COPY_BYTES >> 20} MiB copy reads FETCH_SIZE {cm['FETCH_SIZE']:.0f} KiB and "
+          f"WRITE_SIZE {cm['WRITE_SIZE']:.0f} KiB: factors {ff:.3f} and {wf:.3f}.\n")
+    print("| entry | kernel | workload | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes (scaled) | "
+          "algorithmic bytes | ratio |\n|---|---|---|---:|---:|---:|---:|---:|")
+    for key, (pat, src, wl, alg, what) in kern.items():
+        m = mean.get(key, {})
+        if not ("FETCH_SIZE" in m and "WRITE_SIZE" in m):
+            continue
+        hbm = m["FETCH_SIZE"] * 1024 * ff + m["WRITE_SIZE"] * 1024 * wf
+        with open(os.path.join(ROOT, "exact_io_aware_11_amd", "csrc", src), "rb") as fh:
+            sha = hashlib.sha256(fh.read()).hexdigest()
+        rec[key] = {"kernel": pat, "workload": wl, "source": src, "source_sha256": sha,
+                    "fetch_kib": m["FETCH_SIZE"], "write_kib": m["WRITE_SIZE"],
+                    "bytes_per_launch": hbm, "algorithmic_bytes": alg, "algorithmic": what}
+        ratio = f"{hbm / alg:.3f}" if alg else "—"
+        print(f"| {key} | `{pat}` | {wl} | {m['FETCH_SIZE']:.0f} | {m['WRITE_SIZE']:.0f} | {hbm:.4g} | "
+              f"{alg if alg else '—'} | {ratio} |")
+    if write_traffic:
+        with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as fh:
+            json.dump(rec, fh, indent=1)
+            fh.write("\n")
 
 
 def traffic_record(kernel_key):
@@ -213,6 +345,9 @@ def traffic_record(kernel_key):
 
 def main():
     args = parse()
+    if args.reduce_counters:
+        reduce_counters(args.reduce_counters, args.write_traffic)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
               "(every (batch, head) is independent; see the sharding notes in DESIGN.md)",
