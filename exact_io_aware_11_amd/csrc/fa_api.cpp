@@ -27,6 +27,9 @@ bool total_ok(int B, int H, int N, int d) {
     return rows <= 0x7fffffffLL && rows * d <= (1LL << 50);
 }
 
+// The bf16 kernels address one head's [N,d] tensor with 32-bit byte offsets.
+bool head_fits_u32(int N, int d) { return (long long)N * d * 2 < (1LL << 32); }
+
 fa_status_t from_hip(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
 
 constexpr int kMaxSplits = 256;
@@ -74,6 +77,7 @@ fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, fa_dtyp
     if (in_dtype != FA_BF16 && in_dtype != FA_FP32) return FA_ERR_UNSUPPORTED;
     if (o_dtype != FA_BF16 && o_dtype != FA_FP32) return FA_ERR_UNSUPPORTED;
     if (in_dtype == FA_FP32 && o_dtype != FA_FP32) return FA_ERR_UNSUPPORTED;
+    if (in_dtype == FA_BF16 && !head_fits_u32(N, d)) return FA_ERR_UNSUPPORTED;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return FA_ERR_ALIGN;
     fa::FwdArgs a{q, k, v, o, lse, B, H, N, d, in_dtype == FA_BF16, o_dtype == FA_BF16, causal != 0, scale, stream};
     return from_hip(fa::launch_fwd(a));
@@ -92,6 +96,7 @@ fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, f
     if (!dims_ok(B, H, N) || !scale_ok(scale) || !total_ok(B, H, N, d)) return FA_ERR_ARG;
     if (!head_dim_ok(d) || in_dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
     if (o_dtype != FA_BF16 && o_dtype != FA_FP32) return FA_ERR_UNSUPPORTED;
+    if (!head_fits_u32(N, d)) return FA_ERR_UNSUPPORTED;
     const void* ptrs[] = {q, k, v, o, lse, dout, dq, dk, dv};
     for (const void* p : ptrs)
         if (!aligned16(p)) return FA_ERR_ALIGN;

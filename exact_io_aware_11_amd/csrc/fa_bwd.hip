@@ -151,16 +151,22 @@ bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, cons
     const float* LSEh = LSE + (size_t)bh * N;
     const float* Dh = delta + (size_t)bh * N;
 
+    // one head's Q, dO (N * ROWB bytes < 2^32, checked by the host), LSE, D
+    const __amdgpu_buffer_rsrc_t q_rs = make_rsrc(Qh, (uint32_t)N * ROWB);
+    const __amdgpu_buffer_rsrc_t do_rs = make_rsrc(dOh, (uint32_t)N * ROWB);
+    const __amdgpu_buffer_rsrc_t lse_rs = make_rsrc(LSEh, (uint32_t)N * 4);
+    const __amdgpu_buffer_rsrc_t d_rs = make_rsrc(Dh, (uint32_t)N * 4);
+
     // copy rows [r0, r0 + rows) of a [N, D] tensor into an LDS tile
     // (segments seg0 .. seg0+nseg-1); rows past the end are clamped to N-1
-    auto issue = [&](const __bf16* src, int r0, char* dst, int seg0, int nseg) __attribute__((always_inline)) {
+    auto issue = [&](__amdgpu_buffer_rsrc_t src, int r0, char* dst, int seg0, int nseg) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < nseg; ++i) {
             const int seg = seg0 + i;
             const int row = seg * RPS + lane / CPR;
             const int pc = lane % CPR;
-            const size_t grow = (size_t)min(r0 + row, N - 1) * D;
-            g2lds16(src + grow + 8 * (pc ^ rt_swz<D>(row)), dst + seg * 1024);
+            const uint32_t grow = (uint32_t)min(r0 + row, N - 1) * ROWB;
+            b2lds16(src, grow + 16 * (pc ^ rt_swz<D>(row)), dst + seg * 1024);
         }
     };
 
@@ -213,15 +219,15 @@ bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, cons
     // LSE (wave 0) and D (wave 1) of the query tile starting at row r0, one
     // row per lane; rows past the end are clamped (and masked later)
     auto issue_stats = [&](int r0, float* ldst, float* ddst) __attribute__((always_inline)) {
-        const int row = min(r0 + lane, N - 1);
-        if (w == 0 && lane < BR) g2lds4(LSEh + row, ldst);
-        if (w == 1 && lane < BR) g2lds4(Dh + row, ddst);
+        const uint32_t row = (uint32_t)min(r0 + lane, N - 1);
+        if (w == 0 && lane < BR) b2lds4(lse_rs, 4 * row, ldst);
+        if (w == 1 && lane < BR) b2lds4(d_rs, 4 * row, ddst);
     };
 
     // buffer layout: Q tile | dO tile | LSE[BR] | D[BR]
     auto fill = [&](int r0, char* b) __attribute__((always_inline)) {
-        issue(Qh, r0, b, w * QSPW, QSPW);
-        issue(dOh, r0, b + QTB, w * QSPW, QSPW);
+        issue(q_rs, r0, b, w * QSPW, QSPW);
+        issue(do_rs, r0, b + QTB, w * QSPW, QSPW);
         issue_stats(r0, reinterpret_cast<float*>(b + 2 * QTB), reinterpret_cast<float*>(b + 2 * QTB + 4 * BR));
     };
 
@@ -434,15 +440,17 @@ bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const 
 
     // K is read both ways (rows for S^T, transposed for K^T): rt_swz.
     // V is only read by rows (dP^T = V dO^T): k_swz.
+    const __amdgpu_buffer_rsrc_t k_rs = make_rsrc(Kh, (uint32_t)N * ROWB);
+    const __amdgpu_buffer_rsrc_t v_rs = make_rsrc(Vh, (uint32_t)N * ROWB);
     auto issue = [&](int kt, char* kdst, char* vdst) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < SPW; ++i) {
             const int seg = w * SPW + i;
             const int row = seg * RPS + lane / CPR;
             const int pc = lane % CPR;
-            const size_t grow = (size_t)min(kt * BC + row, N - 1) * D;
-            g2lds16(Kh + grow + 8 * (pc ^ rt_swz<D>(row)), kdst + seg * 1024);
-            g2lds16(Vh + grow + 8 * (pc ^ k_swz<D>(row)), vdst + seg * 1024);
+            const uint32_t grow = (uint32_t)min(kt * BC + row, N - 1) * ROWB;
+            b2lds16(k_rs, grow + 16 * (pc ^ rt_swz<D>(row)), kdst + seg * 1024);
+            b2lds16(v_rs, grow + 16 * (pc ^ k_swz<D>(row)), vdst + seg * 1024);
         }
     };
 

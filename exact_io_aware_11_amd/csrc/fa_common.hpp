@@ -71,6 +71,29 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 typedef __attribute__((address_space(3))) void lds_void;
 
+// Buffer resource over [base, base + bytes) for raw buffer loads (stride 0,
+// bounds-checked: bytes past the end read as zero).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+
+// 16-byte buffer -> LDS copy (buffer_load_dwordx4 ... lds): lane l's 16 bytes,
+// read at byte offset voff of the resource, land at lds_base + 16*l (checked
+// with an in-bounds probe); lds_base must be wave-uniform.  Preferred over the
+// global_ form: the compiler treats a global_load_lds as a FLAT access that may
+// touch LDS and then forces every later LDS-read wait down to lgkmcnt(0) until
+// the copy is known complete, which serialises read prefetching.  The buffer
+// form is tracked on vmcnt only, so LDS reads keep partial lgkmcnt waits.
+__device__ __forceinline__ void b2lds16(__amdgpu_buffer_rsrc_t r, uint32_t voff, void* lds_base) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_base, 16, voff, 0, 0, 0);
+}
+
+// 4-byte buffer -> LDS copy (buffer_load_dword ... lds): lane l's word lands
+// at lds_base + 4*l.
+__device__ __forceinline__ void b2lds4(__amdgpu_buffer_rsrc_t r, uint32_t voff, void* lds_base) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_base, 4, voff, 0, 0, 0);
+}
+
 // 16-byte global -> LDS copy that bypasses registers (global_load_lds_dwordx4).
 // Lane l's 16 bytes land at lds_base + 16*l; lds_base must be wave-uniform.
 __device__ __forceinline__ void g2lds16(const void* gsrc, void* lds_base) {
@@ -127,8 +150,14 @@ __device__ __forceinline__ int perm16(int k) {
 }
 
 // Full-wave butterfly over lanes l and l ^ 32 (ds_bpermute).
-__device__ __forceinline__ float xor32_max(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
-__device__ __forceinline__ float xor32_sum(float x) { return x + __shfl_xor(x, 32); }
+__device__ __forceinline__ float xor32_max(float x) {
+    auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+    auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
 
 // DPP sums inside a row of 16 lanes (quad_perm, half-mirror, mirror).
 __device__ __forceinline__ float dpp_sum8(float v) {

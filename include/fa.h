@@ -47,7 +47,8 @@ typedef enum {
     FA_OK = 0,
     FA_ERR_NULL = 1,        /* a required pointer is NULL                      */
     FA_ERR_ARG = 2,         /* a size is < 1, or scale is not finite           */
-    FA_ERR_UNSUPPORTED = 3, /* a dtype / head-dim combination not built        */
+    FA_ERR_UNSUPPORTED = 3, /* a dtype / head-dim combination not built, or a
+                               bf16 head too large (N*d*2 >= 2^32 bytes)       */
     FA_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned                */
     FA_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required      */
     FA_ERR_HIP = 6          /* the HIP runtime reported an error at launch     */
@@ -72,6 +73,10 @@ typedef enum {
  *   o         [B,H,N,d] of o_dtype.  in_dtype FA_BF16 allows o_dtype FA_BF16
  *             or FA_FP32; in_dtype FA_FP32 requires o_dtype FA_FP32.
  *   lse       [B,H,N] float32, natural log; never NULL (backward needs it).
+ *
+ * With in_dtype FA_BF16 one head's K (and V) must span fewer than 2^32 bytes
+ * (N*d*2 < 2^32, i.e. N < 2^24 at d = 128): the kernels address a head
+ * with 32-bit offsets.  Larger heads return FA_ERR_UNSUPPORTED.
  */
 fa_status_t fa_fwd(const void* q, const void* k, const void* v,
                    void* o, fa_dtype_t o_dtype, float* lse,
@@ -100,6 +105,8 @@ size_t fa_bwd_workspace_bytes(int B, int H, int N, int d);
  *                  atomics, so the results are bitwise reproducible).
  *   workspace      device memory of at least fa_bwd_workspace_bytes(); its
  *                  contents on entry do not matter and are clobbered.
+ *
+ * As for fa_fwd, N*d*2 must be below 2^32 bytes (else FA_ERR_UNSUPPORTED).
  */
 fa_status_t fa_bwd(const void* q, const void* k, const void* v,
                    const void* o, fa_dtype_t o_dtype, const float* lse,

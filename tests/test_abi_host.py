@@ -88,6 +88,7 @@ def fwd(**kw):
     (dict(in_dtype=7), fa.FA_ERR_UNSUPPORTED),
     (dict(o_dtype=5), fa.FA_ERR_UNSUPPORTED),
     (dict(in_dtype=fa.FA_FP32, o_dtype=fa.FA_BF16), fa.FA_ERR_UNSUPPORTED),
+    (dict(N=1 << 24, d=128), fa.FA_ERR_UNSUPPORTED),     # one bf16 head of 2^32 bytes
     (dict(q=MIS), fa.FA_ERR_ALIGN),
     (dict(o=MIS), fa.FA_ERR_ALIGN),
     (dict(lse=MIS), fa.FA_ERR_ALIGN),
@@ -117,6 +118,7 @@ def bwd(ws_bytes=None, **kw):
     (dict(in_dtype=fa.FA_FP32), fa.FA_ERR_UNSUPPORTED),
     (dict(d=32), fa.FA_ERR_UNSUPPORTED),
     (dict(o_dtype=3), fa.FA_ERR_UNSUPPORTED),
+    (dict(N=1 << 24, d=128), fa.FA_ERR_UNSUPPORTED),
     (dict(dk=MIS), fa.FA_ERR_ALIGN),
     (dict(ws=0), fa.FA_ERR_WORKSPACE),
     (dict(ws=MIS), fa.FA_ERR_ALIGN),
