@@ -381,6 +381,11 @@ bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, cons
 constexpr int DQ_BR = 128;       // query rows per workgroup (4 waves x 32)
 constexpr int DQ_BC = 64;        // keys per K/V tile
 
+// instruction schedule of the dQ tile loop (measured best on MI355X)
+constexpr int DQ_AHEAD = 2;         // K^T operands read ahead of the dQ MFMAs
+constexpr int DQ_VALU_FIRST = 40;   // dS work placed before the first dQ MFMA
+constexpr int DQ_VALU_EACH = 8;     // and between the following ones
+
 template <int D, bool CAUSAL>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
@@ -529,6 +534,20 @@ bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const 
                 const uint2 hi = lds_read_tr16x4(Ks + 16 * ks * ROWB + kto[1][mb]);
                 dqt[mb] = mfma_bf16(as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)), sb[ks], dqt[mb]);
             }
+        // K^T reads for the first DQ_AHEAD products go out before the dS
+        // arithmetic; the rest of dS is interleaved with the products.
+        {
+            constexpr int n = (BC / 16) * (D / 32);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 * DQ_AHEAD, 0);     // LDS reads
+            __builtin_amdgcn_sched_group_barrier(0x002, DQ_VALU_FIRST, 0);    // VALU
+#pragma unroll
+            for (int i = 0; i < n - DQ_AHEAD; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);            // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, DQ_VALU_EACH, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, DQ_AHEAD, 0);
+        }
     };
 
     if (nkt > 0) issue(0, kb0, vb0);
