@@ -8,6 +8,7 @@ package imports nothing from it.
 from .attention import (  # noqa: F401
     attention_probs,
     causal_visible,
+    kv_head,
     ref_bwd,
     ref_decode,
     ref_fwd,

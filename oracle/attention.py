@@ -34,6 +34,13 @@ so that a brute-force test can show tiled == naive.
 
 Fully masked rows (unreachable for square causal inputs, where the diagonal is
 always visible) are defined as O = 0 and LSE = -inf.
+
+Grouped-query and multi-query attention (GQA/MQA) are named by the Slovak page
+(section 5, "Limity a co dalej") and by the Greek page's FlashAttention-2
+section (MQA), without a definition.  Reading used here: K and V carry Hkv
+heads, Hkv divides the H query heads, and query head h attends with K/V head
+h // (H / Hkv) (MQA: Hkv = 1; Hkv = H is ordinary multi-head attention).  The
+gradient of a shared K/V head is then the sum over the query heads that use it.
 """
 
 from __future__ import annotations
@@ -41,6 +48,7 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = [
+    "kv_head",
     "causal_visible",
     "attention_probs",
     "ref_fwd",
@@ -50,6 +58,13 @@ __all__ = [
     "ref_decode",
     "ref_merge_partials",
 ]
+
+
+def kv_head(h: int, n_heads: int, n_kv_heads: int) -> int:
+    """K/V head used by query head h: h // (H / Hkv) (reading in the module docstring)."""
+    if n_kv_heads < 1 or n_heads % n_kv_heads:
+        raise ValueError(f"{n_kv_heads} K/V heads do not divide {n_heads} query heads")
+    return h // (n_heads // n_kv_heads)
 
 
 def _f64(x) -> np.ndarray:
@@ -114,21 +129,23 @@ def attention_probs(q, k, causal: bool, scale: float) -> np.ndarray:
 def ref_fwd(q, k, v, causal: bool, scale: float):
     """Forward definition: O = softmax(scale Q K^T [masked]) V and LSE per row.
 
-    Shapes: q [B,H,Nq,d], k and v [B,H,Nk,d] -> O [B,H,Nq,d], LSE [B,H,Nq],
-    both float64.  LSE_i = m_i + ln(sum_j exp(S_ij - m_i)) (natural log).
+    Shapes: q [B,H,Nq,d], k and v [B,Hkv,Nk,d] with Hkv dividing H (query head
+    h uses K/V head ``kv_head(h, H, Hkv)``) -> O [B,H,Nq,d], LSE [B,H,Nq], both
+    float64.  LSE_i = m_i + ln(sum_j exp(S_ij - m_i)) (natural log).
     Source: the displayed formula of the Greek page's problem section; causal
-    variant as in the module docstring.
+    variant and GQA reading as in the module docstring.
     """
     q64, k64, v64 = _f64(q), _f64(k), _f64(v)
     B, H, nq, _ = q64.shape
-    nk = k64.shape[2]
+    Hkv, nk = k64.shape[1], k64.shape[2]
     o = np.empty(q64.shape[:3] + (v64.shape[-1],), dtype=np.float64)
     lse = np.empty((B, H, nq), dtype=np.float64)
     vis = causal_visible(np.arange(nq), nk) if causal else None
     for b in range(B):
         for h in range(H):
-            p, lse[b, h] = _softmax_rows(_scores(q64[b, h], k64[b, h], scale, vis))
-            o[b, h] = p @ v64[b, h]
+            g = kv_head(h, H, Hkv)
+            p, lse[b, h] = _softmax_rows(_scores(q64[b, h], k64[b, g], scale, vis))
+            o[b, h] = p @ v64[b, g]
     return o, lse
 
 
@@ -144,14 +161,15 @@ def ref_fwd_rows(q, k, v, causal: bool, scale: float, rows):
     q64 = _f64(np.asarray(q)[:, :, rows, :])
     k64, v64 = _f64(k), _f64(v)
     B, H = q64.shape[:2]
-    nk = k64.shape[2]
+    Hkv, nk = k64.shape[1], k64.shape[2]
     vis = causal_visible(rows, nk) if causal else None
     o = np.empty((B, H, rows.size, v64.shape[-1]), dtype=np.float64)
     lse = np.empty((B, H, rows.size), dtype=np.float64)
     for b in range(B):
         for h in range(H):
-            p, lse[b, h] = _softmax_rows(_scores(q64[b, h], k64[b, h], scale, vis))
-            o[b, h] = p @ v64[b, h]
+            g = kv_head(h, H, Hkv)
+            p, lse[b, h] = _softmax_rows(_scores(q64[b, h], k64[b, g], scale, vis))
+            o[b, h] = p @ v64[b, g]
     return o, lse
 
 
@@ -224,27 +242,30 @@ def ref_bwd(q, k, v, do, causal: bool, scale: float, return_ds: bool = False):
         dS = P * (dP - D 1^T)
         dQ = scale dS K,  dK = scale dS^T Q
 
-    Shapes [B,H,N,d] in, float64 out.  With ``return_ds`` the per-head dS
+    Shapes: q, do [B,H,N,d]; k, v [B,Hkv,N,d] (GQA reading of the module
+    docstring: a K/V head's dK and dV sum the contributions of the query heads
+    that use it); float64 out.  With ``return_ds`` the per-query-head dS
     [B,H,Nq,Nk] is returned as a fourth value (used by invariant tests).
     """
     q64, k64, v64, do64 = _f64(q), _f64(k), _f64(v), _f64(do)
     B, H, nq, _ = q64.shape
-    nk = k64.shape[2]
+    Hkv, nk = k64.shape[1], k64.shape[2]
     dq = np.empty_like(q64)
-    dk = np.empty_like(k64)
-    dvv = np.empty_like(v64)
+    dk = np.zeros_like(k64)
+    dvv = np.zeros_like(v64)
     ds_all = np.empty((B, H, nq, nk)) if return_ds else None
     vis = causal_visible(np.arange(nq), nk) if causal else None
     for b in range(B):
         for h in range(H):
-            p, _ = _softmax_rows(_scores(q64[b, h], k64[b, h], scale, vis))
-            o = p @ v64[b, h]
-            dvv[b, h] = p.T @ do64[b, h]
-            dp = do64[b, h] @ v64[b, h].T
+            g = kv_head(h, H, Hkv)
+            p, _ = _softmax_rows(_scores(q64[b, h], k64[b, g], scale, vis))
+            o = p @ v64[b, g]
+            dvv[b, g] += p.T @ do64[b, h]
+            dp = do64[b, h] @ v64[b, g].T
             dd = np.sum(do64[b, h] * o, axis=1, keepdims=True)
             ds = p * (dp - dd)
-            dq[b, h] = scale * (ds @ k64[b, h])
-            dk[b, h] = scale * (ds.T @ q64[b, h])
+            dq[b, h] = scale * (ds @ k64[b, g])
+            dk[b, g] += scale * (ds.T @ q64[b, h])
             if return_ds:
                 ds_all[b, h] = ds
     if return_ds:
@@ -255,8 +276,9 @@ def ref_bwd(q, k, v, do, causal: bool, scale: float, return_ds: bool = False):
 def ref_decode(q, k_cache, v_cache, scale: float):
     """One decode step against a KV cache: the forward definition with one query.
 
-    q [B,H,1,d]; k_cache, v_cache [B,H,L,d] (all cached keys visible, no mask)
-    -> O [B,H,1,d] and LSE [B,H] in float64.  The KV cache is the one the
+    q [B,H,1,d]; k_cache, v_cache [B,Hkv,L,d] (all cached keys visible, no
+    mask; query head h reads cache head h // (H / Hkv)) -> O [B,H,1,d] and
+    LSE [B,H] in float64.  The KV cache is the one the
     attention-backend page describes for generation; the decode result is the
     same softmax(q K^T * scale) V over the L cached tokens.
     """

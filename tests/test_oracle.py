@@ -223,9 +223,68 @@ def pin_tiled_equals_naive(fwd, bwd):
                         np.testing.assert_allclose(l_t, l_ref, atol=1e-12, rtol=0)
 
 
+def _gqa_inputs(seed, B, H, Hkv, N, d):
+    r = rng(seed)
+    q = r.standard_normal((B, H, N, d))
+    k = r.standard_normal((B, Hkv, N, d))
+    v = r.standard_normal((B, Hkv, N, d))
+    do = r.standard_normal((B, H, N, d))
+    return q, k, v, do
+
+
+GQA_SHAPES = [(2, 4, 2), (1, 6, 3), (1, 4, 1)]      # (B, H, Hkv): groups of 2, 2 and MQA
+
+
+def pin_sdpa_gqa_fwd(fwd, bwd):
+    # grouped-query attention against torch's own enable_gqa path (fp64, CPU)
+    for i, (B, H, Hkv) in enumerate(GQA_SHAPES):
+        q, k, v, _ = _gqa_inputs(40 + i, B, H, Hkv, 11, 5)
+        for causal in (False, True):
+            o, lse = fwd(q, k, v, causal, 0.45)
+            tq, tk, tv = (torch.from_numpy(x) for x in (q, k, v))
+            ot = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=causal,
+                                                                  scale=0.45, enable_gqa=True)
+            np.testing.assert_allclose(o, ot.numpy(), atol=1e-10, rtol=0)
+
+
+def pin_sdpa_gqa_bwd(fwd, bwd):
+    for i, (B, H, Hkv) in enumerate(GQA_SHAPES):
+        q, k, v, do = _gqa_inputs(50 + i, B, H, Hkv, 9, 4)
+        for causal in (False, True):
+            dq, dk, dv = bwd(q, k, v, do, causal, 0.55)[:3]
+            tq, tk, tv = (torch.from_numpy(x).requires_grad_(True) for x in (q, k, v))
+            ot = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=causal,
+                                                                  scale=0.55, enable_gqa=True)
+            ot.backward(torch.from_numpy(do))
+            np.testing.assert_allclose(dq, tq.grad.numpy(), atol=1e-10, rtol=0)
+            np.testing.assert_allclose(dk, tk.grad.numpy(), atol=1e-10, rtol=0)
+            np.testing.assert_allclose(dv, tv.grad.numpy(), atol=1e-10, rtol=0)
+
+
+def pin_gqa_group_sum(fwd, bwd):
+    # sharing a K/V head among G query heads is the same as giving each query
+    # head its own copy: outputs equal, and the shared head's gradients are the
+    # sums of the copies' gradients (linearity of the chain rule)
+    B, H, Hkv, N, d = 1, 6, 2, 8, 3
+    q, k, v, do = _gqa_inputs(60, B, H, Hkv, N, d)
+    G = H // Hkv
+    k_rep, v_rep = np.repeat(k, G, axis=1), np.repeat(v, G, axis=1)
+    for causal in (False, True):
+        o1, l1 = fwd(q, k, v, causal, 0.8)
+        o2, l2 = fwd(q, k_rep, v_rep, causal, 0.8)
+        np.testing.assert_allclose(o1, o2, atol=1e-12, rtol=0)
+        np.testing.assert_allclose(l1, l2, atol=1e-12, rtol=0)
+        dq1, dk1, dv1 = bwd(q, k, v, do, causal, 0.8)[:3]
+        dq2, dk2, dv2 = bwd(q, k_rep, v_rep, do, causal, 0.8)[:3]
+        np.testing.assert_allclose(dq1, dq2, atol=1e-12, rtol=0)
+        np.testing.assert_allclose(dk1, dk2.reshape(B, Hkv, G, N, d).sum(axis=2), atol=1e-12, rtol=0)
+        np.testing.assert_allclose(dv1, dv2.reshape(B, Hkv, G, N, d).sum(axis=2), atol=1e-12, rtol=0)
+
+
 PINS = [pin_golden, pin_equal_values, pin_uniform_scores, pin_first_causal_row,
         pin_permutation, pin_one_hot_selection, pin_shift_invariance, pin_sdpa_fwd,
-        pin_sdpa_bwd, pin_finite_differences, pin_bwd_invariants]
+        pin_sdpa_bwd, pin_finite_differences, pin_bwd_invariants,
+        pin_sdpa_gqa_fwd, pin_sdpa_gqa_bwd, pin_gqa_group_sum]
 
 
 @pytest.mark.parametrize("pin", PINS + [pin_tiled_equals_naive], ids=lambda p: p.__name__)
@@ -373,6 +432,31 @@ def _mut_bwd(kind):
     return bwd
 
 
+def _mut_gqa_fwd(kind):
+    # K/V head of query head h taken as h % Hkv instead of h // (H / Hkv)
+    def fwd(q, k, v, causal, scale):
+        H, Hkv = np.shape(q)[1], np.shape(k)[1]
+        idx = [h % Hkv for h in range(H)]
+        return ref_fwd(q, np.asarray(k)[:, idx], np.asarray(v)[:, idx], causal, scale)
+    return fwd
+
+
+def _mut_gqa_bwd(kind):
+    # a shared K/V head keeps the gradient of one query head instead of the sum
+    def bwd(q, k, v, do, causal, scale, return_ds=False):
+        H, Hkv = np.shape(q)[1], np.shape(k)[1]
+        G = H // Hkv
+        rep = [h // G for h in range(H)]
+        dq, dk, dv, ds = ref_bwd(q, np.asarray(k)[:, rep], np.asarray(v)[:, rep], do, causal,
+                                 scale, return_ds=True)
+        last = [g * G + G - 1 for g in range(Hkv)]
+        dk, dv = dk[:, last], dv[:, last]
+        if return_ds:
+            return dq, dk, dv, ds
+        return dq, dk, dv
+    return bwd
+
+
 FWD_MUTANTS = ["scale_sqrt", "strict_mask", "mask_transposed", "no_normalise",
                "v_reversed", "lse_no_max"]
 BWD_MUTANTS = ["drop_D", "dk_not_transposed", "dq_no_scale", "dv_wrong_side"]
@@ -395,3 +479,29 @@ def test_pins_catch_forward_mutant(kind):
 @pytest.mark.parametrize("kind", BWD_MUTANTS)
 def test_pins_catch_backward_mutant(kind):
     assert _caught(ref_fwd, _mut_bwd(kind)) is not None, kind
+
+
+def test_pins_catch_gqa_head_mapping_mutant():
+    assert _caught(_mut_gqa_fwd("kv_modulo"), ref_bwd) == "pin_sdpa_gqa_fwd"
+
+
+def test_pins_catch_gqa_gradient_sum_mutant():
+    assert _caught(ref_fwd, _mut_gqa_bwd("kv_grad_one_head")) == "pin_sdpa_gqa_bwd"
+
+
+def test_kv_head_mapping_and_divisibility():
+    assert [oracle.kv_head(h, 8, 2) for h in range(8)] == [0, 0, 0, 0, 1, 1, 1, 1]
+    assert [oracle.kv_head(h, 4, 1) for h in range(4)] == [0, 0, 0, 0]
+    with pytest.raises(ValueError):
+        oracle.kv_head(0, 6, 4)
+
+
+def test_gqa_decode_is_one_query_forward():
+    B, H, Hkv, L, d = 2, 8, 2, 37, 5
+    q, k, v, _ = _gqa_inputs(70, B, H, Hkv, L, d)
+    q1 = q[:, :, :1]
+    o, lse = ref_decode(q1, k, v, 0.3)
+    tq, tk, tv = (torch.from_numpy(x) for x in (q1, k, v))
+    ot = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, scale=0.3, enable_gqa=True)
+    np.testing.assert_allclose(o, ot.numpy(), atol=1e-10, rtol=0)
+    assert lse.shape == (B, H)
