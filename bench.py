@@ -79,15 +79,15 @@ class Buffers:
         self.dq_in, self.kc, self.vc = W.make_inputs(dcfg, dev)
         self.do_out = torch.empty_like(self.dq_in)
         self.dlse = torch.empty((dcfg.B, dcfg.H), dtype=torch.float32, device=dev)
-        self.splits = fa.fa_decode_num_splits(dcfg.B, dcfg.H, dcfg.N, dcfg.d)
-        self.dec_ws_bytes = fa.fa_decode_workspace_bytes(dcfg.B, dcfg.H, dcfg.N, dcfg.d, 0)
+        self.splits = fa.fa_decode_num_splits(dcfg.B, dcfg.H, dcfg.H, dcfg.N, dcfg.d)
+        self.dec_ws_bytes = fa.fa_decode_workspace_bytes(dcfg.B, dcfg.H, dcfg.H, dcfg.N, dcfg.d, 0)
         self.dec_ws = torch.empty((self.dec_ws_bytes,), dtype=torch.uint8, device=dev)
 
 
 def run_fwd(fa, b, stream):
     t = b.w_tr
     st = fa.fa_fwd(b.q.data_ptr(), b.k.data_ptr(), b.v.data_ptr(), b.o.data_ptr(), fa.FA_BF16,
-                   b.lse.data_ptr(), t.B, t.H, t.N, t.d, fa.FA_BF16, 1, t.scale, stream)
+                   b.lse.data_ptr(), t.B, t.H, t.H, t.N, t.d, fa.FA_BF16, 1, t.scale, stream)
     if st != fa.FA_OK:
         raise RuntimeError(fa.fa_status_string(st))
 
@@ -96,7 +96,8 @@ def run_bwd(fa, b, stream):
     t = b.w_tr
     st = fa.fa_bwd(b.q.data_ptr(), b.k.data_ptr(), b.v.data_ptr(), b.o.data_ptr(), fa.FA_BF16,
                    b.lse.data_ptr(), b.do.data_ptr(), b.dq.data_ptr(), b.dk.data_ptr(), b.dv.data_ptr(),
-                   b.bwd_ws.data_ptr(), b.bwd_ws_bytes, t.B, t.H, t.N, t.d, fa.FA_BF16, 1, t.scale, stream)
+                   b.bwd_ws.data_ptr(), b.bwd_ws_bytes, t.B, t.H, t.H, t.N, t.d, fa.FA_BF16, 1, t.scale,
+                   stream)
     if st != fa.FA_OK:
         raise RuntimeError(fa.fa_status_string(st))
 
@@ -104,7 +105,7 @@ def run_bwd(fa, b, stream):
 def run_decode(fa, b, stream):
     t = b.w_dec
     st = fa.fa_decode(b.dq_in.data_ptr(), b.kc.data_ptr(), b.vc.data_ptr(), b.do_out.data_ptr(),
-                      b.dlse.data_ptr(), b.dec_ws.data_ptr(), b.dec_ws_bytes, t.B, t.H, t.N, t.d,
+                      b.dlse.data_ptr(), b.dec_ws.data_ptr(), b.dec_ws_bytes, t.B, t.H, t.H, t.N, t.d,
                       fa.FA_BF16, 0, t.scale, stream)
     if st != fa.FA_OK:
         raise RuntimeError(fa.fa_status_string(st))
@@ -127,12 +128,12 @@ def sweep(torch, fa, W, dev, iters=10):
 
         def f():
             fa.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), fa.FA_BF16, lse.data_ptr(),
-                      B, H, N, d, fa.FA_BF16, 1, scale, stream)
+                      B, H, H, N, d, fa.FA_BF16, 1, scale, stream)
 
         def g():
             fa.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), fa.FA_BF16, lse.data_ptr(),
                       do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr(), nb,
-                      B, H, N, d, fa.FA_BF16, 1, scale, stream)
+                      B, H, H, N, d, fa.FA_BF16, 1, scale, stream)
 
         res = {"N": N, "B": B, "H": H, "d": d}
         for name, fn, mult in (("fwd", f, 1.0), ("bwd", g, 2.5)):

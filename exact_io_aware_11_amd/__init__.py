@@ -59,17 +59,17 @@ def _load() -> ctypes.CDLL:
             "There is no fallback implementation.")
     lib_ = ctypes.CDLL(LIB_PATH)
     P, I, F, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
-    lib_.fa_fwd.argtypes = [P, P, P, P, I, P, I, I, I, I, I, I, F, P]
+    lib_.fa_fwd.argtypes = [P, P, P, P, I, P, I, I, I, I, I, I, I, F, P]
     lib_.fa_fwd.restype = I
     lib_.fa_bwd_workspace_bytes.argtypes = [I, I, I, I]
     lib_.fa_bwd_workspace_bytes.restype = Z
-    lib_.fa_bwd.argtypes = [P, P, P, P, I, P, P, P, P, P, P, Z, I, I, I, I, I, I, F, P]
+    lib_.fa_bwd.argtypes = [P, P, P, P, I, P, P, P, P, P, P, Z, I, I, I, I, I, I, I, F, P]
     lib_.fa_bwd.restype = I
-    lib_.fa_decode_num_splits.argtypes = [I, I, I, I]
+    lib_.fa_decode_num_splits.argtypes = [I, I, I, I, I]
     lib_.fa_decode_num_splits.restype = I
-    lib_.fa_decode_workspace_bytes.argtypes = [I, I, I, I, I]
+    lib_.fa_decode_workspace_bytes.argtypes = [I, I, I, I, I, I]
     lib_.fa_decode_workspace_bytes.restype = Z
-    lib_.fa_decode.argtypes = [P, P, P, P, P, P, Z, I, I, I, I, I, I, F, P]
+    lib_.fa_decode.argtypes = [P, P, P, P, P, P, Z, I, I, I, I, I, I, I, F, P]
     lib_.fa_decode.restype = I
     lib_.fa_status_string.argtypes = [I]
     lib_.fa_status_string.restype = ctypes.c_char_p
@@ -87,8 +87,8 @@ def fa_status_string(status: int) -> str:
     return lib.fa_status_string(int(status)).decode()
 
 
-def fa_fwd(q, k, v, o, o_dtype, lse, B, H, N, d, in_dtype, causal, scale, stream=0) -> int:
-    return lib.fa_fwd(q, k, v, o, o_dtype, lse, B, H, N, d, in_dtype, int(causal), scale, stream)
+def fa_fwd(q, k, v, o, o_dtype, lse, B, H, Hkv, N, d, in_dtype, causal, scale, stream=0) -> int:
+    return lib.fa_fwd(q, k, v, o, o_dtype, lse, B, H, Hkv, N, d, in_dtype, int(causal), scale, stream)
 
 
 def fa_bwd_workspace_bytes(B, H, N, d) -> int:
@@ -96,22 +96,22 @@ def fa_bwd_workspace_bytes(B, H, N, d) -> int:
 
 
 def fa_bwd(q, k, v, o, o_dtype, lse, dout, dq, dk, dv, workspace, workspace_bytes,
-           B, H, N, d, in_dtype, causal, scale, stream=0) -> int:
+           B, H, Hkv, N, d, in_dtype, causal, scale, stream=0) -> int:
     return lib.fa_bwd(q, k, v, o, o_dtype, lse, dout, dq, dk, dv, workspace, workspace_bytes,
-                      B, H, N, d, in_dtype, int(causal), scale, stream)
+                      B, H, Hkv, N, d, in_dtype, int(causal), scale, stream)
 
 
-def fa_decode_num_splits(B, H, L, d) -> int:
-    return lib.fa_decode_num_splits(B, H, L, d)
+def fa_decode_num_splits(B, H, Hkv, L, d) -> int:
+    return lib.fa_decode_num_splits(B, H, Hkv, L, d)
 
 
-def fa_decode_workspace_bytes(B, H, L, d, num_splits=0) -> int:
-    return lib.fa_decode_workspace_bytes(B, H, L, d, num_splits)
+def fa_decode_workspace_bytes(B, H, Hkv, L, d, num_splits=0) -> int:
+    return lib.fa_decode_workspace_bytes(B, H, Hkv, L, d, num_splits)
 
 
-def fa_decode(q, k_cache, v_cache, o, lse, workspace, workspace_bytes, B, H, L, d, dtype,
+def fa_decode(q, k_cache, v_cache, o, lse, workspace, workspace_bytes, B, H, Hkv, L, d, dtype,
               num_splits, scale, stream=0) -> int:
-    return lib.fa_decode(q, k_cache, v_cache, o, lse, workspace, workspace_bytes, B, H, L, d,
+    return lib.fa_decode(q, k_cache, v_cache, o, lse, workspace, workspace_bytes, B, H, Hkv, L, d,
                          dtype, num_splits, scale, stream)
 
 
@@ -156,14 +156,17 @@ def _raise(status: int, where: str):
 def attention(q, k, v, is_causal: bool = False, scale: float | None = None, out_dtype=None):
     """O = softmax(scale Q K^T [causal]) V and the per-row LSE, via ``fa_fwd``.
 
-    q, k, v: contiguous [B,H,N,d] bf16 or fp32 GPU tensors.  Returns
+    q: contiguous [B,H,N,d] bf16 or fp32 GPU tensor; k, v: [B,Hkv,N,d] with
+    Hkv dividing H (grouped-query attention when Hkv < H).  Returns
     (o [B,H,N,d] of ``out_dtype`` (default: q's dtype), lse [B,H,N] fp32).
     """
     torch = _torch()
     _check(q, "q")
     B, H, N, d = q.shape
-    _check(k, "k", q.shape)
-    _check(v, "v", q.shape)
+    _check(k, "k")
+    Hkv = k.shape[1]
+    _check(k, "k", (B, Hkv, N, d))
+    _check(v, "v", (B, Hkv, N, d))
     if k.dtype != q.dtype or v.dtype != q.dtype:
         raise TypeError("q, k and v must share a dtype")
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
@@ -171,18 +174,26 @@ def attention(q, k, v, is_causal: bool = False, scale: float | None = None, out_
     o = torch.empty((B, H, N, d), dtype=out_dtype, device=q.device)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     st = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), _dtype_code(o), lse.data_ptr(),
-                B, H, N, d, _dtype_code(q), is_causal, scale, _stream(q))
+                B, H, Hkv, N, d, _dtype_code(q), is_causal, scale, _stream(q))
     _raise(st, "fa_fwd")
     return o, lse
 
 
 def attention_backward(q, k, v, o, lse, do, is_causal: bool = False, scale: float | None = None):
-    """dQ, dK, dV of ``attention`` by recomputation from (q, k, v, o, lse), via ``fa_bwd``."""
+    """dQ, dK, dV of ``attention`` by recomputation from (q, k, v, o, lse), via ``fa_bwd``.
+
+    dk and dv have k's shape [B,Hkv,N,d]; a shared K/V head gets the sum over
+    its query heads.
+    """
     torch = _torch()
     _check(q, "q")
     B, H, N, d = q.shape
-    for t, n in ((k, "k"), (v, "v"), (o, "o"), (do, "do")):
+    _check(k, "k")
+    Hkv = k.shape[1]
+    for t, n in ((o, "o"), (do, "do")):
         _check(t, n, q.shape)
+    for t, n in ((k, "k"), (v, "v")):
+        _check(t, n, (B, Hkv, N, d))
     _check(lse, "lse", (B, H, N))
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     dq = torch.empty_like(q)
@@ -192,13 +203,13 @@ def attention_backward(q, k, v, o, lse, do, is_causal: bool = False, scale: floa
     ws = torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=q.device)
     st = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), _dtype_code(o), lse.data_ptr(),
                 do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr(), nbytes,
-                B, H, N, d, _dtype_code(q), is_causal, scale, _stream(q))
+                B, H, Hkv, N, d, _dtype_code(q), is_causal, scale, _stream(q))
     _raise(st, "fa_bwd")
     return dq, dk, dv
 
 
 def decode(q, k_cache, v_cache, scale: float | None = None, num_splits: int = 0):
-    """One decode step: q [B,H,1,d] against caches [B,H,L,d] (bf16), via ``fa_decode``.
+    """One decode step: q [B,H,1,d] against caches [B,Hkv,L,d] (bf16), via ``fa_decode``.
 
     Returns (o [B,H,1,d] bf16, lse [B,H] fp32).
     """
@@ -208,15 +219,15 @@ def decode(q, k_cache, v_cache, scale: float | None = None, num_splits: int = 0)
     if one != 1:
         raise ValueError("decode takes one query token per (batch, head)")
     _check(k_cache, "k_cache")
-    L = k_cache.shape[2]
-    _check(k_cache, "k_cache", (B, H, L, d))
-    _check(v_cache, "v_cache", (B, H, L, d))
+    Hkv, L = k_cache.shape[1], k_cache.shape[2]
+    _check(k_cache, "k_cache", (B, Hkv, L, d))
+    _check(v_cache, "v_cache", (B, Hkv, L, d))
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     o = torch.empty((B, H, 1, d), dtype=q.dtype, device=q.device)
     lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
-    nbytes = fa_decode_workspace_bytes(B, H, L, d, num_splits)
+    nbytes = fa_decode_workspace_bytes(B, H, Hkv, L, d, num_splits)
     ws = torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=q.device)
     st = fa_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                   ws.data_ptr(), nbytes, B, H, L, d, _dtype_code(q), num_splits, scale, _stream(q))
+                   ws.data_ptr(), nbytes, B, H, Hkv, L, d, _dtype_code(q), num_splits, scale, _stream(q))
     _raise(st, "fa_decode")
     return o, lse

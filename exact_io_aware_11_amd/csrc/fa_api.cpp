@@ -27,6 +27,9 @@ bool total_ok(int B, int H, int N, int d) {
     return rows <= 0x7fffffffLL && rows * d <= (1LL << 50);
 }
 
+// Hkv K/V heads shared by H query heads in equal groups (Hkv = H: multi-head).
+bool kv_ok(int H, int Hkv) { return Hkv >= 1 && Hkv <= H && H % Hkv == 0; }
+
 // The bf16 kernels address one head's [N,d] tensor with 32-bit byte offsets.
 bool head_fits_u32(int N, int d) { return (long long)N * d * 2 < (1LL << 32); }
 
@@ -60,8 +63,10 @@ const char* fa_status_string(fa_status_t s) {
     switch (s) {
         case FA_OK: return "FA_OK";
         case FA_ERR_NULL: return "FA_ERR_NULL: a required pointer is NULL";
-        case FA_ERR_ARG: return "FA_ERR_ARG: a size is < 1, too large, or scale is not finite and positive";
-        case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: dtype / head-dim combination not built";
+        case FA_ERR_ARG:
+            return "FA_ERR_ARG: a size is < 1 or too large, Hkv does not divide H, or scale is not finite and positive";
+        case FA_ERR_UNSUPPORTED:
+            return "FA_ERR_UNSUPPORTED: dtype / head-dim combination not built, or a bf16 head of 2^32 bytes or more";
         case FA_ERR_ALIGN: return "FA_ERR_ALIGN: a pointer is not 16-byte aligned";
         case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace missing or too small";
         case FA_ERR_HIP: return "FA_ERR_HIP: the HIP runtime reported an error";
@@ -70,16 +75,18 @@ const char* fa_status_string(fa_status_t s) {
 }
 
 fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, fa_dtype_t o_dtype, float* lse,
-                   int B, int H, int N, int d, fa_dtype_t in_dtype, int causal, float scale, void* stream) {
+                   int B, int H, int Hkv, int N, int d, fa_dtype_t in_dtype, int causal, float scale,
+                   void* stream) {
     if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
-    if (!dims_ok(B, H, N) || !scale_ok(scale) || !total_ok(B, H, N, d)) return FA_ERR_ARG;
+    if (!dims_ok(B, H, N) || !kv_ok(H, Hkv) || !scale_ok(scale) || !total_ok(B, H, N, d)) return FA_ERR_ARG;
     if (!head_dim_ok(d)) return FA_ERR_UNSUPPORTED;
     if (in_dtype != FA_BF16 && in_dtype != FA_FP32) return FA_ERR_UNSUPPORTED;
     if (o_dtype != FA_BF16 && o_dtype != FA_FP32) return FA_ERR_UNSUPPORTED;
     if (in_dtype == FA_FP32 && o_dtype != FA_FP32) return FA_ERR_UNSUPPORTED;
     if (in_dtype == FA_BF16 && !head_fits_u32(N, d)) return FA_ERR_UNSUPPORTED;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return FA_ERR_ALIGN;
-    fa::FwdArgs a{q, k, v, o, lse, B, H, N, d, in_dtype == FA_BF16, o_dtype == FA_BF16, causal != 0, scale, stream};
+    fa::FwdArgs a{q, k, v, o, lse, B, H, Hkv, N, d, in_dtype == FA_BF16, o_dtype == FA_BF16, causal != 0, scale,
+                  stream};
     return from_hip(fa::launch_fwd(a));
 }
 
@@ -90,10 +97,10 @@ size_t fa_bwd_workspace_bytes(int B, int H, int N, int d) {
 
 fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, fa_dtype_t o_dtype,
                    const float* lse, const void* dout, void* dq, void* dk, void* dv, void* workspace,
-                   size_t workspace_bytes, int B, int H, int N, int d, fa_dtype_t in_dtype, int causal,
+                   size_t workspace_bytes, int B, int H, int Hkv, int N, int d, fa_dtype_t in_dtype, int causal,
                    float scale, void* stream) {
     if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_NULL;
-    if (!dims_ok(B, H, N) || !scale_ok(scale) || !total_ok(B, H, N, d)) return FA_ERR_ARG;
+    if (!dims_ok(B, H, N) || !kv_ok(H, Hkv) || !scale_ok(scale) || !total_ok(B, H, N, d)) return FA_ERR_ARG;
     if (!head_dim_ok(d) || in_dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
     if (o_dtype != FA_BF16 && o_dtype != FA_FP32) return FA_ERR_UNSUPPORTED;
     if (!head_fits_u32(N, d)) return FA_ERR_UNSUPPORTED;
@@ -104,21 +111,21 @@ fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, f
     if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
     if (!aligned16(workspace)) return FA_ERR_ALIGN;
     float* delta = static_cast<float*>(workspace);
-    fa::BwdArgs a{q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d, o_dtype == FA_BF16, causal != 0,
+    fa::BwdArgs a{q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, Hkv, N, d, o_dtype == FA_BF16, causal != 0,
                   scale, stream};
     return from_hip(fa::launch_bwd(a));
 }
 
-int fa_decode_num_splits(int B, int H, int L, int d) {
+int fa_decode_num_splits(int B, int H, int Hkv, int L, int d) {
     (void)d;
-    if (!dims_ok(B, H, L)) return 1;
+    if (!dims_ok(B, H, L) || !kv_ok(H, Hkv)) return 1;
     int splits, chunk;
     split_plan(L, auto_splits(B, H, L), splits, chunk);
     return splits;
 }
 
-size_t fa_decode_workspace_bytes(int B, int H, int L, int d, int num_splits) {
-    if (!dims_ok(B, H, L) || d < 1 || num_splits < 0 || !total_ok(B, H, L, d)) return 0;
+size_t fa_decode_workspace_bytes(int B, int H, int Hkv, int L, int d, int num_splits) {
+    if (!dims_ok(B, H, L) || !kv_ok(H, Hkv) || d < 1 || num_splits < 0 || !total_ok(B, H, L, d)) return 0;
     int splits, chunk;
     split_plan(L, num_splits == 0 ? auto_splits(B, H, L) : (num_splits > L ? L : num_splits), splits, chunk);
     const size_t parts = (size_t)B * H * splits;
@@ -127,15 +134,16 @@ size_t fa_decode_workspace_bytes(int B, int H, int L, int d, int num_splits) {
 }
 
 fa_status_t fa_decode(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
-                      void* workspace, size_t workspace_bytes, int B, int H, int L, int d, fa_dtype_t dtype,
-                      int num_splits, float scale, void* stream) {
+                      void* workspace, size_t workspace_bytes, int B, int H, int Hkv, int L, int d,
+                      fa_dtype_t dtype, int num_splits, float scale, void* stream) {
     if (!q || !k_cache || !v_cache || !o) return FA_ERR_NULL;
-    if (!dims_ok(B, H, L) || !scale_ok(scale) || num_splits < 0 || num_splits > L || !total_ok(B, H, L, d))
+    if (!dims_ok(B, H, L) || !kv_ok(H, Hkv) || !scale_ok(scale) || num_splits < 0 || num_splits > L ||
+        !total_ok(B, H, L, d))
         return FA_ERR_ARG;
     if (!head_dim_ok(d) || dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
     if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o)) return FA_ERR_ALIGN;
     if (lse && !aligned16(lse)) return FA_ERR_ALIGN;
-    const size_t need = fa_decode_workspace_bytes(B, H, L, d, num_splits);
+    const size_t need = fa_decode_workspace_bytes(B, H, Hkv, L, d, num_splits);
     if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
     if (!aligned16(workspace)) return FA_ERR_ALIGN;
     int splits, chunk;
@@ -144,7 +152,7 @@ fa_status_t fa_decode(const void* q, const void* k_cache, const void* v_cache, v
     float* o_part = static_cast<float*>(workspace);
     float* lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                                (((parts * (size_t)d * sizeof(float)) + 255) & ~(size_t)255));
-    fa::DecodeArgs a{q, k_cache, v_cache, o, lse, o_part, lse_part, B, H, L, d, splits, chunk, scale, stream};
+    fa::DecodeArgs a{q, k_cache, v_cache, o, lse, o_part, lse_part, B, H, Hkv, L, d, splits, chunk, scale, stream};
     return from_hip(fa::launch_decode(a));
 }
 

@@ -117,7 +117,7 @@ __global__ void __launch_bounds__(BWD_THREADS)
 bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
                 const __bf16* __restrict__ dO, const float* __restrict__ LSE,
                 const float* __restrict__ delta, __bf16* __restrict__ dK,
-                __bf16* __restrict__ dV, int BH, int N, float c /* scale*log2e */, float scale) {
+                __bf16* __restrict__ dV, int BHkv, int G, int N, float c /* scale*log2e */, float scale) {
     constexpr int BR = BWD_BR, BC = BWD_BC;
     constexpr int ROWB = 2 * D;                  // bytes per row of a Q/dO/K tile
     constexpr int CPR = D / 8;
@@ -139,23 +139,27 @@ bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, cons
     const int lane = tid & 63, w = tid >> 6;
     const int l32 = lane & 31, g = lane >> 5;
 
-    // heavy tiles first: key tile 0 sees every query tile
-    const int bh = blockIdx.x % BH;
-    const int kt = blockIdx.x / BH;
+    // One workgroup per (K/V head, key tile); heavy tiles first: key tile 0
+    // sees every query tile.  The G query heads sharing this K/V head are
+    // visited in turn, so dK and dV sum their contributions in registers.
+    const int kvh = blockIdx.x % BHkv;
+    const int kt = blockIdx.x / BHkv;
     const int k0 = kt * BC;
-    const size_t hoff = (size_t)bh * (size_t)N * D;
-    const __bf16* Qh = Q + hoff;
-    const __bf16* Kh = K + hoff;
-    const __bf16* Vh = V + hoff;
-    const __bf16* dOh = dO + hoff;
-    const float* LSEh = LSE + (size_t)bh * N;
-    const float* Dh = delta + (size_t)bh * N;
+    const size_t kvoff = (size_t)kvh * (size_t)N * D;
+    const __bf16* Kh = K + kvoff;
+    const __bf16* Vh = V + kvoff;
 
-    // one head's Q, dO (N * ROWB bytes < 2^32, checked by the host), LSE, D
-    const __amdgpu_buffer_rsrc_t q_rs = make_rsrc(Qh, (uint32_t)N * ROWB);
-    const __amdgpu_buffer_rsrc_t do_rs = make_rsrc(dOh, (uint32_t)N * ROWB);
-    const __amdgpu_buffer_rsrc_t lse_rs = make_rsrc(LSEh, (uint32_t)N * 4);
-    const __amdgpu_buffer_rsrc_t d_rs = make_rsrc(Dh, (uint32_t)N * 4);
+    // query head r of the group: its Q, dO (N * ROWB bytes < 2^32, checked by
+    // the host), LSE and D
+    auto head_rsrc = [&](int r, __amdgpu_buffer_rsrc_t& q_rs, __amdgpu_buffer_rsrc_t& do_rs,
+                         __amdgpu_buffer_rsrc_t& lse_rs, __amdgpu_buffer_rsrc_t& d_rs)
+        __attribute__((always_inline)) {
+        const size_t qh = (size_t)kvh * G + r;
+        q_rs = make_rsrc(Q + qh * N * D, (uint32_t)N * ROWB);
+        do_rs = make_rsrc(dO + qh * N * D, (uint32_t)N * ROWB);
+        lse_rs = make_rsrc(LSE + qh * N, (uint32_t)N * 4);
+        d_rs = make_rsrc(delta + qh * N, (uint32_t)N * 4);
+    };
 
     // copy rows [r0, r0 + rows) of a [N, D] tensor into an LDS tile
     // (segments seg0 .. seg0+nseg-1); rows past the end are clamped to N-1
@@ -216,36 +220,40 @@ bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, cons
     const int nqt = (N + BR - 1) / BR;
     const int qt_begin = CAUSAL ? (k0 / BR) : 0;
 
-    // LSE (wave 0) and D (wave 1) of the query tile starting at row r0, one
-    // row per lane; rows past the end are clamped (and masked later)
-    auto issue_stats = [&](int r0, float* ldst, float* ddst) __attribute__((always_inline)) {
-        const uint32_t row = (uint32_t)min(r0 + lane, N - 1);
-        if (w == 0 && lane < BR) b2lds4(lse_rs, 4 * row, ldst);
-        if (w == 1 && lane < BR) b2lds4(d_rs, 4 * row, ddst);
-    };
+    // Work items: (query head r of the group, query tile qt) for r = 0..G-1
+    // and qt = qt_begin..nqt-1, flattened to it = r * nq + (qt - qt_begin).
+    const int nq = nqt - qt_begin;
+    const int n_items = G * nq;
 
-    // buffer layout: Q tile | dO tile | LSE[BR] | D[BR]
-    auto fill = [&](int r0, char* b) __attribute__((always_inline)) {
+    // buffer layout: Q tile | dO tile | LSE[BR] | D[BR].  LSE (wave 0) and D
+    // (wave 1) are one row per lane; rows past the end are clamped (and
+    // masked later).
+    auto fill = [&](int it, char* b) __attribute__((always_inline)) {
+        __amdgpu_buffer_rsrc_t q_rs, do_rs, lse_rs, d_rs;
+        head_rsrc(it / nq, q_rs, do_rs, lse_rs, d_rs);
+        const int r0 = (qt_begin + it % nq) * BR;
         issue(q_rs, r0, b, w * QSPW, QSPW);
         issue(do_rs, r0, b + QTB, w * QSPW, QSPW);
-        issue_stats(r0, reinterpret_cast<float*>(b + 2 * QTB), reinterpret_cast<float*>(b + 2 * QTB + 4 * BR));
+        const uint32_t row = (uint32_t)min(r0 + lane, N - 1);
+        if (w == 0 && lane < BR) b2lds4(lse_rs, 4 * row, reinterpret_cast<float*>(b + 2 * QTB));
+        if (w == 1 && lane < BR) b2lds4(d_rs, 4 * row, reinterpret_cast<float*>(b + 2 * QTB + 4 * BR));
     };
 
-    // prologue: the first query tile
-    if (qt_begin < nqt) fill(qt_begin * BR, buf0);
+    // prologue: the first work item
+    if (n_items > 0) fill(0, buf0);
     FA_WAIT_VMCNT(0);
 
-    auto tile = [&](int qt, const char* cur, char* nxt) __attribute__((always_inline)) {
+    auto tile = [&](int it, const char* cur, char* nxt) __attribute__((always_inline)) {
         const char* qs = cur;
         const char* os = cur + QTB;
         const float* ls = reinterpret_cast<const float*>(cur + 2 * QTB);
         const float* ds_ = reinterpret_cast<const float*>(cur + 2 * QTB + 4 * BR);
-        const int q0 = qt * BR;
+        const int q0 = (qt_begin + it % nq) * BR;
         // copies of this tile have landed, and every wave is done with the
         // previous tile, so its buffers may be refilled
         FA_WAIT_VMCNT(0);
         __builtin_amdgcn_s_barrier();
-        if (qt + 1 < nqt) fill(q0 + BR, nxt);
+        if (it + 1 < n_items) fill(it + 1, nxt);
 
         // a wave whose keys see none of the tile's queries has nothing to add
         const bool wave_dead = (CAUSAL && wk0 > q0 + BR - 1) || wk0 >= N;
@@ -351,15 +359,15 @@ bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, cons
         }
     };
 
-    for (int qt = qt_begin; qt < nqt; qt += 2) {
-        tile(qt, buf0, buf1);
-        if (qt + 1 < nqt) tile(qt + 1, buf1, buf0);
+    for (int it = 0; it < n_items; it += 2) {
+        tile(it, buf0, buf1);
+        if (it + 1 < n_items) tile(it + 1, buf1, buf0);
     }
 
     // dV = (dV^T)^T, dK = scale (dK^T)^T: lane holds key `key`, dims in runs of 4
     if (key_live) {
-        __bf16* dvrow = dV + hoff + (size_t)key * D;
-        __bf16* dkrow = dK + hoff + (size_t)key * D;
+        __bf16* dvrow = dV + kvoff + (size_t)key * D;
+        __bf16* dkrow = dK + kvoff + (size_t)key * D;
 #pragma unroll
         for (int mb = 0; mb < D / 32; ++mb)
 #pragma unroll
@@ -390,7 +398,7 @@ template <int D, bool CAUSAL>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
               const __bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ delta,
-              __bf16* __restrict__ dQ, int BH, int N, int nqt, float c /* scale*log2e */, float scale) {
+              __bf16* __restrict__ dQ, int BH, int G, int N, int nqt, float c /* scale*log2e */, float scale) {
     constexpr int BR = DQ_BR, BC = DQ_BC;
     constexpr int ROWB = 2 * D;
     constexpr int CPR = D / 8;
@@ -410,14 +418,18 @@ bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const 
     const int lane = tid & 63, w = tid >> 6;
     const int l32 = lane & 31, g = lane >> 5;
 
-    // heavy (late) query tiles first; consecutive blocks are different heads
-    const int bh = blockIdx.x % BH;
+    // heavy (late) query tiles first; within one sweep over the heads the G
+    // query heads of a K/V head are BH / G blocks apart (same XCD when that is
+    // a multiple of 8, as in the forward's block order)
+    const int j = blockIdx.x % BH, NG = BH / G;
+    const int bh = (j % NG) * G + j / NG;
     const int qt = CAUSAL ? (nqt - 1 - blockIdx.x / BH) : (blockIdx.x / BH);
     const int q0 = qt * BR;
     const size_t hoff = (size_t)bh * (size_t)N * D;
+    const size_t kvoff = (size_t)(bh / G) * (size_t)N * D;
     const __bf16* Qh = Q + hoff;
-    const __bf16* Kh = K + hoff;
-    const __bf16* Vh = V + hoff;
+    const __bf16* Kh = K + kvoff;
+    const __bf16* Vh = V + kvoff;
     const __bf16* dOh = dO + hoff;
 
     // Q^T and dO^T fragments: B operands of S^T = K Q^T and dP^T = V dO^T
@@ -586,15 +598,16 @@ hipError_t launch_kernels(const BwdArgs& a) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int nkt = (a.N + BWD_BC - 1) / BWD_BC;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)(nkt * BH)), dim3(BWD_THREADS), 0, st,
+    const int G = a.H / a.Hkv, BHkv = a.B * a.Hkv;
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)(nkt * BHkv)), dim3(BWD_THREADS), 0, st,
                        (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (const __bf16*)a.dout, a.lse,
-                       a.delta, (__bf16*)a.dk, (__bf16*)a.dv, BH, a.N, a.scale * kLog2e, a.scale);
+                       a.delta, (__bf16*)a.dk, (__bf16*)a.dv, BHkv, G, a.N, a.scale * kLog2e, a.scale);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int nqt = (a.N + DQ_BR - 1) / DQ_BR;
     hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)(nqt * BH)), dim3(256), 0, st,
                        (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (const __bf16*)a.dout, a.lse,
-                       a.delta, (__bf16*)a.dq, BH, a.N, nqt, a.scale * kLog2e, a.scale);
+                       a.delta, (__bf16*)a.dq, BH, G, a.N, nqt, a.scale * kLog2e, a.scale);
     return hipGetLastError();
 }
 

@@ -44,7 +44,7 @@ template <int D>
 __global__ void __launch_bounds__(DEC_THREADS)
 decode_split_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ Kc,
                     const __bf16* __restrict__ Vc, float* __restrict__ Opart,
-                    float* __restrict__ LSEpart, int L, int S, int chunk, float c) {
+                    float* __restrict__ LSEpart, int G, int L, int S, int chunk, float c) {
     constexpr int LPK = D / 8;           // lanes per key (8 bf16 each)
     constexpr int KPL = 64 / LPK;        // keys covered by one wave-wide load
     constexpr int U = DEC_UNROLL;
@@ -73,7 +73,7 @@ decode_split_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ Kc,
         }
     }
 
-    const size_t hoff = (size_t)bh * (size_t)L * D;
+    const size_t hoff = (size_t)(bh / G) * (size_t)L * D;   // this query head's cache head
     const __bf16* Kh = Kc + hoff + 8 * dc;
     const __bf16* Vh = Vc + hoff + 8 * dc;
 
@@ -196,8 +196,8 @@ hipError_t launch_d(const DecodeArgs& a) {
     const int BH = a.B * a.H;
     hipStream_t st = (hipStream_t)a.stream;
     hipLaunchKernelGGL((decode_split_kernel<D>), dim3((unsigned)(BH * a.splits)), dim3(DEC_THREADS), 0, st,
-                       (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, a.o_part, a.lse_part, a.L,
-                       a.splits, a.chunk, a.scale * kLog2e);
+                       (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, a.o_part, a.lse_part,
+                       a.H / a.Hkv, a.L, a.splits, a.chunk, a.scale * kLog2e);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((decode_merge_kernel<D>), dim3((unsigned)((BH + DEC_WAVES - 1) / DEC_WAVES)),

@@ -45,14 +45,17 @@ constexpr int PV_VALU_FIRST = 24;  // exponent work placed before the first O MF
 constexpr int PV_VALU_EACH = 5;    // and between the following ones
 constexpr int FWD_THREADS = 256;
 
-// Map the flat block id to (head, query tile).  Consecutive ids are
-// consecutive heads, so every head's tiles land on the same XCD when the head
-// count is a multiple of 8 (the hardware deals blocks round-robin to the 8
-// XCDs), and with a causal mask the most expensive (last) query tiles of all
-// heads are issued first.
-__device__ __forceinline__ void fwd_tile_of(int bid, int BH, int nqt, bool causal,
+// Map the flat block id to (query head, query tile).  One sweep of BH
+// consecutive ids covers every head once, so with a causal mask the most
+// expensive (last) query tiles of all heads are issued first.  Within a sweep
+// the G query heads that share a K/V head are NG = BH / G ids apart: the
+// hardware deals blocks round-robin to the 8 XCDs, so when NG is a multiple
+// of 8 a whole group -- and every tile of it -- runs on one XCD and shares
+// that XCD's L2 copy of its K/V.  G = 1 gives bh = id % BH.
+__device__ __forceinline__ void fwd_tile_of(int bid, int BH, int G, int nqt, bool causal,
                                             int& bh, int& qt) {
-    bh = bid % BH;
+    const int j = bid % BH, NG = BH / G;
+    bh = (j % NG) * G + j / NG;
     const int t = bid / BH;
     qt = causal ? (nqt - 1 - t) : t;
 }
@@ -66,7 +69,7 @@ template <int D, bool CAUSAL, bool OUT_BF16>
 __global__ void __launch_bounds__(FWD_THREADS) __attribute__((amdgpu_waves_per_eu(2)))
 fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                 const __bf16* __restrict__ V, void* __restrict__ O, float* __restrict__ LSE,
-                int BH, int N, int nqt, float c /* scale * log2(e) */) {
+                int BH, int G, int N, int nqt, float c /* scale * log2(e) */) {
     constexpr int BR = FWD_BR, BC = FWD_BC;
     constexpr int ROWB = 2 * D;              // bytes per K/V row in LDS
     constexpr int CPR = D / 8;               // 16-byte chunks per row
@@ -91,12 +94,13 @@ fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     const int l32 = lane & 31, g = lane >> 5;
 
     int bh, qt;
-    fwd_tile_of(blockIdx.x, BH, nqt, CAUSAL, bh, qt);
+    fwd_tile_of(blockIdx.x, BH, G, nqt, CAUSAL, bh, qt);
     const int q0 = qt * BR;
     const size_t hoff = (size_t)bh * (size_t)N * D;
+    const size_t kvoff = (size_t)(bh / G) * (size_t)N * D;   // this head's K/V head
     const __bf16* Qh = Q + hoff;
-    const __bf16* Kh = K + hoff;
-    const __bf16* Vh = V + hoff;
+    const __bf16* Kh = K + kvoff;
+    const __bf16* Vh = V + kvoff;
 
     // Q^T fragment: B operand of S^T = K Q^T, column = query row of this lane.
     const int qrow = q0 + 32 * w + l32;
@@ -313,7 +317,7 @@ template <int D, bool CAUSAL>
 __global__ void __launch_bounds__(FWD_THREADS)
 fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
                const float* __restrict__ V, float* __restrict__ O, float* __restrict__ LSE,
-               int BH, int N, int nqt, float c) {
+               int BH, int G, int N, int nqt, float c) {
     constexpr int BR = FWD_BR, BC = FWD_BC32;
     constexpr int KS = D + 1;      // odd stride: column reads hit distinct banks
     constexpr int VS = D;
@@ -329,12 +333,13 @@ fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
     const int l32 = lane & 31, g = lane >> 5;
 
     int bh, qt;
-    fwd_tile_of(blockIdx.x, BH, nqt, CAUSAL, bh, qt);
+    fwd_tile_of(blockIdx.x, BH, G, nqt, CAUSAL, bh, qt);
     const int q0 = qt * BR;
     const size_t hoff = (size_t)bh * (size_t)N * D;
+    const size_t kvoff = (size_t)(bh / G) * (size_t)N * D;
     const float* Qh = Q + hoff;
-    const float* Kh = K + hoff;
-    const float* Vh = V + hoff;
+    const float* Kh = K + kvoff;
+    const float* Vh = V + kvoff;
 
     const int qrow = q0 + 32 * w + l32;
     float qf[D / 2];
@@ -433,8 +438,8 @@ hipError_t launch_bf16(const FwdArgs& a) {
     const int nqt = (a.N + FWD_BR - 1) / FWD_BR;
     const dim3 grid((unsigned)(nqt * BH)), block(FWD_THREADS);
     hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, OUT_BF16>), grid, block, 0, (hipStream_t)a.stream,
-                       (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, a.o, a.lse, BH, a.N, nqt,
-                       a.scale * kLog2e);
+                       (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, a.o, a.lse, BH,
+                       a.H / a.Hkv, a.N, nqt, a.scale * kLog2e);
     return hipGetLastError();
 }
 
@@ -444,8 +449,8 @@ hipError_t launch_f32(const FwdArgs& a) {
     const int nqt = (a.N + FWD_BR - 1) / FWD_BR;
     const dim3 grid((unsigned)(nqt * BH)), block(FWD_THREADS);
     hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL>), grid, block, 0, (hipStream_t)a.stream,
-                       (const float*)a.q, (const float*)a.k, (const float*)a.v, (float*)a.o, a.lse, BH, a.N,
-                       nqt, a.scale * kLog2e);
+                       (const float*)a.q, (const float*)a.k, (const float*)a.v, (float*)a.o, a.lse, BH,
+                       a.H / a.Hkv, a.N, nqt, a.scale * kLog2e);
     return hipGetLastError();
 }
 

@@ -13,7 +13,7 @@ struct FwdArgs {
     const void* v;
     void* o;
     float* lse;
-    int B, H, N, d;
+    int B, H, Hkv, N, d;   // H query heads; Hkv K/V heads, dividing H
     bool in_bf16;    // false: fp32 inputs
     bool out_bf16;   // O element type
     bool causal;
@@ -32,7 +32,7 @@ struct BwdArgs {
     void* dk;
     void* dv;
     float* delta;    // workspace: [B,H,N] fp32, rowsum(dO * O)
-    int B, H, N, d;
+    int B, H, Hkv, N, d;
     bool o_bf16;
     bool causal;
     float scale;
@@ -47,7 +47,7 @@ struct DecodeArgs {
     float* lse;      // may be null
     float* o_part;   // workspace: [B,H,S,d] fp32
     float* lse_part; // workspace: [B,H,S] fp32
-    int B, H, L, d;
+    int B, H, Hkv, L, d;
     int splits;      // S >= 1, every split non-empty
     int chunk;       // keys per split
     float scale;

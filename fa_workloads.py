@@ -123,6 +123,15 @@ def make_custom(B: int, H: int, N: int, d: int, dtype: str, seed: int,
     return [t.to(device) for t in draw(shapes, seed, tdt, sigma, device="cpu")]
 
 
+def make_gqa(B: int, H: int, Hkv: int, N: int, d: int, dtype: str, seed: int,
+             with_dout: bool = False, device="cpu", Nk: int | None = None):
+    """Seeded grouped-query inputs: Q [B,H,N,d], K and V [B,Hkv,Nk,d] (and dO [B,H,N,d])."""
+    tdt = torch.float32 if dtype == "fp32" else torch.bfloat16
+    nk = N if Nk is None else Nk
+    shapes = [(B, H, N, d), (B, Hkv, nk, d), (B, Hkv, nk, d)] + ([(B, H, N, d)] if with_dout else [])
+    return [t.to(device) for t in draw(shapes, seed, tdt, 1.0, device="cpu")]
+
+
 def sample_rows(n: int, count: int, seed: int):
     """``count`` distinct query rows drawn uniformly from [0, n) with a seeded generator."""
     g = _gen(seed, "cpu")

@@ -46,7 +46,8 @@ extern "C" {
 typedef enum {
     FA_OK = 0,
     FA_ERR_NULL = 1,        /* a required pointer is NULL                      */
-    FA_ERR_ARG = 2,         /* a size is < 1, or scale is not finite           */
+    FA_ERR_ARG = 2,         /* a size is < 1, Hkv does not divide H, or scale
+                               is not finite and positive                      */
     FA_ERR_UNSUPPORTED = 3, /* a dtype / head-dim combination not built, or a
                                bf16 head too large (N*d*2 >= 2^32 bytes)       */
     FA_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned                */
@@ -68,8 +69,13 @@ typedef enum {
  * on fusing operations describes).  Uses no workspace: memory beyond the
  * outputs is O(1) in N.
  *
- *   q, k, v   [B,H,N,d] of in_dtype (FA_BF16: bf16 MFMA with fp32
+ *   q         [B,H,N,d] of in_dtype (FA_BF16: bf16 MFMA with fp32
  *             accumulation; FA_FP32: fp32 MFMA).
+ *   k, v      [B,Hkv,N,d] of in_dtype.  Hkv divides H; query head h attends
+ *             with K/V head h / (H/Hkv) -- grouped-query attention, which the
+ *             Slovak page (section 5) and the Greek page (FlashAttention-2
+ *             section, multi-query) name; Hkv = 1 is multi-query and Hkv = H
+ *             ordinary multi-head attention.
  *   o         [B,H,N,d] of o_dtype.  in_dtype FA_BF16 allows o_dtype FA_BF16
  *             or FA_FP32; in_dtype FA_FP32 requires o_dtype FA_FP32.
  *   lse       [B,H,N] float32, natural log; never NULL (backward needs it).
@@ -80,7 +86,7 @@ typedef enum {
  */
 fa_status_t fa_fwd(const void* q, const void* k, const void* v,
                    void* o, fa_dtype_t o_dtype, float* lse,
-                   int B, int H, int N, int d, fa_dtype_t in_dtype,
+                   int B, int H, int Hkv, int N, int d, fa_dtype_t in_dtype,
                    int causal, float scale, void* stream);
 
 /*
@@ -98,11 +104,15 @@ size_t fa_bwd_workspace_bytes(int B, int H, int N, int d);
  *     dV = P^T dO,  dP = dO V^T,  D_i = sum_k dO_ik O_ik,
  *     dS = P * (dP - D),  dQ = scale dS K,  dK = scale dS^T Q.
  *
- *   q, k, v, dout  [B,H,N,d] bf16 (in_dtype must be FA_BF16).
+ *   q, dout        [B,H,N,d] bf16 (in_dtype must be FA_BF16).
+ *   k, v           [B,Hkv,N,d] bf16, grouped as for fa_fwd.
  *   o              [B,H,N,d] of o_dtype (FA_BF16 or FA_FP32), from fa_fwd.
  *   lse            [B,H,N] float32, from fa_fwd with the same causal/scale.
- *   dq, dk, dv     [B,H,N,d] bf16 outputs (fp32 accumulation inside; no
- *                  atomics, so the results are bitwise reproducible).
+ *   dq             [B,H,N,d] bf16 output.
+ *   dk, dv         [B,Hkv,N,d] bf16 outputs; a shared K/V head receives the
+ *                  sum over the H/Hkv query heads that use it.  fp32
+ *                  accumulation inside; no atomics, so the results are
+ *                  bitwise reproducible.
  *   workspace      device memory of at least fa_bwd_workspace_bytes(); its
  *                  contents on entry do not matter and are clobbered.
  *
@@ -112,21 +122,21 @@ fa_status_t fa_bwd(const void* q, const void* k, const void* v,
                    const void* o, fa_dtype_t o_dtype, const float* lse,
                    const void* dout, void* dq, void* dk, void* dv,
                    void* workspace, size_t workspace_bytes,
-                   int B, int H, int N, int d, fa_dtype_t in_dtype,
+                   int B, int H, int Hkv, int N, int d, fa_dtype_t in_dtype,
                    int causal, float scale, void* stream);
 
 /*
  * fa_decode_num_splits -- the split count fa_decode uses when called with
  * num_splits = 0 for this shape (always >= 1 and <= L).
  */
-int fa_decode_num_splits(int B, int H, int L, int d);
+int fa_decode_num_splits(int B, int H, int Hkv, int L, int d);
 
 /*
  * fa_decode_workspace_bytes -- workspace of fa_decode: fp32 partial outputs
  * [B,H,S,d] and partial LSEs [B,H,S] for S splits (num_splits = 0 means the
  * library's choice).  Returns 0 if a size is < 1.
  */
-size_t fa_decode_workspace_bytes(int B, int H, int L, int d, int num_splits);
+size_t fa_decode_workspace_bytes(int B, int H, int Hkv, int L, int d, int num_splits);
 
 /*
  * fa_decode -- one generation step against a KV cache (the cache the
@@ -138,16 +148,17 @@ size_t fa_decode_workspace_bytes(int B, int H, int L, int d, int num_splits);
  *          O = sum_s exp(lse_s - lse) o_s.
  *
  *   q                 [B,H,1,d] bf16 (dtype must be FA_BF16).
- *   k_cache, v_cache  [B,H,L,d] bf16, contiguous.
+ *   k_cache, v_cache  [B,Hkv,L,d] bf16, contiguous; query head h reads cache
+ *                     head h / (H/Hkv) (grouped-query attention, as for fa_fwd).
  *   o                 [B,H,1,d] bf16 output.
  *   lse               [B,H] float32 output, or NULL if not wanted.
- *   workspace         at least fa_decode_workspace_bytes(B,H,L,d,num_splits).
+ *   workspace         at least fa_decode_workspace_bytes(B,H,Hkv,L,d,num_splits).
  *   num_splits        0 = library's choice, else 1..L.
  */
 fa_status_t fa_decode(const void* q, const void* k_cache, const void* v_cache,
                       void* o, float* lse,
                       void* workspace, size_t workspace_bytes,
-                      int B, int H, int L, int d, fa_dtype_t dtype,
+                      int B, int H, int Hkv, int L, int d, fa_dtype_t dtype,
                       int num_splits, float scale, void* stream);
 
 /* fa_status_string -- a static, human-readable name for a status code. */

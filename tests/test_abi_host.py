@@ -61,11 +61,12 @@ def test_status_strings():
 
 
 def fwd(**kw):
-    args = dict(q=A, k=A, v=A, o=A, o_dtype=fa.FA_BF16, lse=A, B=1, H=1, N=16, d=64,
+    args = dict(q=A, k=A, v=A, o=A, o_dtype=fa.FA_BF16, lse=A, B=1, H=4, Hkv=None, N=16, d=64,
                 in_dtype=fa.FA_BF16, causal=0, scale=0.125)
     args.update(kw)
+    hkv = args["H"] if args["Hkv"] is None else args["Hkv"]
     return fa.fa_fwd(args["q"], args["k"], args["v"], args["o"], args["o_dtype"], args["lse"],
-                     args["B"], args["H"], args["N"], args["d"], args["in_dtype"], args["causal"],
+                     args["B"], args["H"], hkv, args["N"], args["d"], args["in_dtype"], args["causal"],
                      args["scale"], 0)
 
 
@@ -83,6 +84,9 @@ def fwd(**kw):
     (dict(scale=0.0), fa.FA_ERR_ARG),
     (dict(scale=-0.5), fa.FA_ERR_ARG),
     (dict(B=1 << 16, H=1 << 16, N=16), fa.FA_ERR_ARG),
+    (dict(Hkv=3), fa.FA_ERR_ARG),        # 3 K/V heads do not divide 4 query heads
+    (dict(Hkv=0), fa.FA_ERR_ARG),
+    (dict(Hkv=8), fa.FA_ERR_ARG),        # more K/V heads than query heads
     (dict(d=96), fa.FA_ERR_UNSUPPORTED),
     (dict(d=256), fa.FA_ERR_UNSUPPORTED),
     (dict(in_dtype=7), fa.FA_ERR_UNSUPPORTED),
@@ -98,19 +102,20 @@ def test_fwd_rejects(kw, status):
 
 
 def bwd(ws_bytes=None, **kw):
-    B, H, N, d = kw.get("B", 1), kw.get("H", 1), kw.get("N", 16), kw.get("d", 64)
+    B, H, N, d = kw.get("B", 1), kw.get("H", 4), kw.get("N", 16), kw.get("d", 64)
     need = fa.fa_bwd_workspace_bytes(B, H, N, d)
     args = dict(q=A, k=A, v=A, o=A, o_dtype=fa.FA_BF16, lse=A, dout=A, dq=A, dk=A, dv=A, ws=A,
-                B=B, H=H, N=N, d=d, in_dtype=fa.FA_BF16, causal=1, scale=0.125)
+                B=B, H=H, Hkv=2, N=N, d=d, in_dtype=fa.FA_BF16, causal=1, scale=0.125)
     args.update(kw)
     return fa.fa_bwd(args["q"], args["k"], args["v"], args["o"], args["o_dtype"], args["lse"],
                      args["dout"], args["dq"], args["dk"], args["dv"], args["ws"],
-                     need if ws_bytes is None else ws_bytes, args["B"], args["H"], args["N"], args["d"],
-                     args["in_dtype"], args["causal"], args["scale"], 0)
+                     need if ws_bytes is None else ws_bytes, args["B"], args["H"], args["Hkv"], args["N"],
+                     args["d"], args["in_dtype"], args["causal"], args["scale"], 0)
 
 
 @pytest.mark.parametrize("kw,status", [
     (dict(dout=0), fa.FA_ERR_NULL),
+    (dict(Hkv=3), fa.FA_ERR_ARG),
     (dict(dq=0), fa.FA_ERR_NULL),
     (dict(lse=0), fa.FA_ERR_NULL),
     (dict(N=0), fa.FA_ERR_ARG),
@@ -128,7 +133,7 @@ def test_bwd_rejects(kw, status):
 
 
 def test_bwd_rejects_small_workspace():
-    need = fa.fa_bwd_workspace_bytes(1, 1, 16, 64)
+    need = fa.fa_bwd_workspace_bytes(1, 4, 16, 64)
     assert bwd(ws_bytes=need - 1) == fa.FA_ERR_WORKSPACE
 
 
@@ -141,13 +146,13 @@ def test_bwd_workspace_size():
 
 def dec(ws_bytes=None, **kw):
     B, H, L, d, s = kw.get("B", 2), kw.get("H", 2), kw.get("L", 100), kw.get("d", 128), kw.get("splits", 0)
-    need = fa.fa_decode_workspace_bytes(B, H, L, d, max(s, 0))
-    args = dict(q=A, k=A, v=A, o=A, lse=A, ws=A, B=B, H=H, L=L, d=d, dtype=fa.FA_BF16,
+    need = fa.fa_decode_workspace_bytes(B, H, 1, L, d, max(s, 0))
+    args = dict(q=A, k=A, v=A, o=A, lse=A, ws=A, B=B, H=H, Hkv=1, L=L, d=d, dtype=fa.FA_BF16,
                 splits=s, scale=0.1)
     args.update(kw)
     return fa.fa_decode(args["q"], args["k"], args["v"], args["o"], args["lse"], args["ws"],
-                        need if ws_bytes is None else ws_bytes, args["B"], args["H"], args["L"],
-                        args["d"], args["dtype"], args["splits"], args["scale"], 0)
+                        need if ws_bytes is None else ws_bytes, args["B"], args["H"], args["Hkv"],
+                        args["L"], args["d"], args["dtype"], args["splits"], args["scale"], 0)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -155,6 +160,7 @@ def dec(ws_bytes=None, **kw):
     (dict(k=0), fa.FA_ERR_NULL),
     (dict(o=0), fa.FA_ERR_NULL),
     (dict(L=0), fa.FA_ERR_ARG),
+    (dict(Hkv=3), fa.FA_ERR_ARG),
     (dict(splits=-1), fa.FA_ERR_ARG),
     (dict(splits=101), fa.FA_ERR_ARG),
     (dict(scale=-1.0), fa.FA_ERR_ARG),
@@ -169,18 +175,20 @@ def test_decode_rejects(kw, status):
 
 
 def test_decode_rejects_small_workspace():
-    need = fa.fa_decode_workspace_bytes(2, 2, 100, 128, 4)
+    need = fa.fa_decode_workspace_bytes(2, 2, 1, 100, 128, 4)
     assert dec(ws_bytes=need - 1, splits=4) == fa.FA_ERR_WORKSPACE
 
 
 def test_decode_split_plan():
     # the automatic split count never exceeds L and never leaves a chunk empty
     for (B, H, L) in [(64, 32, 8192), (1, 1, 1), (1, 32, 16384), (2, 3, 700), (1, 1, 513)]:
-        s = fa.fa_decode_num_splits(B, H, L, 128)
+        s = fa.fa_decode_num_splits(B, H, H, L, 128)
         assert 1 <= s <= L
         chunk = -(-L // s)
         assert (s - 1) * chunk < L
     # a workspace holds d + 1 floats per (b, h, split)
-    s = fa.fa_decode_num_splits(64, 32, 8192, 128)
+    s = fa.fa_decode_num_splits(64, 32, 32, 8192, 128)
     parts = 64 * 32 * s
-    assert fa.fa_decode_workspace_bytes(64, 32, 8192, 128, 0) == ((parts * 128 * 4 + 255) // 256) * 256 + parts * 4
+    assert fa.fa_decode_workspace_bytes(64, 32, 32, 8192, 128, 0) == ((parts * 128 * 4 + 255) // 256) * 256 + parts * 4
+    # an invalid grouping sizes nothing
+    assert fa.fa_decode_workspace_bytes(64, 32, 5, 8192, 128, 0) == 0

@@ -165,7 +165,7 @@ def test_fwd_deterministic_and_allocation_free():
     say("fa_fwd determinism / no allocation")
     for o, l in ((o1, l1), (o2, l2)):
         st = fa.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), fa.FA_BF16, l.data_ptr(),
-                       2, 4, 1000, 128, fa.FA_BF16, 1, 1 / math.sqrt(128), stream)
+                       2, 4, 4, 1000, 128, fa.FA_BF16, 1, 1 / math.sqrt(128), stream)
         assert st == fa.FA_OK
     torch.cuda.synchronize()
     assert torch.cuda.max_memory_allocated() == before
@@ -300,3 +300,97 @@ def test_decode_deterministic():
     b = fa.decode(q, kc, vc)
     torch.cuda.synchronize()
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+# ----------------------------------------------------------------------------
+# grouped-query / multi-query attention: K and V carry Hkv < H heads
+# ----------------------------------------------------------------------------
+
+GQA_FWD = [
+    # (B, H, Hkv, N, d, dtype, causal)
+    (1, 8, 2, 300, 128, "bf16", True),
+    (2, 4, 1, 130, 64, "bf16", False),
+    (1, 6, 3, 257, 128, "bf16", False),
+    (1, 8, 1, 1000, 128, "bf16", True),
+    (2, 16, 8, 129, 64, "bf16", True),
+    (1, 4, 2, 200, 64, "fp32", True),
+    (1, 6, 2, 97, 128, "fp32", False),
+]
+
+
+@pytest.mark.parametrize("B,H,Hkv,N,d,dtype,causal", GQA_FWD)
+def test_fwd_gqa(B, H, Hkv, N, d, dtype, causal):
+    fa = _fa()
+    q, k, v = W.make_gqa(B, H, Hkv, N, d, dtype, seed=4000 + N + H + Hkv, device=DEV)
+    scale = 1.0 / math.sqrt(d)
+    say(f"fa_fwd gqa {dtype} B{B} H{H} Hkv{Hkv} N{N} d{d} causal={causal}")
+    o, lse = fa.attention(q, k, v, is_causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = ref_fwd(to64(q), to64(k), to64(v), causal, scale)
+    check = assert_fp32_close if dtype == "fp32" else assert_bf16_close
+    check(to64(o), o_ref, "O")
+    check(to64(lse), lse_ref, "LSE")
+
+
+GQA_BWD = [
+    # (B, H, Hkv, N, d, causal)
+    (1, 8, 2, 256, 128, True),
+    (2, 4, 1, 190, 64, False),
+    (1, 6, 3, 129, 128, True),
+    (1, 4, 1, 700, 128, True),
+    (1, 8, 4, 65, 64, True),
+]
+
+
+@pytest.mark.parametrize("B,H,Hkv,N,d,causal", GQA_BWD)
+def test_bwd_gqa(B, H, Hkv, N, d, causal):
+    fa = _fa()
+    q, k, v, do = W.make_gqa(B, H, Hkv, N, d, "bf16", seed=4100 + N + H + Hkv, with_dout=True, device=DEV)
+    scale = 1.0 / math.sqrt(d)
+    say(f"fa_bwd gqa B{B} H{H} Hkv{Hkv} N{N} d{d} causal={causal}")
+    o, lse = fa.attention(q, k, v, is_causal=causal, scale=scale)
+    dq, dk, dv = fa.attention_backward(q, k, v, o, lse, do, is_causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    assert tuple(dk.shape) == tuple(k.shape) and tuple(dv.shape) == tuple(v.shape)
+    rq, rk, rv = ref_bwd(to64(q), to64(k), to64(v), to64(do), causal, scale)
+    assert_grad_close(to64(dq), rq, "dQ")
+    assert_grad_close(to64(dk), rk, "dK")
+    assert_grad_close(to64(dv), rv, "dV")
+
+
+def test_bwd_gqa_deterministic():
+    fa = _fa()
+    q, k, v, do = W.make_gqa(1, 8, 2, 600, 128, "bf16", seed=4200, with_dout=True, device=DEV)
+    say("fa_bwd gqa determinism")
+    o, lse = fa.attention(q, k, v, is_causal=True)
+    a = fa.attention_backward(q, k, v, o, lse, do, is_causal=True)
+    b = fa.attention_backward(q, k, v, o, lse, do, is_causal=True)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+GQA_DEC = [
+    # (B, H, Hkv, L, d)
+    (3, 8, 2, 1000, 128),
+    (2, 8, 1, 777, 64),
+    (1, 32, 8, 4097, 128),
+    (2, 6, 3, 1, 128),
+    (2, 4, 4, 300, 64),
+]
+
+
+@pytest.mark.parametrize("B,H,Hkv,L,d", GQA_DEC)
+def test_decode_gqa(B, H, Hkv, L, d):
+    fa = _fa()
+    q, kc, vc = W.make_gqa(B, H, Hkv, 1, d, "bf16", seed=4300 + L + H + Hkv, device=DEV, Nk=L)
+    scale = 1.0 / math.sqrt(d)
+    o_ref, lse_ref = ref_decode(to64(q), to64(kc), to64(vc), scale)
+    for s in (0, 1, 4):
+        if s > L:
+            continue
+        say(f"fa_decode gqa B{B} H{H} Hkv{Hkv} L{L} d{d} splits={s}")
+        o, lse = fa.decode(q, kc, vc, scale=scale, num_splits=s)
+        torch.cuda.synchronize()
+        assert_bf16_close(to64(o), o_ref, f"O splits={s}")
+        assert_bf16_close(to64(lse), lse_ref, f"LSE splits={s}")
