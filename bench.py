@@ -14,8 +14,12 @@ A sweep over N = 2K..16K (H=32, B=16384/N, causal) reports forward and
 backward TFLOP/s as the metric's range asks, and the oracle's CPU time on a
 bounded sample is reported as ``cpu_baseline``.
 
+A grouped-query block (decode with 8 cache heads for 32 query heads, and
+fwd/bwd with groups of 4) is measured after the sweep and reported as ``gqa``.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-sweep]
-                       [--no-cpu-baseline]
+                       [--no-gqa] [--no-cpu-baseline]
+       python bench.py --reduce-counters DIR... [--write-traffic]   (host only)
 """
 
 from __future__ import annotations
@@ -47,6 +51,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-gqa", action="store_true", help="skip the grouped-query measurements")
     ap.add_argument("--reduce-counters", nargs="+", metavar="DIR",
                     help="host only: summarise rocprofv3 --pmc output of this script and exit")
     ap.add_argument("--write-traffic", action="store_true",
@@ -154,6 +159,72 @@ def sweep(torch, fa, W, dev, iters=10):
         out.append(res)
         del q, k, v, do, o, lse, dq, dk, dv, ws
         torch.cuda.empty_cache()
+    return out
+
+
+def gqa_measure(torch, fa, W, dev, iters=20):
+    """Grouped-query attention (K/V heads shared by groups of query heads).
+
+    decode: B64 H32 Hkv8 L8192 d128 (groups of 4); each cache head is read
+    once per group, so the algorithmic bytes are 2*B*Hkv*L*d*2.
+    fwd/bwd: B4 H16 Hkv4 N2048 d128 causal; same flops as multi-head.
+    """
+    stream = torch.cuda.current_stream().cuda_stream
+    out = {}
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(iters):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / iters
+
+    B, H, Hkv, L, d = 64, 32, 8, 8192, 128
+    q, kc, vc = W.make_gqa(B, H, Hkv, 1, d, "bf16", seed=20, device=dev, Nk=L)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    nb = fa.fa_decode_workspace_bytes(B, H, Hkv, L, d, 0)
+    ws = torch.empty((nb,), dtype=torch.uint8, device=dev)
+    scale = 1.0 / math.sqrt(d)
+    ms = timed(lambda: fa.fa_decode(q.data_ptr(), kc.data_ptr(), vc.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                    ws.data_ptr(), nb, B, H, Hkv, L, d, fa.FA_BF16, 0, scale, stream))
+    byt = 2.0 * B * Hkv * L * d * 2
+    gbs = byt / (ms * 1e-3) / 1e9
+    out["decode"] = {"workload": f"B{B} H{H} Hkv{Hkv} L{L} d{d}", "ms": round(ms, 4), "GBps": round(gbs, 1),
+                     "bound": "hbm", "frac": round(gbs / PEAK_HBM_GBPS, 4), "algorithmic_bytes": byt,
+                     "splits": fa.fa_decode_num_splits(B, H, Hkv, L, d)}
+    log(f"gqa decode {out['decode']['workload']}: {ms:.4f} ms, {gbs:.1f} GB/s")
+    del q, kc, vc, o, ws
+
+    B, H, Hkv, N = 4, 16, 4, 2048
+    q, k, v, do = W.make_gqa(B, H, Hkv, N, d, "bf16", seed=21, with_dout=True, device=dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    nb = fa.fa_bwd_workspace_bytes(B, H, N, d)
+    ws = torch.empty((nb,), dtype=torch.uint8, device=dev)
+
+    def f():
+        fa.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), fa.FA_BF16, lse.data_ptr(),
+                  B, H, Hkv, N, d, fa.FA_BF16, 1, scale, stream)
+
+    def g():
+        fa.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), fa.FA_BF16, lse.data_ptr(),
+                  do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr(), nb,
+                  B, H, Hkv, N, d, fa.FA_BF16, 1, scale, stream)
+
+    ff = fwd_flops(B, H, N, d)
+    for name, fn, mult in (("fwd", f, 1.0), ("bwd", g, 2.5)):
+        f()
+        ms = timed(fn)
+        tf = mult * ff / (ms * 1e-3) / 1e12
+        out[name] = {"workload": f"B{B} H{H} Hkv{Hkv} N{N} d{d} causal", "ms": round(ms, 4),
+                     "tflops": round(tf, 1), "bound": "mfma", "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
+        log(f"gqa {name} {out[name]['workload']}: {ms:.4f} ms, {tf:.1f} TFLOP/s")
     return out
 
 
@@ -435,6 +506,11 @@ def main():
         log("sweep N=2K..16K")
         sweep_res = sweep(torch, fa, W, dev)
 
+    gqa_res = None
+    if not args.no_gqa:
+        log("grouped-query attention")
+        gqa_res = gqa_measure(torch, fa, W, dev)
+
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
@@ -464,6 +540,7 @@ def main():
                     | {"kernel": dominant["kernel"]},
         "rooflines": roofs,
         "sweep": sweep_res,
+        "gqa": gqa_res,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

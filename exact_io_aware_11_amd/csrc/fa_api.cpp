@@ -37,12 +37,25 @@ fa_status_t from_hip(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP
 
 constexpr int kMaxSplits = 256;
 
-int auto_splits(int B, int H, int L) {
-    // Aim for at least ~4096 workgroups so every CU holds several, but keep
-    // each split at 512 keys or more so the merge stays negligible.
-    const long long bh = (long long)B * H;
-    long long s = (4096 + bh - 1) / bh;
-    const long long max_by_len = (L + 511) / 512;
+int auto_splits(int B, int H, int Hkv, int L) {
+    long long units, target, min_keys;
+    if (fa::decode_group_path(H, Hkv)) {
+        // grouped kernel: one wave per (b, cache head, chunk), four per
+        // workgroup and one workgroup per CU (its tiles fill the LDS): aim
+        // for ~1024 units, one round over the chip (measured better than two
+        // rounds of shorter chunks), with chunks of 256 keys or more
+        units = (long long)B * Hkv;
+        target = 1024;
+        min_keys = 256;
+    } else {
+        // per-head kernel: at least ~4096 workgroups so every CU holds
+        // several, chunks of 512 keys or more so the merge stays negligible
+        units = (long long)B * H;
+        target = 4096;
+        min_keys = 512;
+    }
+    long long s = (target + units - 1) / units;
+    const long long max_by_len = (L + min_keys - 1) / min_keys;
     if (s > max_by_len) s = max_by_len;
     if (s > kMaxSplits) s = kMaxSplits;
     if (s < 1) s = 1;
@@ -120,14 +133,14 @@ int fa_decode_num_splits(int B, int H, int Hkv, int L, int d) {
     (void)d;
     if (!dims_ok(B, H, L) || !kv_ok(H, Hkv)) return 1;
     int splits, chunk;
-    split_plan(L, auto_splits(B, H, L), splits, chunk);
+    split_plan(L, auto_splits(B, H, Hkv, L), splits, chunk);
     return splits;
 }
 
 size_t fa_decode_workspace_bytes(int B, int H, int Hkv, int L, int d, int num_splits) {
     if (!dims_ok(B, H, L) || !kv_ok(H, Hkv) || d < 1 || num_splits < 0 || !total_ok(B, H, L, d)) return 0;
     int splits, chunk;
-    split_plan(L, num_splits == 0 ? auto_splits(B, H, L) : (num_splits > L ? L : num_splits), splits, chunk);
+    split_plan(L, num_splits == 0 ? auto_splits(B, H, Hkv, L) : (num_splits > L ? L : num_splits), splits, chunk);
     const size_t parts = (size_t)B * H * splits;
     const size_t o_bytes = parts * (size_t)d * sizeof(float);
     return ((o_bytes + 255) & ~(size_t)255) + parts * sizeof(float);
@@ -140,14 +153,14 @@ fa_status_t fa_decode(const void* q, const void* k_cache, const void* v_cache, v
     if (!dims_ok(B, H, L) || !kv_ok(H, Hkv) || !scale_ok(scale) || num_splits < 0 || num_splits > L ||
         !total_ok(B, H, L, d))
         return FA_ERR_ARG;
-    if (!head_dim_ok(d) || dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+    if (!head_dim_ok(d) || dtype != FA_BF16 || !head_fits_u32(L, d)) return FA_ERR_UNSUPPORTED;
     if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o)) return FA_ERR_ALIGN;
     if (lse && !aligned16(lse)) return FA_ERR_ALIGN;
     const size_t need = fa_decode_workspace_bytes(B, H, Hkv, L, d, num_splits);
     if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
     if (!aligned16(workspace)) return FA_ERR_ALIGN;
     int splits, chunk;
-    split_plan(L, num_splits == 0 ? auto_splits(B, H, L) : num_splits, splits, chunk);
+    split_plan(L, num_splits == 0 ? auto_splits(B, H, Hkv, L) : num_splits, splits, chunk);
     const size_t parts = (size_t)B * H * splits;
     float* o_part = static_cast<float*>(workspace);
     float* lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) +

@@ -161,6 +161,176 @@ decode_split_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ Kc,
     }
 }
 
+// ---------------------------------------------------------------------------
+// Grouped-query decode: the G <= 32 query heads that share a cache head are
+// processed together, so each cached key and value is read from HBM once per
+// group instead of once per query head.  The heads are the rows of a small
+// matrix product: with q^T of the group as the B operand (G columns, padded
+// to 32 with zeros), S^T = K q^T and O^T += V^T P^T run on
+// v_mfma_f32_32x32x16_bf16 exactly as in the forward kernel, with the keys as
+// the streamed dimension.  Each wave is an independent unit of work -- one
+// (batch, cache head, key chunk) -- with its own double-buffered 32-key K and
+// V tiles in LDS filled by buffer DMA, so no workgroup barrier is needed.  The
+// online softmax (lazy rescaling as in the forward) runs per head column; the
+// unit writes the normalised partial o_s and lse_s of its G heads, and the
+// merge kernel below combines the chunks.
+// ---------------------------------------------------------------------------
+constexpr int DG_BC = 32;          // keys per tile
+static_assert(kDecodeMaxGroup <= 32, "one 32-column MFMA block of heads per unit");
+
+template <int D>
+__global__ void __launch_bounds__(DEC_THREADS)
+decode_group_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ Kc,
+                    const __bf16* __restrict__ Vc, float* __restrict__ Opart,
+                    float* __restrict__ LSEpart, int G, int L, int S, int chunk, int units,
+                    float c /* scale * log2(e) */) {
+    constexpr int ROWB = 2 * D;             // bytes per cached row
+    constexpr int CPR = D / 8;              // 16-byte chunks per row
+    constexpr int TILEB = DG_BC * ROWB;     // one K (or V) tile of one wave
+    constexpr int SEGS = TILEB / 1024;      // 1 KiB copy segments per tile
+    constexpr int RPS = 1024 / ROWB;        // rows per segment
+    constexpr float TAU = 8.f;              // lazy-rescale threshold, log2 units
+
+    // per-wave tile buffers; four separate LDS objects so that the copies into
+    // one buffer pair do not make the reads of the other wait
+    __shared__ __attribute__((aligned(1024))) char kb0[DEC_WAVES][TILEB];
+    __shared__ __attribute__((aligned(1024))) char kb1[DEC_WAVES][TILEB];
+    __shared__ __attribute__((aligned(1024))) char vb0[DEC_WAVES][TILEB];
+    __shared__ __attribute__((aligned(1024))) char vb1[DEC_WAVES][TILEB];
+
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int l32 = lane & 31, g = lane >> 5;
+    const int unit = blockIdx.x * DEC_WAVES + w;
+    if (unit >= units) return;              // no barrier below: waves are independent
+    const int s = unit % S;
+    const int gkv = unit / S;               // b * Hkv + cache head
+    const int k_begin = s * chunk;
+    const int k_end = min(L, k_begin + chunk);
+    const int ntile = (k_end - k_begin + DG_BC - 1) / DG_BC;
+
+    // q^T of the group as the B operand: column l32 is query head gkv*G + l32
+    bf16x8 qf[D / 16];
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+        uint4 u = make_uint4(0, 0, 0, 0);
+        if (l32 < G)
+            u = *reinterpret_cast<const uint4*>(Q + ((size_t)gkv * G + l32) * D + 16 * ks + 8 * g);
+        qf[ks] = as_bf16x8(u);
+    }
+
+    // one cache head (L * ROWB bytes < 2^32, checked by the host)
+    const size_t hoff = (size_t)gkv * (size_t)L * D;
+    const __amdgpu_buffer_rsrc_t k_rs = make_rsrc(Kc + hoff, (uint32_t)L * ROWB);
+    const __amdgpu_buffer_rsrc_t v_rs = make_rsrc(Vc + hoff, (uint32_t)L * ROWB);
+    // copy the 32 rows of tile t (rows past the cache end clamped to L-1; they
+    // are masked for K and weighted by 0 for V)
+    auto issue = [&](int t, char* kdst, char* vdst) __attribute__((always_inline)) {
+        const int k0 = k_begin + t * DG_BC;
+#pragma unroll
+        for (int seg = 0; seg < SEGS; ++seg) {
+            const int row = seg * RPS + lane / CPR;
+            const int pc = lane % CPR;
+            const uint32_t grow = (uint32_t)min(k0 + row, L - 1) * ROWB;
+            b2lds16(k_rs, grow + 16 * (pc ^ k_swz<D>(row)), kdst + seg * 1024);
+            b2lds16(v_rs, grow + 16 * (pc ^ v_swz<D>(row)), vdst + seg * 1024);
+        }
+    };
+
+    // LDS offsets as in the forward: K rows read one chunk per lane, V^T read
+    // with the transposing 8-byte read
+    int k_off[D / 16];
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) k_off[ks] = l32 * ROWB + 16 * ((2 * ks + g) ^ k_swz<D>(l32));
+    const int vr = 4 * g + ((lane & 15) >> 2);
+    const int vc = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    const int vsw = v_swz<D>(vr) >> 2;
+    int v_off[D / 32];
+#pragma unroll
+    for (int mb = 0; mb < D / 32; ++mb) v_off[mb] = vr * ROWB + 16 * (4 * (mb ^ vsw) + (vc >> 3)) + 2 * (vc & 7);
+
+    f32x16 oacc[D / 32];
+#pragma unroll
+    for (int mb = 0; mb < D / 32; ++mb) oacc[mb] = zero16();
+    float m_ref = -INFINITY, l_run = 0.f;
+
+    auto step = [&](int t, const char* Ks, const char* Vs, char* kn, char* vn) __attribute__((always_inline)) {
+        // this tile's copies have landed, and this wave's reads of the other
+        // buffer pair (the previous tile) are complete before it is refilled
+        __builtin_amdgcn_s_waitcnt(0);
+        if (t + 1 < ntile) issue(t + 1, kn, vn);
+        // S^T = K q^T: keys x heads; lane holds head l32, keys 8(r/4) + 4g + r%4
+        f32x16 st = zero16();
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks)
+            st = mfma_bf16(*reinterpret_cast<const bf16x8*>(Ks + k_off[ks]), qf[ks], st);
+        const int lim = k_end - 1 - (k_begin + t * DG_BC) - 4 * g;   // last live key slot
+        float mx = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            st[r] = (8 * (r >> 2) + (r & 3) > lim) ? -INFINITY : st[r];
+            mx = fmaxf(mx, st[r]);
+        }
+        mx = xor32_max(mx) * c;
+        if (__any(mx > m_ref + TAU)) {
+            const float m_new = fmaxf(m_ref, mx);
+            const float alpha = exp2_fast(m_ref - m_new);   // 0 on the first tile
+            m_ref = m_new;
+            l_run *= alpha;
+#pragma unroll
+            for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[mb][r] *= alpha;
+        }
+        const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
+        bf16x8 pb[2];
+        float psum = 0.f;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            uint32_t pk[4];
+#pragma unroll
+            for (int j = 0; j < 8; j += 2) {
+                const float p0 = exp2_fast(fmaf(st[8 * h + j], c, -m_use));
+                const float p1 = exp2_fast(fmaf(st[8 * h + j + 1], c, -m_use));
+                pk[j / 2] = pack_bf16x2(p0, p1);
+                psum = sum_bf16x2(pk[j / 2], psum);
+            }
+            pb[h] = as_bf16x8(make_uint4(pk[0], pk[1], pk[2], pk[3]));
+        }
+        l_run += psum;
+        // O^T += V^T P^T
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int mb = 0; mb < D / 32; ++mb) {
+                const uint2 lo = lds_read_tr16x4(Vs + (16 * ks) * ROWB + v_off[mb]);
+                const uint2 hi = lds_read_tr16x4(Vs + (16 * ks + 8) * ROWB + v_off[mb]);
+                oacc[mb] = mfma_bf16(as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)), pb[ks], oacc[mb]);
+            }
+    };
+
+    issue(0, kb0[w], vb0[w]);
+    for (int t = 0; t < ntile; t += 2) {
+        step(t, kb0[w], vb0[w], kb1[w], vb1[w]);
+        if (t + 1 < ntile) step(t + 1, kb1[w], vb1[w], kb0[w], vb0[w]);
+    }
+
+    // normalised partial of each real head of the group
+    const float l_tot = xor32_sum(l_run);
+    if (l32 < G) {
+        const size_t pidx = ((size_t)gkv * G + l32) * S + s;
+        const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
+        float* orow = Opart + pidx * D;
+#pragma unroll
+        for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb)
+                *reinterpret_cast<float4*>(orow + 32 * mb + 8 * rb + 4 * g) =
+                    make_float4(oacc[mb][4 * rb] * inv, oacc[mb][4 * rb + 1] * inv,
+                                oacc[mb][4 * rb + 2] * inv, oacc[mb][4 * rb + 3] * inv);
+        if (g == 0) LSEpart[pidx] = (l_tot > 0.f) ? m_ref * kLn2 + __logf(l_tot) : -INFINITY;
+    }
+}
+
 // One wave per (b, h); lane t handles dims t and t + 64 (d = 128) or t (d = 64).
 template <int D>
 __global__ void __launch_bounds__(DEC_THREADS)
@@ -194,10 +364,18 @@ decode_merge_kernel(const float* __restrict__ Opart, const float* __restrict__ L
 template <int D>
 hipError_t launch_d(const DecodeArgs& a) {
     const int BH = a.B * a.H;
+    const int G = a.H / a.Hkv;
     hipStream_t st = (hipStream_t)a.stream;
-    hipLaunchKernelGGL((decode_split_kernel<D>), dim3((unsigned)(BH * a.splits)), dim3(DEC_THREADS), 0, st,
-                       (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, a.o_part, a.lse_part,
-                       a.H / a.Hkv, a.L, a.splits, a.chunk, a.scale * kLog2e);
+    if (decode_group_path(a.H, a.Hkv)) {
+        const int units = a.B * a.Hkv * a.splits;
+        hipLaunchKernelGGL((decode_group_kernel<D>), dim3((unsigned)((units + DEC_WAVES - 1) / DEC_WAVES)),
+                           dim3(DEC_THREADS), 0, st, (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v,
+                           a.o_part, a.lse_part, G, a.L, a.splits, a.chunk, units, a.scale * kLog2e);
+    } else {
+        hipLaunchKernelGGL((decode_split_kernel<D>), dim3((unsigned)(BH * a.splits)), dim3(DEC_THREADS), 0, st,
+                           (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, a.o_part, a.lse_part,
+                           G, a.L, a.splits, a.chunk, a.scale * kLog2e);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((decode_merge_kernel<D>), dim3((unsigned)((BH + DEC_WAVES - 1) / DEC_WAVES)),

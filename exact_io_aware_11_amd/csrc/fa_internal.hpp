@@ -54,6 +54,15 @@ struct DecodeArgs {
     void* stream;
 };
 
+// Decode takes the grouped-query kernel (each cache head read once for all
+// the query heads sharing it) when 2 <= H/Hkv <= kDecodeMaxGroup; otherwise
+// the per-query-head kernel.
+constexpr int kDecodeMaxGroup = 32;
+inline bool decode_group_path(int H, int Hkv) {
+    const int G = H / Hkv;
+    return G >= 2 && G <= kDecodeMaxGroup;
+}
+
 hipError_t launch_fwd(const FwdArgs& a);
 hipError_t launch_bwd(const BwdArgs& a);
 hipError_t launch_decode(const DecodeArgs& a);

@@ -192,3 +192,21 @@ def test_decode_split_plan():
     assert fa.fa_decode_workspace_bytes(64, 32, 32, 8192, 128, 0) == ((parts * 128 * 4 + 255) // 256) * 256 + parts * 4
     # an invalid grouping sizes nothing
     assert fa.fa_decode_workspace_bytes(64, 32, 5, 8192, 128, 0) == 0
+
+
+def test_decode_split_plan_grouped():
+    # grouped path (2 <= H/Hkv <= 32): splits sized by the B*Hkv units
+    for (B, H, Hkv, L) in [(64, 32, 8, 8192), (1, 32, 1, 100), (2, 8, 2, 255), (4, 6, 3, 1)]:
+        s = fa.fa_decode_num_splits(B, H, Hkv, L, 128)
+        assert 1 <= s <= L
+        chunk = -(-L // s)
+        assert (s - 1) * chunk < L
+        parts = B * H * s
+        assert fa.fa_decode_workspace_bytes(B, H, Hkv, L, 128, 0) == \
+            ((parts * 128 * 4 + 255) // 256) * 256 + parts * 4
+    # 512 (batch, cache head) units of 8192 keys: 2 chunks of 4096
+    assert fa.fa_decode_num_splits(64, 32, 8, 8192, 128) == 2
+
+
+def test_decode_rejects_cache_head_of_4gib():
+    assert dec(L=1 << 24, d=128) == fa.FA_ERR_UNSUPPORTED

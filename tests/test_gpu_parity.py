@@ -371,12 +371,16 @@ def test_bwd_gqa_deterministic():
 
 
 GQA_DEC = [
-    # (B, H, Hkv, L, d)
+    # (B, H, Hkv, L, d): groups of 2..32 take the grouped kernel; G = 1 and
+    # G > 32 the per-head kernel
     (3, 8, 2, 1000, 128),
     (2, 8, 1, 777, 64),
     (1, 32, 8, 4097, 128),
     (2, 6, 3, 1, 128),
     (2, 4, 4, 300, 64),
+    (1, 32, 1, 2049, 128),
+    (1, 64, 1, 500, 64),
+    (2, 12, 4, 33, 64),
 ]
 
 
@@ -386,7 +390,7 @@ def test_decode_gqa(B, H, Hkv, L, d):
     q, kc, vc = W.make_gqa(B, H, Hkv, 1, d, "bf16", seed=4300 + L + H + Hkv, device=DEV, Nk=L)
     scale = 1.0 / math.sqrt(d)
     o_ref, lse_ref = ref_decode(to64(q), to64(kc), to64(vc), scale)
-    for s in (0, 1, 4):
+    for s in (0, 1, 2, 4, 7):
         if s > L:
             continue
         say(f"fa_decode gqa B{B} H{H} Hkv{Hkv} L{L} d{d} splits={s}")
@@ -394,3 +398,19 @@ def test_decode_gqa(B, H, Hkv, L, d):
         torch.cuda.synchronize()
         assert_bf16_close(to64(o), o_ref, f"O splits={s}")
         assert_bf16_close(to64(lse), lse_ref, f"LSE splits={s}")
+
+
+def test_decode_gqa_b64h32kv8l8192d128_sampled_batches():
+    # the cache workload's shape with 8 cache heads (groups of 4), at the
+    # launch configuration the grouped kernel picks
+    fa = _fa()
+    B, H, Hkv, L, d = 64, 32, 8, 8192, 128
+    q, kc, vc = W.make_gqa(B, H, Hkv, 1, d, "bf16", seed=4400, device=DEV, Nk=L)
+    scale = 1.0 / math.sqrt(d)
+    say(f"fa_decode gqa B{B} H{H} Hkv{Hkv} L{L} splits=auto")
+    o, lse = fa.decode(q, kc, vc, scale=scale)
+    torch.cuda.synchronize()
+    for b in (0, 17, 40, B - 1):
+        o_ref, lse_ref = ref_decode(to64(q[b:b + 1]), to64(kc[b:b + 1]), to64(vc[b:b + 1]), scale)
+        assert_bf16_close(to64(o[b:b + 1]), o_ref, f"O batch {b}")
+        assert_bf16_close(to64(lse[b:b + 1]), lse_ref, f"LSE batch {b}")
