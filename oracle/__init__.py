@@ -11,6 +11,7 @@ from .attention import (  # noqa: F401
     kv_head,
     ref_bwd,
     ref_decode,
+    ref_decode_paged,
     ref_fwd,
     ref_fwd_rows,
     ref_fwd_tiled,

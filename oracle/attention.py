@@ -56,6 +56,7 @@ __all__ = [
     "ref_fwd_tiled",
     "ref_bwd",
     "ref_decode",
+    "ref_decode_paged",
     "ref_merge_partials",
 ]
 
@@ -284,6 +285,41 @@ def ref_decode(q, k_cache, v_cache, scale: float):
     """
     o, lse = ref_fwd(q, k_cache, v_cache, causal=False, scale=scale)
     return o, lse[:, :, 0]
+
+
+def ref_decode_paged(q, k_pool, v_pool, block_table, seq_lens, scale: float):
+    """Decode step against a paged KV cache.
+
+    The attention-backend page (sections "Wat is het precies?" and "Voorbeelden
+    uit de praktijk", PagedAttention) describes cutting the KV cache into small
+    blocks allocated from a pool instead of one contiguous reservation, with the
+    same mathematical result.  Reading used here: the pool holds P pages of
+    ``page_size`` tokens per K/V head, k_pool and v_pool [P, Hkv, page_size, d];
+    sequence b owns the pages block_table[b, 0], block_table[b, 1], ... in
+    token order, and its first seq_lens[b] tokens are its cache.  The result is
+    ``ref_decode`` over that token sequence.  A sequence of length 0 gets
+    O = 0 and LSE = -inf (the fully-masked convention).
+
+    q [B,H,1,d] -> O [B,H,1,d], LSE [B,H] in float64.
+    """
+    q64 = _f64(q)
+    kp, vp = _f64(k_pool), _f64(v_pool)
+    bt = np.asarray(block_table, dtype=np.int64)
+    lens = np.asarray(seq_lens, dtype=np.int64)
+    B, H, _, d = q64.shape
+    Hkv, ps = kp.shape[1], kp.shape[2]
+    o = np.zeros((B, H, 1, vp.shape[-1]))
+    lse = np.full((B, H), -np.inf)
+    for b in range(B):
+        n_tok = int(lens[b])
+        n_pg = -(-n_tok // ps)
+        pages = bt[b, :n_pg]
+        # gather the sequence's pages in order: [Hkv, n_pg * ps, d], then cut to its length
+        kb = np.concatenate([kp[p] for p in pages], axis=1)[:, :n_tok] if n_pg else np.zeros((Hkv, 0, d))
+        vb = np.concatenate([vp[p] for p in pages], axis=1)[:, :n_tok] if n_pg else np.zeros((Hkv, 0, d))
+        ob, lb = ref_fwd(q64[b:b + 1], kb[None], vb[None], causal=False, scale=scale)
+        o[b], lse[b] = ob[0], lb[0, :, 0]
+    return o, lse
 
 
 def ref_merge_partials(o_parts, lse_parts):

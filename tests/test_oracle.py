@@ -505,3 +505,66 @@ def test_gqa_decode_is_one_query_forward():
     ot = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, scale=0.3, enable_gqa=True)
     np.testing.assert_allclose(o, ot.numpy(), atol=1e-10, rtol=0)
     assert lse.shape == (B, H)
+
+
+
+# ----------------------------------------------------------------------------
+# paged KV cache (next row f2)
+# ----------------------------------------------------------------------------
+
+def _scatter_to_pool(k, v, lens, ps, seed, extra_pages=3):
+    """Test-side construction of a paged pool from contiguous caches [B,Hkv,L,d]:
+    the pages of all sequences are placed at shuffled pool slots."""
+    B, Hkv, L, d = k.shape
+    n_pg = [-(-int(n) // ps) for n in lens]
+    total = sum(n_pg) + extra_pages
+    slots = rng(seed).permutation(total)
+    kp = rng(seed + 1).standard_normal((total, Hkv, ps, d))   # garbage in unused rows
+    vp = rng(seed + 2).standard_normal((total, Hkv, ps, d))
+    table = np.full((B, max(max(n_pg), 1)), -1, dtype=np.int64)
+    i = 0
+    for b in range(B):
+        for j in range(n_pg[b]):
+            t0, t1 = j * ps, min(int(lens[b]), (j + 1) * ps)
+            kp[slots[i], :, :t1 - t0] = k[b, :, t0:t1]
+            vp[slots[i], :, :t1 - t0] = v[b, :, t0:t1]
+            table[b, j] = slots[i]
+            i += 1
+    return kp, vp, table
+
+
+def pin_paged_equals_contiguous(decode_paged):
+    B, H, Hkv, L, d, ps = 3, 4, 2, 23, 5, 4
+    q, k, v, _ = _gqa_inputs(80, B, H, Hkv, L, d)
+    q1 = q[:, :, :1]
+    lens = np.array([23, 9, 1])
+    kp, vp, table = _scatter_to_pool(k, v, lens, ps, seed=81)
+    o, lse = decode_paged(q1, kp, vp, table, lens, 0.6)
+    for b in range(B):
+        n = int(lens[b])
+        tq, tk, tv = (torch.from_numpy(x) for x in (q1[b:b + 1], k[b:b + 1, :, :n], v[b:b + 1, :, :n]))
+        ot = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, scale=0.6, enable_gqa=True)
+        np.testing.assert_allclose(o[b:b + 1], ot.numpy(), atol=1e-10, rtol=0)
+        o_ref, lse_ref = ref_decode(q1[b:b + 1], k[b:b + 1, :, :n], v[b:b + 1, :, :n], 0.6)
+        np.testing.assert_allclose(lse[b:b + 1], lse_ref, atol=1e-12, rtol=0)
+
+
+def test_paged_decode_pin():
+    pin_paged_equals_contiguous(oracle.ref_decode_paged)
+
+
+def test_paged_decode_empty_sequence():
+    q, k, v, _ = _gqa_inputs(82, 2, 2, 1, 8, 3)
+    kp, vp, table = _scatter_to_pool(k, v, [8, 0], 4, seed=83)
+    o, lse = oracle.ref_decode_paged(q[:, :, :1], kp, vp, table, [8, 0], 0.5)
+    assert np.all(o[1] == 0.0) and np.all(np.isneginf(lse[1]))
+    assert np.all(np.isfinite(lse[0]))
+
+
+def test_paged_pin_catches_ignored_block_table():
+    # a paged decode that reads pages in pool order instead of through the table
+    def wrong(q, kp, vp, table, lens, scale):
+        ident = np.arange(np.asarray(table).size).reshape(np.shape(table))
+        return oracle.ref_decode_paged(q, kp, vp, ident, lens, scale)
+    with pytest.raises(AssertionError):
+        pin_paged_equals_contiguous(wrong)
