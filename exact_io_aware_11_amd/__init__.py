@@ -7,14 +7,16 @@ no fallback: if the library is missing, importing this package fails.
 
 Entry points with the C names (raw pointers, sizes, stream handle):
 ``fa_fwd``, ``fa_bwd``, ``fa_bwd_workspace_bytes``, ``fa_decode``,
-``fa_decode_workspace_bytes``, ``fa_decode_num_splits``, ``fa_status_string``.
+``fa_decode_workspace_bytes``, ``fa_decode_num_splits``, ``fa_decode_paged``,
+``fa_status_string``.
 
 Tensor-level helpers with the same semantics:
 ``attention(q, k, v, is_causal=False, scale=None, out_dtype=None) -> (o, lse)``
 (the call shape of PyTorch's scaled_dot_product_attention that the pages show),
 ``attention_backward(q, k, v, o, lse, do, is_causal=False, scale=None)``
 ``-> (dq, dk, dv)`` and ``decode(q, k_cache, v_cache, scale=None,
-num_splits=0) -> (o, lse)``.
+num_splits=0) -> (o, lse)`` and ``decode_paged(q, k_pool, v_pool, block_table,
+seq_lens, scale=None, num_splits=0) -> (o, lse)``.
 """
 
 from __future__ import annotations
@@ -27,8 +29,8 @@ __all__ = [
     "LIB_PATH", "FA_OK", "FA_ERR_NULL", "FA_ERR_ARG", "FA_ERR_UNSUPPORTED", "FA_ERR_ALIGN",
     "FA_ERR_WORKSPACE", "FA_ERR_HIP", "FA_FP32", "FA_BF16", "FaError",
     "fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_decode", "fa_decode_workspace_bytes",
-    "fa_decode_num_splits", "fa_status_string",
-    "attention", "attention_backward", "decode", "lib",
+    "fa_decode_num_splits", "fa_decode_paged", "fa_status_string",
+    "attention", "attention_backward", "decode", "decode_paged", "lib",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
@@ -55,7 +57,7 @@ def _load() -> ctypes.CDLL:
         pass
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is missing: build it first (python -m exact_io_aware_11_amd.build). "
+            f"{LIB_PATH} is missing: build it first (python exact_io_aware_11_amd/build.py). "
             "There is no fallback implementation.")
     lib_ = ctypes.CDLL(LIB_PATH)
     P, I, F, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
@@ -71,6 +73,8 @@ def _load() -> ctypes.CDLL:
     lib_.fa_decode_workspace_bytes.restype = Z
     lib_.fa_decode.argtypes = [P, P, P, P, P, P, Z, I, I, I, I, I, I, I, F, P]
     lib_.fa_decode.restype = I
+    lib_.fa_decode_paged.argtypes = [P, P, P, P, P, P, P, P, Z, I, I, I, I, I, I, I, I, I, F, P]
+    lib_.fa_decode_paged.restype = I
     lib_.fa_status_string.argtypes = [I]
     lib_.fa_status_string.restype = ctypes.c_char_p
     return lib_
@@ -113,6 +117,14 @@ def fa_decode(q, k_cache, v_cache, o, lse, workspace, workspace_bytes, B, H, Hkv
               num_splits, scale, stream=0) -> int:
     return lib.fa_decode(q, k_cache, v_cache, o, lse, workspace, workspace_bytes, B, H, Hkv, L, d,
                          dtype, num_splits, scale, stream)
+
+
+def fa_decode_paged(q, k_pool, v_pool, block_table, seq_lens, o, lse, workspace, workspace_bytes,
+                    B, H, Hkv, num_pages, page_size, max_pages_per_seq, d, dtype, num_splits, scale,
+                    stream=0) -> int:
+    return lib.fa_decode_paged(q, k_pool, v_pool, block_table, seq_lens, o, lse, workspace, workspace_bytes,
+                               B, H, Hkv, num_pages, page_size, max_pages_per_seq, d, dtype, num_splits,
+                               scale, stream)
 
 
 # ----------------------------------------------------------------------------
@@ -230,4 +242,40 @@ def decode(q, k_cache, v_cache, scale: float | None = None, num_splits: int = 0)
     st = fa_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), o.data_ptr(), lse.data_ptr(),
                    ws.data_ptr(), nbytes, B, H, Hkv, L, d, _dtype_code(q), num_splits, scale, _stream(q))
     _raise(st, "fa_decode")
+    return o, lse
+
+
+def decode_paged(q, k_pool, v_pool, block_table, seq_lens, scale: float | None = None, num_splits: int = 0):
+    """One decode step against a paged cache, via ``fa_decode_paged``.
+
+    q [B,H,1,d] bf16; k_pool, v_pool [num_pages, Hkv, page_size, d] bf16;
+    block_table [B, max_pages] int32 and seq_lens [B] int32 on the GPU.
+    Returns (o [B,H,1,d] bf16, lse [B,H] fp32).
+    """
+    torch = _torch()
+    _check(q, "q")
+    B, H, one, d = q.shape
+    if one != 1:
+        raise ValueError("decode takes one query token per (batch, head)")
+    _check(k_pool, "k_pool")
+    num_pages, Hkv, page_size = k_pool.shape[0], k_pool.shape[1], k_pool.shape[2]
+    _check(k_pool, "k_pool", (num_pages, Hkv, page_size, d))
+    _check(v_pool, "v_pool", (num_pages, Hkv, page_size, d))
+    _check(block_table, "block_table")
+    _check(seq_lens, "seq_lens", (B,))
+    if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
+        raise TypeError("block_table and seq_lens must be int32")
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be [B, max_pages_per_seq]")
+    max_pages = block_table.shape[1]
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    o = torch.empty((B, H, 1, d), dtype=q.dtype, device=q.device)
+    lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    nbytes = fa_decode_workspace_bytes(B, H, Hkv, max_pages * page_size, d, num_splits)
+    ws = torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=q.device)
+    st = fa_decode_paged(q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), block_table.data_ptr(),
+                         seq_lens.data_ptr(), o.data_ptr(), lse.data_ptr(), ws.data_ptr(), nbytes,
+                         B, H, Hkv, num_pages, page_size, max_pages, d, _dtype_code(q), num_splits, scale,
+                         _stream(q))
+    _raise(st, "fa_decode_paged")
     return o, lse

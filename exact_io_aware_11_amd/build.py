@@ -1,6 +1,8 @@
 """Build the HIP library ``libfa.so`` in-tree for gfx950.
 
-Usage: ``python -m exact_io_aware_11_amd.build`` (or ``build()`` from Python).
+Usage: ``python exact_io_aware_11_amd/build.py`` (or ``build()`` of the repository's
+``__graft_entry__``).  Run it as a script, not as ``-m exact_io_aware_11_amd.build``:
+importing the package loads the library this script is meant to (re)build.
 Every call recompiles: hipcc cross-compiles for gfx950 without a GPU.
 """
 

@@ -62,10 +62,20 @@ int auto_splits(int B, int H, int Hkv, int L) {
     return (int)s;
 }
 
-// Effective split count: chunks of ceil(L/S) keys, with no empty chunk.
+// Effective split count: chunks of ceil(L/S) keys rounded up to a multiple of
+// 32 (a 32-key tile of the grouped kernel then never straddles a page of a
+// paged cache), with no empty chunk for a cache of length L.
 void split_plan(int L, int requested, int& splits, int& chunk) {
     chunk = (L + requested - 1) / requested;
+    chunk = (chunk + 31) / 32 * 32;
     splits = (L + chunk - 1) / chunk;
+}
+
+bool pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+int log2i(int x) {
+    int r = 0;
+    while ((1 << r) < x) ++r;
+    return r;
 }
 
 }  // namespace
@@ -166,6 +176,38 @@ fa_status_t fa_decode(const void* q, const void* k_cache, const void* v_cache, v
     float* lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                                (((parts * (size_t)d * sizeof(float)) + 255) & ~(size_t)255));
     fa::DecodeArgs a{q, k_cache, v_cache, o, lse, o_part, lse_part, B, H, Hkv, L, d, splits, chunk, scale, stream};
+    return from_hip(fa::launch_decode(a));
+}
+
+fa_status_t fa_decode_paged(const void* q, const void* k_pool, const void* v_pool, const int32_t* block_table,
+                            const int32_t* seq_lens, void* o, float* lse, void* workspace, size_t workspace_bytes,
+                            int B, int H, int Hkv, int num_pages, int page_size, int max_pages_per_seq, int d,
+                            fa_dtype_t dtype, int num_splits, float scale, void* stream) {
+    if (!q || !k_pool || !v_pool || !block_table || !seq_lens || !o) return FA_ERR_NULL;
+    if (!dims_ok(B, H, 1) || !kv_ok(H, Hkv) || !scale_ok(scale) || num_pages < 1 || max_pages_per_seq < 1 ||
+        num_splits < 0)
+        return FA_ERR_ARG;
+    const long long Lmax = (long long)max_pages_per_seq * page_size;
+    if (!pow2(page_size) || page_size < 32 || page_size > (1 << 16) || Lmax > 0x7fffffffLL ||
+        num_splits > Lmax || !total_ok(B, H, (int)Lmax, d) || (long long)B * max_pages_per_seq > 0x7fffffffLL)
+        return FA_ERR_ARG;
+    if (!head_dim_ok(d) || dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+    if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(o)) return FA_ERR_ALIGN;
+    if ((reinterpret_cast<uintptr_t>(block_table) & 3) || (reinterpret_cast<uintptr_t>(seq_lens) & 3))
+        return FA_ERR_ALIGN;
+    if (lse && !aligned16(lse)) return FA_ERR_ALIGN;
+    const int L = (int)Lmax;
+    const size_t need = fa_decode_workspace_bytes(B, H, Hkv, L, d, num_splits);
+    if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return FA_ERR_ALIGN;
+    int splits, chunk;
+    split_plan(L, num_splits == 0 ? auto_splits(B, H, Hkv, L) : num_splits, splits, chunk);
+    const size_t parts = (size_t)B * H * splits;
+    float* o_part = static_cast<float*>(workspace);
+    float* lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                               (((parts * (size_t)d * sizeof(float)) + 255) & ~(size_t)255));
+    fa::DecodeArgs a{q, k_pool, v_pool, o, lse, o_part, lse_part, B, H, Hkv, L, d, splits, chunk, scale, stream,
+                     fa::Paging{block_table, seq_lens, num_pages, max_pages_per_seq, log2i(page_size), Hkv}};
     return from_hip(fa::launch_decode(a));
 }
 

@@ -40,11 +40,11 @@ __device__ __forceinline__ void merge_state(float& ma, float& la, float* oa, flo
     ma = mn;
 }
 
-template <int D>
+template <int D, bool PAGED>
 __global__ void __launch_bounds__(DEC_THREADS)
 decode_split_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ Kc,
                     const __bf16* __restrict__ Vc, float* __restrict__ Opart,
-                    float* __restrict__ LSEpart, int G, int L, int S, int chunk, float c) {
+                    float* __restrict__ LSEpart, int G, int L, int S, int chunk, float c, Paging pg) {
     constexpr int LPK = D / 8;           // lanes per key (8 bf16 each)
     constexpr int KPL = 64 / LPK;        // keys covered by one wave-wide load
     constexpr int U = DEC_UNROLL;
@@ -58,8 +58,31 @@ decode_split_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ Kc,
     const int slot = lane / LPK, dc = lane % LPK;
     const int s = blockIdx.x % S;
     const int bh = blockIdx.x / S;
+    const int gkv = bh / G;                 // b * Hkv + cache head of this query head
+    int Lb = L;                             // this sequence's cache length
+    int b = 0, hk = 0;
+    if constexpr (PAGED) {
+        b = gkv / pg.Hkv;
+        hk = gkv % pg.Hkv;
+        Lb = min(max(pg.seq_lens[b], 0), L);
+    }
     const int k_begin = s * chunk;
-    const int k_end = min(L, k_begin + chunk);
+    const int k_end = min(Lb, k_begin + chunk);   // may be <= k_begin: an empty chunk
+
+    // element offset of cached row `key` of this head; `ok` is false for a
+    // key on a page outside the pool (such keys are skipped)
+    auto row_of = [&](int key, bool& ok) __attribute__((always_inline)) -> size_t {
+        if constexpr (PAGED) {
+            const int page = pg.block_table[(size_t)b * pg.max_pages + (key >> pg.ps_log2)];
+            ok = page >= 0 && page < pg.num_pages;
+            const size_t prow = (((size_t)(ok ? page : 0) * pg.Hkv + hk) << pg.ps_log2) +
+                                (size_t)(key & ((1 << pg.ps_log2) - 1));
+            return prow * D;
+        } else {
+            ok = true;
+            return ((size_t)gkv * L + key) * D;
+        }
+    };
 
     // q, pre-multiplied by scale*log2(e), 8 dims per lane
     float qv[8];
@@ -73,9 +96,8 @@ decode_split_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ Kc,
         }
     }
 
-    const size_t hoff = (size_t)(bh / G) * (size_t)L * D;   // this query head's cache head
-    const __bf16* Kh = Kc + hoff + 8 * dc;
-    const __bf16* Vh = Vc + hoff + 8 * dc;
+    const __bf16* Kl = Kc + 8 * dc;         // this lane's 8 dims of any row
+    const __bf16* Vl = Vc + 8 * dc;
 
     float m = -INFINITY, l = 0.f;
     float o[8];
@@ -84,14 +106,19 @@ decode_split_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ Kc,
 
     for (int base = k_begin + w * STEP; base < k_end; base += DEC_WAVES * STEP) {
         uint4 kr[U], vr[U];
+        bool live[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int key = base + u * KPL + slot;
             kr[u] = make_uint4(0, 0, 0, 0);
             vr[u] = kr[u];
+            live[u] = false;
             if (key < k_end) {
-                kr[u] = load_stream16(Kh + (size_t)key * D);
-                vr[u] = load_stream16(Vh + (size_t)key * D);
+                const size_t r = row_of(key, live[u]);
+                if (live[u]) {
+                    kr[u] = load_stream16(Kl + r);
+                    vr[u] = load_stream16(Vl + r);
+                }
             }
         }
         float x[U];
@@ -106,7 +133,7 @@ decode_split_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ Kc,
                 dot = fmaf(bf16_hi(p[j]), qv[2 * j + 1], dot);
             }
             dot = (LPK == 16) ? dpp_sum16(dot) : dpp_sum8(dot);
-            x[u] = (base + u * KPL + slot < k_end) ? dot : -INFINITY;
+            x[u] = live[u] ? dot : -INFINITY;
             mx = fmaxf(mx, x[u]);
         }
         const float mn = fmaxf(m, mx);
@@ -178,12 +205,12 @@ decode_split_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ Kc,
 constexpr int DG_BC = 32;          // keys per tile
 static_assert(kDecodeMaxGroup <= 32, "one 32-column MFMA block of heads per unit");
 
-template <int D>
+template <int D, bool PAGED>
 __global__ void __launch_bounds__(DEC_THREADS)
 decode_group_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ Kc,
                     const __bf16* __restrict__ Vc, float* __restrict__ Opart,
                     float* __restrict__ LSEpart, int G, int L, int S, int chunk, int units,
-                    float c /* scale * log2(e) */) {
+                    float c /* scale * log2(e) */, Paging pg) {
     constexpr int ROWB = 2 * D;             // bytes per cached row
     constexpr int CPR = D / 8;              // 16-byte chunks per row
     constexpr int TILEB = DG_BC * ROWB;     // one K (or V) tile of one wave
@@ -204,9 +231,16 @@ decode_group_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ Kc,
     if (unit >= units) return;              // no barrier below: waves are independent
     const int s = unit % S;
     const int gkv = unit / S;               // b * Hkv + cache head
-    const int k_begin = s * chunk;
-    const int k_end = min(L, k_begin + chunk);
-    const int ntile = (k_end - k_begin + DG_BC - 1) / DG_BC;
+    int Lb = L;                             // this sequence's cache length
+    int b = 0, hk = 0;
+    if constexpr (PAGED) {
+        b = gkv / pg.Hkv;
+        hk = gkv % pg.Hkv;
+        Lb = min(max(pg.seq_lens[b], 0), L);
+    }
+    const int k_begin = s * chunk;          // chunk is a multiple of 32, so a paged
+    const int k_end = min(Lb, k_begin + chunk);   // tile never straddles two pages
+    const int ntile = k_end > k_begin ? (k_end - k_begin + DG_BC - 1) / DG_BC : 0;
 
     // q^T of the group as the B operand: column l32 is query head gkv*G + l32
     bf16x8 qf[D / 16];
@@ -218,19 +252,36 @@ decode_group_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ Kc,
         qf[ks] = as_bf16x8(u);
     }
 
-    // one cache head (L * ROWB bytes < 2^32, checked by the host)
+    // Contiguous: one resource over the cache head (L * ROWB bytes < 2^32,
+    // checked by the host).  Paged: one resource per tile over its 32 rows of
+    // a page, empty when the page index lies outside the pool (its loads then
+    // read zeros and its keys are masked).
     const size_t hoff = (size_t)gkv * (size_t)L * D;
-    const __amdgpu_buffer_rsrc_t k_rs = make_rsrc(Kc + hoff, (uint32_t)L * ROWB);
-    const __amdgpu_buffer_rsrc_t v_rs = make_rsrc(Vc + hoff, (uint32_t)L * ROWB);
-    // copy the 32 rows of tile t (rows past the cache end clamped to L-1; they
-    // are masked for K and weighted by 0 for V)
+    __amdgpu_buffer_rsrc_t k_rs = make_rsrc(Kc + hoff, (uint32_t)L * ROWB);
+    __amdgpu_buffer_rsrc_t v_rs = make_rsrc(Vc + hoff, (uint32_t)L * ROWB);
+    auto page_of = [&](int k0, bool& ok) __attribute__((always_inline)) -> size_t {
+        const int page = pg.block_table[(size_t)b * pg.max_pages + (k0 >> pg.ps_log2)];
+        ok = page >= 0 && page < pg.num_pages;
+        return ((((size_t)(ok ? page : 0) * pg.Hkv + hk) << pg.ps_log2) +
+                (size_t)(k0 & ((1 << pg.ps_log2) - 1))) * D;
+    };
+    // copy the 32 rows of tile t; rows past the live keys repeat the last live
+    // row (masked for K, weighted by 0 for V), so no unwritten cache row is read
     auto issue = [&](int t, char* kdst, char* vdst) __attribute__((always_inline)) {
         const int k0 = k_begin + t * DG_BC;
+        int rbase = k0;                      // row of the resource where the tile starts
+        if constexpr (PAGED) {
+            bool ok;
+            const size_t off = page_of(k0, ok);
+            k_rs = make_rsrc(Kc + off, ok ? (uint32_t)(DG_BC * ROWB) : 0u);
+            v_rs = make_rsrc(Vc + off, ok ? (uint32_t)(DG_BC * ROWB) : 0u);
+            rbase = 0;
+        }
 #pragma unroll
         for (int seg = 0; seg < SEGS; ++seg) {
             const int row = seg * RPS + lane / CPR;
             const int pc = lane % CPR;
-            const uint32_t grow = (uint32_t)min(k0 + row, L - 1) * ROWB;
+            const uint32_t grow = (uint32_t)(rbase + min(row, k_end - 1 - k0)) * ROWB;
             b2lds16(k_rs, grow + 16 * (pc ^ k_swz<D>(row)), kdst + seg * 1024);
             b2lds16(v_rs, grow + 16 * (pc ^ v_swz<D>(row)), vdst + seg * 1024);
         }
@@ -263,7 +314,13 @@ decode_group_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ Kc,
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks)
             st = mfma_bf16(*reinterpret_cast<const bf16x8*>(Ks + k_off[ks]), qf[ks], st);
-        const int lim = k_end - 1 - (k_begin + t * DG_BC) - 4 * g;   // last live key slot
+        int live_keys = k_end - (k_begin + t * DG_BC);
+        if constexpr (PAGED) {
+            bool ok;
+            (void)page_of(k_begin + t * DG_BC, ok);
+            if (!ok) live_keys = 0;
+        }
+        const int lim = live_keys - 1 - 4 * g;   // last live key slot of this lane
         float mx = -INFINITY;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -308,7 +365,7 @@ decode_group_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ Kc,
             }
     };
 
-    issue(0, kb0[w], vb0[w]);
+    if (ntile > 0) issue(0, kb0[w], vb0[w]);
     for (int t = 0; t < ntile; t += 2) {
         step(t, kb0[w], vb0[w], kb1[w], vb1[w]);
         if (t + 1 < ntile) step(t + 1, kb1[w], vb1[w], kb0[w], vb0[w]);
@@ -361,20 +418,20 @@ decode_merge_kernel(const float* __restrict__ Opart, const float* __restrict__ L
     if (LSE != nullptr && lane == 0) LSE[bh] = lse;
 }
 
-template <int D>
+template <int D, bool PAGED>
 hipError_t launch_d(const DecodeArgs& a) {
     const int BH = a.B * a.H;
     const int G = a.H / a.Hkv;
     hipStream_t st = (hipStream_t)a.stream;
     if (decode_group_path(a.H, a.Hkv)) {
         const int units = a.B * a.Hkv * a.splits;
-        hipLaunchKernelGGL((decode_group_kernel<D>), dim3((unsigned)((units + DEC_WAVES - 1) / DEC_WAVES)),
+        hipLaunchKernelGGL((decode_group_kernel<D, PAGED>), dim3((unsigned)((units + DEC_WAVES - 1) / DEC_WAVES)),
                            dim3(DEC_THREADS), 0, st, (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v,
-                           a.o_part, a.lse_part, G, a.L, a.splits, a.chunk, units, a.scale * kLog2e);
+                           a.o_part, a.lse_part, G, a.L, a.splits, a.chunk, units, a.scale * kLog2e, a.paging);
     } else {
-        hipLaunchKernelGGL((decode_split_kernel<D>), dim3((unsigned)(BH * a.splits)), dim3(DEC_THREADS), 0, st,
-                           (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, a.o_part, a.lse_part,
-                           G, a.L, a.splits, a.chunk, a.scale * kLog2e);
+        hipLaunchKernelGGL((decode_split_kernel<D, PAGED>), dim3((unsigned)(BH * a.splits)), dim3(DEC_THREADS), 0,
+                           st, (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, a.o_part, a.lse_part,
+                           G, a.L, a.splits, a.chunk, a.scale * kLog2e, a.paging);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -387,7 +444,8 @@ hipError_t launch_d(const DecodeArgs& a) {
 
 hipError_t launch_decode(const DecodeArgs& a) {
     if ((long long)a.B * a.H * a.splits > 0x7fffffffLL) return hipErrorInvalidValue;
-    return a.d == 64 ? launch_d<64>(a) : launch_d<128>(a);
+    if (a.paging.block_table != nullptr) return a.d == 64 ? launch_d<64, true>(a) : launch_d<128, true>(a);
+    return a.d == 64 ? launch_d<64, false>(a) : launch_d<128, false>(a);
 }
 
 }  // namespace fa

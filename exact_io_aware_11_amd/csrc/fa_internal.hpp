@@ -39,6 +39,17 @@ struct BwdArgs {
     void* stream;
 };
 
+// Paged KV cache: pool [num_pages, Hkv, page_size, d]; sequence b owns pages
+// block_table[b * max_pages + 0 ..] in token order and has seq_lens[b] tokens.
+struct Paging {
+    const int* block_table;   // null: contiguous cache
+    const int* seq_lens;
+    int num_pages;
+    int max_pages;
+    int ps_log2;              // page_size = 1 << ps_log2 (>= 32)
+    int Hkv;
+};
+
 struct DecodeArgs {
     const void* q;
     const void* k;
@@ -48,10 +59,12 @@ struct DecodeArgs {
     float* o_part;   // workspace: [B,H,S,d] fp32
     float* lse_part; // workspace: [B,H,S] fp32
     int B, H, Hkv, L, d;
-    int splits;      // S >= 1, every split non-empty
-    int chunk;       // keys per split
+    int splits;      // S >= 1; contiguous: every split non-empty
+    int chunk;       // keys per split, a multiple of 32
     float scale;
     void* stream;
+    Paging paging;   // block_table == nullptr for a contiguous cache (L = its length);
+                     // paged: L = max_pages * page_size
 };
 
 // Decode takes the grouped-query kernel (each cache head read once for all

@@ -161,6 +161,45 @@ fa_status_t fa_decode(const void* q, const void* k_cache, const void* v_cache,
                       int B, int H, int Hkv, int L, int d, fa_dtype_t dtype,
                       int num_splits, float scale, void* stream);
 
+/*
+ * fa_decode_paged -- fa_decode against a paged KV cache.  The attention-backend
+ * page (sections "Wat is het precies?" and "Voorbeelden uit de praktijk")
+ * describes PagedAttention: the cache is cut into small blocks allocated from a
+ * pool rather than one contiguous reservation, with the same result.  Here a
+ * page holds page_size consecutive tokens of every K/V head, and sequence b
+ * lists its pages in token order in row b of a block table.  The result is
+ * fa_decode over the first seq_lens[b] tokens of that page sequence; a length
+ * of 0 gives O = 0 and LSE = -inf.
+ *
+ *   q                 [B,H,1,d] bf16.
+ *   k_pool, v_pool    [num_pages, Hkv, page_size, d] bf16 (page p of head h is
+ *                     the contiguous block k_pool[p][h]).
+ *   block_table       [B, max_pages_per_seq] int32, device memory: page indices
+ *                     in [0, num_pages).  Entries past a sequence's last page
+ *                     are not read.  Keys on a page index outside the pool are
+ *                     skipped (treated as absent) rather than read.
+ *   seq_lens          [B] int32, device memory; values are clamped to
+ *                     [0, max_pages_per_seq * page_size].
+ *   o, lse            as for fa_decode (lse may be NULL).
+ *   workspace         at least fa_decode_workspace_bytes(B, H, Hkv,
+ *                     max_pages_per_seq * page_size, d, num_splits).
+ *   page_size         a power of two, 32 .. 65536.
+ *   num_splits        0 = library's choice for that maximal length, else
+ *                     1 .. max_pages_per_seq * page_size.
+ *
+ * Errors: FA_ERR_NULL for a missing pointer (lse excepted); FA_ERR_ARG for
+ * sizes < 1, a page size that is not a power of two in range, Hkv not
+ * dividing H, a bad scale or split count; FA_ERR_ALIGN for q, pools, o, lse or
+ * workspace not 16-byte aligned or the int32 arrays not 4-byte aligned.
+ */
+fa_status_t fa_decode_paged(const void* q, const void* k_pool, const void* v_pool,
+                            const int32_t* block_table, const int32_t* seq_lens,
+                            void* o, float* lse,
+                            void* workspace, size_t workspace_bytes,
+                            int B, int H, int Hkv, int num_pages, int page_size,
+                            int max_pages_per_seq, int d, fa_dtype_t dtype,
+                            int num_splits, float scale, void* stream);
+
 /* fa_status_string -- a static, human-readable name for a status code. */
 const char* fa_status_string(fa_status_t s);
 

@@ -18,7 +18,7 @@ import pytest
 import torch
 
 import fa_workloads as W
-from oracle import ref_bwd, ref_decode, ref_fwd, ref_fwd_rows
+from oracle import ref_bwd, ref_decode, ref_decode_paged, ref_fwd, ref_fwd_rows
 from parity_util import (assert_bf16_close, assert_fp32_close, assert_grad_close, to64)
 
 pytestmark = pytest.mark.gpu
@@ -414,3 +414,109 @@ def test_decode_gqa_b64h32kv8l8192d128_sampled_batches():
         o_ref, lse_ref = ref_decode(to64(q[b:b + 1]), to64(kc[b:b + 1]), to64(vc[b:b + 1]), scale)
         assert_bf16_close(to64(o[b:b + 1]), o_ref, f"O batch {b}")
         assert_bf16_close(to64(lse[b:b + 1]), lse_ref, f"LSE batch {b}")
+
+
+
+# ----------------------------------------------------------------------------
+# paged KV cache: pool [P, Hkv, page_size, d], block table, ragged lengths
+# ----------------------------------------------------------------------------
+
+def _paged_inputs(B, H, Hkv, ps, lens, d, seed, extra_pages=5):
+    """Seeded q and a page pool whose every row that no sequence owns is NaN,
+    so any read of an unowned row would show up in the output."""
+    g = torch.Generator().manual_seed(seed)
+    n_pg = [-(-n // ps) for n in lens]
+    total = sum(n_pg) + extra_pages
+    max_pages = max(max(n_pg), 1) + 1
+    slots = torch.randperm(total, generator=g).tolist()
+    q = torch.randn((B, H, 1, d), generator=g).to(torch.bfloat16)
+    kp = torch.full((total, Hkv, ps, d), float("nan"), dtype=torch.bfloat16)
+    vp = torch.full((total, Hkv, ps, d), float("nan"), dtype=torch.bfloat16)
+    table = torch.full((B, max_pages), 1 << 30, dtype=torch.int32)   # unused entries: out of range
+    i = 0
+    for b in range(B):
+        for j in range(n_pg[b]):
+            rows = min(ps, lens[b] - j * ps)
+            kp[slots[i], :, :rows] = torch.randn((Hkv, rows, d), generator=g).to(torch.bfloat16)
+            vp[slots[i], :, :rows] = torch.randn((Hkv, rows, d), generator=g).to(torch.bfloat16)
+            table[b, j] = slots[i]
+            i += 1
+    return q, kp, vp, table, torch.tensor(lens, dtype=torch.int32)
+
+
+PAGED = [
+    # (B, H, Hkv, page_size, lens, d): grouped kernel for 2 <= H/Hkv <= 32,
+    # per-head kernel otherwise
+    (3, 8, 2, 32, [1000, 1, 33], 128),
+    (2, 8, 8, 64, [700, 64], 128),
+    (4, 32, 8, 256, [4097, 0, 31, 2048], 128),
+    (2, 4, 1, 128, [300, 129], 64),
+    (2, 64, 1, 32, [100, 45], 64),
+    (1, 6, 3, 1024, [3000], 128),
+]
+
+
+@pytest.mark.parametrize("B,H,Hkv,ps,lens,d", PAGED)
+def test_decode_paged(B, H, Hkv, ps, lens, d):
+    fa = _fa()
+    q, kp, vp, table, sl = _paged_inputs(B, H, Hkv, ps, lens, d, seed=5000 + ps + H + sum(lens))
+    scale = 1.0 / math.sqrt(d)
+    o_ref, lse_ref = ref_decode_paged(to64(q), to64(kp), to64(vp), table.numpy(), sl.numpy(), scale)
+    qd, kpd, vpd, td, sld = (x.to(DEV) for x in (q, kp, vp, table, sl))
+    for s in (0, 1, 3):
+        say(f"fa_decode_paged B{B} H{H} Hkv{Hkv} ps{ps} lens{lens} d{d} splits={s}")
+        o, lse = fa.decode_paged(qd, kpd, vpd, td, sld, scale=scale, num_splits=s)
+        torch.cuda.synchronize()
+        assert torch.isfinite(o.float()).all(), "an unowned (NaN) cache row reached the output"
+        assert_bf16_close(to64(o), o_ref, f"O splits={s}")
+        assert_bf16_close(to64(lse), lse_ref, f"LSE splits={s}")
+
+
+def test_decode_paged_matches_contiguous():
+    # the same cache once contiguous and once scattered over a shuffled pool
+    fa = _fa()
+    B, H, Hkv, L, d, ps = 4, 16, 4, 1500, 128, 64
+    q, kc, vc = W.make_gqa(B, H, Hkv, 1, d, "bf16", seed=5100, device="cpu", Nk=L)
+    n_pg = -(-L // ps)
+    g = torch.Generator().manual_seed(5101)
+    slots = torch.randperm(B * n_pg, generator=g)
+    kp = torch.zeros((B * n_pg, Hkv, ps, d), dtype=torch.bfloat16)
+    vp = torch.zeros_like(kp)
+    table = torch.empty((B, n_pg), dtype=torch.int32)
+    for b in range(B):
+        for j in range(n_pg):
+            rows = min(ps, L - j * ps)
+            kp[slots[b * n_pg + j], :, :rows] = kc[b, :, j * ps:j * ps + rows]
+            vp[slots[b * n_pg + j], :, :rows] = vc[b, :, j * ps:j * ps + rows]
+            table[b, j] = slots[b * n_pg + j]
+    sl = torch.full((B,), L, dtype=torch.int32)
+    say("fa_decode_paged vs fa_decode")
+    o1, l1 = fa.decode(q.to(DEV), kc.to(DEV), vc.to(DEV))
+    o2, l2 = fa.decode_paged(q.to(DEV), kp.to(DEV), vp.to(DEV), table.to(DEV), sl.to(DEV))
+    torch.cuda.synchronize()
+    o_ref, lse_ref = ref_decode(to64(q), to64(kc), to64(vc), 1 / math.sqrt(d))
+    assert_bf16_close(to64(o2), o_ref, "O paged")
+    assert_bf16_close(to64(l2), lse_ref, "LSE paged")
+    # same split plan and key order inside each chunk: the two layouts agree closely
+    assert (l1 - l2).abs().max().item() <= 1e-3
+    assert (o1.float() - o2.float()).abs().max().item() <= 2e-2
+
+
+def test_decode_paged_skips_pages_outside_the_pool():
+    # a page index outside [0, num_pages) is skipped: the result is the decode
+    # over the remaining tokens
+    fa = _fa()
+    B, H, Hkv, ps, d = 1, 8, 2, 32, 128
+    lens = [32 * 5]
+    q, kp, vp, table, sl = _paged_inputs(B, H, Hkv, ps, lens, d, seed=5200)
+    keep = [0, 1, 3, 4]
+    table_bad = table.clone()
+    table_bad[0, 2] = kp.shape[0] + 7
+    say("fa_decode_paged with an out-of-pool page")
+    o, lse = fa.decode_paged(q.to(DEV), kp.to(DEV), vp.to(DEV), table_bad.to(DEV), sl.to(DEV))
+    torch.cuda.synchronize()
+    kk = torch.cat([kp[int(table[0, j])] for j in keep], dim=1)[None]
+    vv = torch.cat([vp[int(table[0, j])] for j in keep], dim=1)[None]
+    o_ref, lse_ref = ref_decode(to64(q), to64(kk), to64(vv), 1 / math.sqrt(d))
+    assert_bf16_close(to64(o), o_ref, "O")
+    assert_bf16_close(to64(lse), lse_ref, "LSE")
