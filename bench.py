@@ -15,7 +15,8 @@ backward TFLOP/s as the metric's range asks, and the oracle's CPU time on a
 bounded sample is reported as ``cpu_baseline``.
 
 A grouped-query block (decode with 8 cache heads for 32 query heads, and
-fwd/bwd with groups of 4) is measured after the sweep and reported as ``gqa``.
+fwd/bwd with groups of 4) and paged-cache decodes are measured after the
+sweep and reported under ``gqa``.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-sweep]
                        [--no-gqa] [--no-cpu-baseline]
@@ -51,7 +52,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-gqa", action="store_true", help="skip the grouped-query measurements")
+    ap.add_argument("--no-gqa", action="store_true", help="skip the grouped-query and paged measurements")
     ap.add_argument("--reduce-counters", nargs="+", metavar="DIR",
                     help="host only: summarise rocprofv3 --pmc output of this script and exit")
     ap.add_argument("--write-traffic", action="store_true",
@@ -225,6 +226,55 @@ def gqa_measure(torch, fa, W, dev, iters=20):
         out[name] = {"workload": f"B{B} H{H} Hkv{Hkv} N{N} d{d} causal", "ms": round(ms, 4),
                      "tflops": round(tf, 1), "bound": "mfma", "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
         log(f"gqa {name} {out[name]['workload']}: {ms:.4f} ms, {tf:.1f} TFLOP/s")
+    return out
+
+
+def paged_measure(torch, fa, dev, iters=20):
+    """Decode against a paged cache: B64 H32 L8192 d128, 64-token pages of one
+    pool in shuffled order, every sequence full length; multi-head (32 cache
+    heads, per-head kernel) and grouped (8 cache heads, grouped kernel).
+    Algorithmic bytes: the K and V rows read, 2*B*Hkv*L*d*2."""
+    stream = torch.cuda.current_stream().cuda_stream
+    B, H, L, d, ps = 64, 32, 8192, 128, 64
+    scale = 1.0 / math.sqrt(d)
+    g = torch.Generator(device=dev)
+    g.manual_seed(30)
+    out = {}
+    for name, Hkv in (("mha", 32), ("gqa", 8)):
+        pages = B * (L // ps)
+        q = torch.randn((B, H, 1, d), generator=g, device=dev).to(torch.bfloat16)
+        kp = torch.randn((pages, Hkv, ps, d), generator=g, device=dev).to(torch.bfloat16)
+        vp = torch.randn((pages, Hkv, ps, d), generator=g, device=dev).to(torch.bfloat16)
+        table = torch.randperm(pages, generator=g, device=dev).to(torch.int32).reshape(B, L // ps)
+        lens = torch.full((B,), L, dtype=torch.int32, device=dev)
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+        nb = fa.fa_decode_workspace_bytes(B, H, Hkv, L, d, 0)
+        ws = torch.empty((nb,), dtype=torch.uint8, device=dev)
+
+        def fn():
+            st = fa.fa_decode_paged(q.data_ptr(), kp.data_ptr(), vp.data_ptr(), table.data_ptr(), lens.data_ptr(),
+                                    o.data_ptr(), lse.data_ptr(), ws.data_ptr(), nb, B, H, Hkv, pages, ps,
+                                    L // ps, d, fa.FA_BF16, 0, scale, stream)
+            if st != fa.FA_OK:
+                raise RuntimeError(fa.fa_status_string(st))
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(iters):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / iters
+        byt = 2.0 * B * Hkv * L * d * 2
+        gbs = byt / (ms * 1e-3) / 1e9
+        out[name] = {"workload": f"B{B} H{H} Hkv{Hkv} L{L} d{d} page{ps}", "ms": round(ms, 4),
+                     "GBps": round(gbs, 1), "bound": "hbm", "frac": round(gbs / PEAK_HBM_GBPS, 4),
+                     "algorithmic_bytes": byt}
+        log(f"paged decode {out[name]['workload']}: {ms:.4f} ms, {gbs:.1f} GB/s")
+        del q, kp, vp, table, lens, o, lse, ws
+        torch.cuda.empty_cache()
     return out
 
 
@@ -510,6 +560,8 @@ def main():
     if not args.no_gqa:
         log("grouped-query attention")
         gqa_res = gqa_measure(torch, fa, W, dev)
+        log("paged KV cache")
+        gqa_res["paged_decode"] = paged_measure(torch, fa, dev)
 
     cpu = None
     if not args.no_cpu_baseline:
