@@ -17,6 +17,8 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 bool dims_ok(int B, int H, int N) { return B >= 1 && H >= 1 && N >= 1; }
 
 bool head_dim_ok(int d) { return d == 64 || d == 128; }
+// bf16 forward and decode also run at d = 256 (fp32 forward and the backward do not)
+bool head_dim_ok_bf16(int d) { return head_dim_ok(d) || d == 256; }
 
 bool scale_ok(float s) { return std::isfinite(s) && s > 0.f; }
 
@@ -102,8 +104,8 @@ fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, fa_dtyp
                    void* stream) {
     if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
     if (!dims_ok(B, H, N) || !kv_ok(H, Hkv) || !scale_ok(scale) || !total_ok(B, H, N, d)) return FA_ERR_ARG;
-    if (!head_dim_ok(d)) return FA_ERR_UNSUPPORTED;
     if (in_dtype != FA_BF16 && in_dtype != FA_FP32) return FA_ERR_UNSUPPORTED;
+    if (in_dtype == FA_BF16 ? !head_dim_ok_bf16(d) : !head_dim_ok(d)) return FA_ERR_UNSUPPORTED;
     if (o_dtype != FA_BF16 && o_dtype != FA_FP32) return FA_ERR_UNSUPPORTED;
     if (in_dtype == FA_FP32 && o_dtype != FA_FP32) return FA_ERR_UNSUPPORTED;
     if (in_dtype == FA_BF16 && !head_fits_u32(N, d)) return FA_ERR_UNSUPPORTED;
@@ -163,7 +165,7 @@ fa_status_t fa_decode(const void* q, const void* k_cache, const void* v_cache, v
     if (!dims_ok(B, H, L) || !kv_ok(H, Hkv) || !scale_ok(scale) || num_splits < 0 || num_splits > L ||
         !total_ok(B, H, L, d))
         return FA_ERR_ARG;
-    if (!head_dim_ok(d) || dtype != FA_BF16 || !head_fits_u32(L, d)) return FA_ERR_UNSUPPORTED;
+    if (!head_dim_ok_bf16(d) || dtype != FA_BF16 || !head_fits_u32(L, d)) return FA_ERR_UNSUPPORTED;
     if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o)) return FA_ERR_ALIGN;
     if (lse && !aligned16(lse)) return FA_ERR_ALIGN;
     const size_t need = fa_decode_workspace_bytes(B, H, Hkv, L, d, num_splits);
@@ -191,7 +193,7 @@ fa_status_t fa_decode_paged(const void* q, const void* k_pool, const void* v_poo
     if (!pow2(page_size) || page_size < 32 || page_size > (1 << 16) || Lmax > 0x7fffffffLL ||
         num_splits > Lmax || !total_ok(B, H, (int)Lmax, d) || (long long)B * max_pages_per_seq > 0x7fffffffLL)
         return FA_ERR_ARG;
-    if (!head_dim_ok(d) || dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+    if (!head_dim_ok_bf16(d) || dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
     if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(o)) return FA_ERR_ALIGN;
     if ((reinterpret_cast<uintptr_t>(block_table) & 3) || (reinterpret_cast<uintptr_t>(seq_lens) & 3))
         return FA_ERR_ALIGN;

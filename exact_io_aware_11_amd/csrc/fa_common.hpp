@@ -149,7 +149,10 @@ __device__ __forceinline__ int perm16(int k) {
     return (k & ~15) | (pq << 2) | (k & 3);
 }
 
-// Full-wave butterfly over lanes l and l ^ 32 (ds_bpermute).
+// Max / sum of x over lanes l and l ^ 32, in every lane: v_permlane32_swap of
+// x with itself gives (x of lanes 0-31 twice, x of lanes 32-63 twice); the
+// max or sum of its two results is the xor-32 reduction (checked with an
+// in-bounds probe of the builtin).
 __device__ __forceinline__ float xor32_max(float x) {
     auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
@@ -176,13 +179,15 @@ __device__ __forceinline__ float dpp_sum16(float v) {
 // padding), applied when the tile is copied in and when it is read.
 //  k_swz: rows read one 16-byte chunk per lane by 32 consecutive rows.
 //  v_swz: rows read with the transposing 8-byte read (4 rows x 32 bytes per
-//         16-lane group).
+//         16-lane group).  D = 64, 128 or 256.
 //  rt_swz: both patterns on the same tile (4*(row%4) + (row/4)%4).
 template <int D>
 __device__ __forceinline__ int k_swz(int row) { return row & (D / 8 - 1); }
 template <int D>
 __device__ __forceinline__ int v_swz(int row) {
-    return D == 128 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2);
+    // rows of 256 or 512 bytes start in the same bank: shift rows r..r+3 of a
+    // 4-row group by 64 bytes each; 128-byte rows pair up, shift by 64 bytes
+    return D >= 128 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2);
 }
 template <int D>
 __device__ __forceinline__ int rt_swz(int row) {

@@ -132,7 +132,12 @@ decode_split_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ Kc,
                 dot = fmaf(bf16_lo(p[j]), qv[2 * j], dot);
                 dot = fmaf(bf16_hi(p[j]), qv[2 * j + 1], dot);
             }
-            dot = (LPK == 16) ? dpp_sum16(dot) : dpp_sum8(dot);
+            if constexpr (LPK == 8) {
+                dot = dpp_sum8(dot);
+            } else {
+                dot = dpp_sum16(dot);
+                if constexpr (LPK == 32) dot += __shfl_xor(dot, 16);   // d = 256: two rows per key
+            }
             x[u] = live[u] ? dot : -INFINITY;
             mx = fmaxf(mx, x[u]);
         }
@@ -205,8 +210,12 @@ decode_split_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ Kc,
 constexpr int DG_BC = 32;          // keys per tile
 static_assert(kDecodeMaxGroup <= 32, "one 32-column MFMA block of heads per unit");
 
+// waves (units) per workgroup: the d = 256 tiles are twice as large
+template <int D>
+constexpr int dg_waves() { return D == 256 ? 2 : 4; }
+
 template <int D, bool PAGED>
-__global__ void __launch_bounds__(DEC_THREADS)
+__global__ void __launch_bounds__(64 * dg_waves<D>())
 decode_group_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ Kc,
                     const __bf16* __restrict__ Vc, float* __restrict__ Opart,
                     float* __restrict__ LSEpart, int G, int L, int S, int chunk, int units,
@@ -220,14 +229,14 @@ decode_group_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ Kc,
 
     // per-wave tile buffers; four separate LDS objects so that the copies into
     // one buffer pair do not make the reads of the other wait
-    __shared__ __attribute__((aligned(1024))) char kb0[DEC_WAVES][TILEB];
-    __shared__ __attribute__((aligned(1024))) char kb1[DEC_WAVES][TILEB];
-    __shared__ __attribute__((aligned(1024))) char vb0[DEC_WAVES][TILEB];
-    __shared__ __attribute__((aligned(1024))) char vb1[DEC_WAVES][TILEB];
+    __shared__ __attribute__((aligned(1024))) char kb0[dg_waves<D>()][TILEB];
+    __shared__ __attribute__((aligned(1024))) char kb1[dg_waves<D>()][TILEB];
+    __shared__ __attribute__((aligned(1024))) char vb0[dg_waves<D>()][TILEB];
+    __shared__ __attribute__((aligned(1024))) char vb1[dg_waves<D>()][TILEB];
 
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int l32 = lane & 31, g = lane >> 5;
-    const int unit = blockIdx.x * DEC_WAVES + w;
+    const int unit = blockIdx.x * dg_waves<D>() + w;
     if (unit >= units) return;              // no barrier below: waves are independent
     const int s = unit % S;
     const int gkv = unit / S;               // b * Hkv + cache head
@@ -425,8 +434,9 @@ hipError_t launch_d(const DecodeArgs& a) {
     hipStream_t st = (hipStream_t)a.stream;
     if (decode_group_path(a.H, a.Hkv)) {
         const int units = a.B * a.Hkv * a.splits;
-        hipLaunchKernelGGL((decode_group_kernel<D, PAGED>), dim3((unsigned)((units + DEC_WAVES - 1) / DEC_WAVES)),
-                           dim3(DEC_THREADS), 0, st, (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v,
+        constexpr int WV = dg_waves<D>();
+        hipLaunchKernelGGL((decode_group_kernel<D, PAGED>), dim3((unsigned)((units + WV - 1) / WV)),
+                           dim3(64 * WV), 0, st, (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v,
                            a.o_part, a.lse_part, G, a.L, a.splits, a.chunk, units, a.scale * kLog2e, a.paging);
     } else {
         hipLaunchKernelGGL((decode_split_kernel<D, PAGED>), dim3((unsigned)(BH * a.splits)), dim3(DEC_THREADS), 0,
@@ -444,7 +454,11 @@ hipError_t launch_d(const DecodeArgs& a) {
 
 hipError_t launch_decode(const DecodeArgs& a) {
     if ((long long)a.B * a.H * a.splits > 0x7fffffffLL) return hipErrorInvalidValue;
-    if (a.paging.block_table != nullptr) return a.d == 64 ? launch_d<64, true>(a) : launch_d<128, true>(a);
+    if (a.paging.block_table != nullptr) {
+        if (a.d == 256) return launch_d<256, true>(a);
+        return a.d == 64 ? launch_d<64, true>(a) : launch_d<128, true>(a);
+    }
+    if (a.d == 256) return launch_d<256, false>(a);
     return a.d == 64 ? launch_d<64, false>(a) : launch_d<128, false>(a);
 }
 

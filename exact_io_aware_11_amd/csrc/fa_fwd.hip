@@ -66,7 +66,7 @@ __device__ __forceinline__ void fwd_tile_of(int bid, int BH, int G, int nqt, boo
 // (k_swz for K, read one chunk per lane by 32 consecutive rows; v_swz for V,
 // read with the transposing 8-byte read).
 template <int D, bool CAUSAL, bool OUT_BF16>
-__global__ void __launch_bounds__(FWD_THREADS) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ void __launch_bounds__(FWD_THREADS) __attribute__((amdgpu_waves_per_eu(D == 256 ? 1 : 2)))
 fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                 const __bf16* __restrict__ V, void* __restrict__ O, float* __restrict__ LSE,
                 int BH, int G, int N, int nqt, float c /* scale * log2(e) */) {
@@ -456,7 +456,9 @@ hipError_t launch_f32(const FwdArgs& a) {
 
 template <int D>
 hipError_t dispatch_d(const FwdArgs& a) {
-    if (!a.in_bf16) return a.causal ? launch_f32<D, true>(a) : launch_f32<D, false>(a);
+    if constexpr (D != 256) {   // fp32 inputs: d = 64 and 128 only (the host rejects d = 256)
+        if (!a.in_bf16) return a.causal ? launch_f32<D, true>(a) : launch_f32<D, false>(a);
+    }
     if (a.out_bf16) return a.causal ? launch_bf16<D, true, true>(a) : launch_bf16<D, false, true>(a);
     return a.causal ? launch_bf16<D, true, false>(a) : launch_bf16<D, false, false>(a);
 }
@@ -465,6 +467,7 @@ hipError_t dispatch_d(const FwdArgs& a) {
 
 hipError_t launch_fwd(const FwdArgs& a) {
     if ((long long)((a.N + FWD_BR - 1) / FWD_BR) * a.B * a.H > 0x7fffffffLL) return hipErrorInvalidValue;
+    if (a.d == 256) return dispatch_d<256>(a);
     return a.d == 64 ? dispatch_d<64>(a) : dispatch_d<128>(a);
 }
 

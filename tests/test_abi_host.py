@@ -88,7 +88,8 @@ def fwd(**kw):
     (dict(Hkv=0), fa.FA_ERR_ARG),
     (dict(Hkv=8), fa.FA_ERR_ARG),        # more K/V heads than query heads
     (dict(d=96), fa.FA_ERR_UNSUPPORTED),
-    (dict(d=256), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=512), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=256, in_dtype=fa.FA_FP32, o_dtype=fa.FA_FP32), fa.FA_ERR_UNSUPPORTED),   # d = 256: bf16 only
     (dict(in_dtype=7), fa.FA_ERR_UNSUPPORTED),
     (dict(o_dtype=5), fa.FA_ERR_UNSUPPORTED),
     (dict(in_dtype=fa.FA_FP32, o_dtype=fa.FA_BF16), fa.FA_ERR_UNSUPPORTED),
@@ -122,6 +123,7 @@ def bwd(ws_bytes=None, **kw):
     (dict(scale=float("nan")), fa.FA_ERR_ARG),
     (dict(in_dtype=fa.FA_FP32), fa.FA_ERR_UNSUPPORTED),
     (dict(d=32), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=256), fa.FA_ERR_UNSUPPORTED),    # no backward at d = 256
     (dict(o_dtype=3), fa.FA_ERR_UNSUPPORTED),
     (dict(N=1 << 24, d=128), fa.FA_ERR_UNSUPPORTED),
     (dict(dk=MIS), fa.FA_ERR_ALIGN),
@@ -166,6 +168,7 @@ def dec(ws_bytes=None, **kw):
     (dict(scale=-1.0), fa.FA_ERR_ARG),
     (dict(dtype=fa.FA_FP32), fa.FA_ERR_UNSUPPORTED),
     (dict(d=80), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=512), fa.FA_ERR_UNSUPPORTED),
     (dict(v=MIS), fa.FA_ERR_ALIGN),
     (dict(lse=MIS), fa.FA_ERR_ALIGN),
     (dict(ws=0), fa.FA_ERR_WORKSPACE),

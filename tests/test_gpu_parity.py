@@ -101,6 +101,11 @@ SMALL = [
     (1, 2, 33, 128, "fp32", True),
     (2, 1, 129, 64, "fp32", True),
     (1, 1, 300, 128, "fp32", False),
+    # head dim 256 (bf16 only)
+    (1, 2, 300, 256, "bf16", True),
+    (2, 1, 129, 256, "bf16", False),
+    (1, 2, 1000, 256, "bf16", True),
+    (1, 1, 1, 256, "bf16", True),
 ]
 
 
@@ -315,6 +320,7 @@ GQA_FWD = [
     (2, 16, 8, 129, 64, "bf16", True),
     (1, 4, 2, 200, 64, "fp32", True),
     (1, 6, 2, 97, 128, "fp32", False),
+    (1, 8, 2, 257, 256, "bf16", True),
 ]
 
 
@@ -381,6 +387,8 @@ GQA_DEC = [
     (1, 32, 1, 2049, 128),
     (1, 64, 1, 500, 64),
     (2, 12, 4, 33, 64),
+    (2, 8, 2, 777, 256),
+    (2, 4, 4, 300, 256),
 ]
 
 
@@ -453,6 +461,8 @@ PAGED = [
     (2, 4, 1, 128, [300, 129], 64),
     (2, 64, 1, 32, [100, 45], 64),
     (1, 6, 3, 1024, [3000], 128),
+    (2, 8, 2, 64, [500, 33], 256),
+    (2, 4, 4, 32, [100, 1], 256),
 ]
 
 
@@ -518,5 +528,17 @@ def test_decode_paged_skips_pages_outside_the_pool():
     kk = torch.cat([kp[int(table[0, j])] for j in keep], dim=1)[None]
     vv = torch.cat([vp[int(table[0, j])] for j in keep], dim=1)[None]
     o_ref, lse_ref = ref_decode(to64(q), to64(kk), to64(vv), 1 / math.sqrt(d))
+    assert_bf16_close(to64(o), o_ref, "O")
+    assert_bf16_close(to64(lse), lse_ref, "LSE")
+
+
+
+def test_fwd_d256_fp32_output():
+    fa = _fa()
+    q, k, v = W.make_custom(2, 2, 333, 256, "bf16", seed=6000, device=DEV)
+    say("fa_fwd d256 causal, O in fp32")
+    o, lse = fa.attention(q, k, v, is_causal=True, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = ref_fwd(to64(q), to64(k), to64(v), True, 1 / 16.0)
     assert_bf16_close(to64(o), o_ref, "O")
     assert_bf16_close(to64(lse), lse_ref, "LSE")
