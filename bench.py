@@ -14,12 +14,12 @@ A sweep over N = 2K..16K (H=32, B=16384/N, causal) reports forward and
 backward TFLOP/s as the metric's range asks, and the oracle's CPU time on a
 bounded sample is reported as ``cpu_baseline``.
 
-A grouped-query block (decode with 8 cache heads for 32 query heads, and
-fwd/bwd with groups of 4) and paged-cache decodes are measured after the
-sweep and reported under ``gqa``.
+After the sweep, ``next_rows`` reports grouped-query attention (decode with
+8 cache heads for 32 query heads, fwd/bwd with groups of 4), paged-cache
+decodes and head dim 256 (forward and decode).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-sweep]
-                       [--no-gqa] [--no-cpu-baseline]
+                       [--no-next] [--no-cpu-baseline]
        python bench.py --reduce-counters DIR... [--write-traffic]   (host only)
 """
 
@@ -52,7 +52,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-gqa", action="store_true", help="skip the grouped-query and paged measurements")
+    ap.add_argument("--no-next", action="store_true",
+                    help="skip the grouped-query, paged-cache and head-dim-256 measurements")
     ap.add_argument("--reduce-counters", nargs="+", metavar="DIR",
                     help="host only: summarise rocprofv3 --pmc output of this script and exit")
     ap.add_argument("--write-traffic", action="store_true",
@@ -275,6 +276,52 @@ def paged_measure(torch, fa, dev, iters=20):
         log(f"paged decode {out[name]['workload']}: {ms:.4f} ms, {gbs:.1f} GB/s")
         del q, kp, vp, table, lens, o, lse, ws
         torch.cuda.empty_cache()
+    return out
+
+
+def d256_measure(torch, fa, W, dev, iters=10):
+    """Head dim 256: causal bf16 forward at B4 H16 N4096 and decode at
+    B64 H16 L4096 (multi-head) -- same flop formula / bytes as at d = 128."""
+    stream = torch.cuda.current_stream().cuda_stream
+    out = {}
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(iters):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / iters
+
+    B, H, N, d = 4, 16, 4096, 256
+    scale = 1.0 / math.sqrt(d)
+    q, k, v = W.make_custom(B, H, N, d, "bf16", seed=40, device=dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    ms = timed(lambda: fa.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), fa.FA_BF16,
+                                 lse.data_ptr(), B, H, H, N, d, fa.FA_BF16, 1, scale, stream))
+    tf = fwd_flops(B, H, N, d) / (ms * 1e-3) / 1e12
+    out["fwd"] = {"workload": f"B{B} H{H} N{N} d{d} causal", "ms": round(ms, 4), "tflops": round(tf, 1),
+                  "bound": "mfma", "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
+    log(f"d256 fwd {out['fwd']['workload']}: {ms:.4f} ms, {tf:.1f} TFLOP/s")
+    del q, k, v, o, lse
+
+    B, H, L = 64, 16, 4096
+    q, kc, vc = W.make_custom(B, H, 1, d, "bf16", seed=41, device=dev, Nk=L)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    nb = fa.fa_decode_workspace_bytes(B, H, H, L, d, 0)
+    ws = torch.empty((nb,), dtype=torch.uint8, device=dev)
+    ms = timed(lambda: fa.fa_decode(q.data_ptr(), kc.data_ptr(), vc.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                    ws.data_ptr(), nb, B, H, H, L, d, fa.FA_BF16, 0, scale, stream))
+    byt = 2.0 * B * H * L * d * 2
+    gbs = byt / (ms * 1e-3) / 1e9
+    out["decode"] = {"workload": f"B{B} H{H} L{L} d{d}", "ms": round(ms, 4), "GBps": round(gbs, 1),
+                     "bound": "hbm", "frac": round(gbs / PEAK_HBM_GBPS, 4), "algorithmic_bytes": byt}
+    log(f"d256 decode {out['decode']['workload']}: {ms:.4f} ms, {gbs:.1f} GB/s")
     return out
 
 
@@ -556,12 +603,14 @@ def main():
         log("sweep N=2K..16K")
         sweep_res = sweep(torch, fa, W, dev)
 
-    gqa_res = None
-    if not args.no_gqa:
+    next_rows = None
+    if not args.no_next:
         log("grouped-query attention")
-        gqa_res = gqa_measure(torch, fa, W, dev)
+        next_rows = {"gqa": gqa_measure(torch, fa, W, dev)}
         log("paged KV cache")
-        gqa_res["paged_decode"] = paged_measure(torch, fa, dev)
+        next_rows["paged_decode"] = paged_measure(torch, fa, dev)
+        log("head dim 256")
+        next_rows["head_dim_256"] = d256_measure(torch, fa, W, dev)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -592,7 +641,7 @@ def main():
                     | {"kernel": dominant["kernel"]},
         "rooflines": roofs,
         "sweep": sweep_res,
-        "gqa": gqa_res,
+        "next_rows": next_rows,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
