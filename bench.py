@@ -393,6 +393,25 @@ def _step_kernels():
     }
 
 
+def kernel_digest(src, csrc=None):
+    """SHA-256 of what a kernel is compiled from: its .hip file and the two
+    shared headers, with comments and whitespace removed (so a comment edit
+    keeps a traffic record valid, while any code change in the file or the
+    headers invalidates it)."""
+    import hashlib
+    import re
+    csrc = csrc or os.path.join(ROOT, "exact_io_aware_11_amd", "csrc")
+    h = hashlib.sha256()
+    for name in (src, "fa_common.hpp", "fa_internal.hpp"):
+        with open(os.path.join(csrc, name)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(name.encode())
+        h.update(" ".join(text.split()).encode())
+    return h.hexdigest()
+
+
 COPY_KERNEL = "copyBuffer"            # the 256 MiB device copy main() runs at set-up
 COPY_BYTES = 256 * 1024 * 1024
 
@@ -408,7 +427,6 @@ def reduce_counters(dirs, write_traffic):
     """
     import csv
     import glob
-    import hashlib
     from collections import defaultdict
 
     kern = _step_kernels()
@@ -462,7 +480,8 @@ def reduce_counters(dirs, write_traffic):
     wf = COPY_BYTES / 1024 / cm["WRITE_SIZE"]
     rec = {"_about": "HBM bytes per launch from rocprofv3 FETCH_SIZE and WRITE_SIZE (separate passes "
                      "over bench.py), each scaled by what the counter reads for bench.py's 256 MiB device "
-                     "copy; valid while the kernel source matches source_sha256",
+                     "copy; valid while source_digest matches the kernel's code (its .hip file and the "
+                     "shared headers, comments and whitespace removed)",
            "copy_calibration": {"bytes": COPY_BYTES, "fetch_kib": cm["FETCH_SIZE"], "write_kib": cm["WRITE_SIZE"],
                                 "fetch_factor": ff, "write_factor": wf}}
     print(f"\nCalibration: the {COPY_BYTES >> 20} MiB copy reads FETCH_SIZE {cm['FETCH_SIZE']:.0f} KiB and "
@@ -474,9 +493,7 @@ def reduce_counters(dirs, write_traffic):
         if not ("FETCH_SIZE" in m and "WRITE_SIZE" in m):
             continue
         hbm = m["FETCH_SIZE"] * 1024 * ff + m["WRITE_SIZE"] * 1024 * wf
-        with open(os.path.join(ROOT, "exact_io_aware_11_amd", "csrc", src), "rb") as fh:
-            sha = hashlib.sha256(fh.read()).hexdigest()
-        rec[key] = {"kernel": pat, "workload": wl, "source": src, "source_sha256": sha,
+        rec[key] = {"kernel": pat, "workload": wl, "source": src, "source_digest": kernel_digest(src),
                     "fetch_kib": m["FETCH_SIZE"], "write_kib": m["WRITE_SIZE"],
                     "bytes_per_launch": hbm, "algorithmic_bytes": alg, "algorithmic": what}
         ratio = f"{hbm / alg:.3f}" if alg else "—"
@@ -491,10 +508,9 @@ def reduce_counters(dirs, write_traffic):
 def traffic_record(kernel_key):
     """HBM bytes per launch measured with rocprofv3 counters (profiles/traffic.json).
 
-    Returns None when there is no record or when the kernel's source has
+    Returns None when there is no record or when the kernel's code has
     changed since the counters were taken.
     """
-    import hashlib
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         with open(path) as f:
@@ -504,12 +520,11 @@ def traffic_record(kernel_key):
     ent = rec.get(kernel_key)
     if not ent:
         return None
-    src = os.path.join(ROOT, "exact_io_aware_11_amd", "csrc", ent["source"])
     try:
-        h = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        d = kernel_digest(ent["source"])
     except OSError:
         return None
-    return round(ent["bytes_per_launch"]) if h == ent.get("source_sha256") else None
+    return round(ent["bytes_per_launch"]) if d == ent.get("source_digest") else None
 
 
 def main():

@@ -10,12 +10,14 @@
 //
 // Three launches on the caller's stream:
 //   1. bwd_prep:  D = rowsum(dO * O) in fp32.
-//   2. bwd_dkdv:  one workgroup per tile of BC = 128 keys of one head (4 waves,
-//                 32 keys each), walking the query tiles (BR = 64 rows) that can
-//                 see its keys.  K and V of the tile stay in registers; Q, dO,
-//                 LSE and D of the next query tile are copied global -> LDS
-//                 while the current one is computed.  dK^T and dV^T accumulate
-//                 in registers and are stored once.
+//   2. bwd_dkdv:  one workgroup per tile of BC = 128 keys of one K/V head (4
+//                 waves, 32 keys each), walking the query tiles (BR = 64 rows)
+//                 that can see its keys -- for each of the H/Hkv query heads
+//                 sharing that K/V head, so a shared head's gradient is summed
+//                 in registers.  K and V of the tile stay in registers; Q, dO,
+//                 LSE and D of the next query tile are copied global -> LDS by
+//                 buffer DMA while the current one is computed.  dK^T and dV^T
+//                 accumulate in registers and are stored once.
 //   3. bwd_dq:    one workgroup per tile of 128 query rows, streaming the K/V
 //                 tiles of its head like the forward pass: it recomputes S, P
 //                 and dP, forms dS and accumulates dQ^T = K^T dS^T in

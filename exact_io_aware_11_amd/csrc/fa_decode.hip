@@ -1,17 +1,24 @@
 // fa_decode.hip -- split-KV decode for gfx950: one query token per (batch,
-// head) against a contiguous [B,H,L,d] bf16 KV cache (the KV cache of the
-// attention-backend page).  The work is bound by HBM bandwidth: every cached
-// key and value is read exactly once and reused by nothing.
+// query head) against a bf16 KV cache of Hkv heads (the KV cache of the
+// attention-backend page), either contiguous [B,Hkv,L,d] or paged (a pool of
+// fixed-size pages and a block table per sequence, the PagedAttention layout
+// that page describes).  The work is bound by HBM bandwidth: every cached key
+// and value is read once per (b, cache head) on the grouped path, once per
+// query head otherwise.
 //
-// Phase 1 (split kernel): the cache of each (b, h) is cut into S contiguous
-// chunks, one workgroup per chunk.  Each wave streams 16-byte pieces of
-// consecutive keys (d/8 lanes per key, so one load instruction covers 1 KiB of
-// contiguous cache), keeps U loads of K and of V in flight per lane, reduces
-// the dot products with DPP inside each row of 16 lanes and runs the online
-// softmax (running max, running sum, rescaled accumulator: Slovak page,
-// section 2; Greek page, online-softmax section) in fp32.  The partial states
-// of the lanes and waves are merged with the same rule, and the chunk writes
-// its normalised output o_s and its log-sum-exp lse_s.
+// Phase 1, per-head kernel (decode_split_kernel; H = Hkv, or groups larger
+// than 32): the cache of each (b, h) is cut into S contiguous chunks, one
+// workgroup per chunk.  Each wave streams 16-byte pieces of consecutive keys
+// (d/8 lanes per key, so one load instruction covers 1 KiB of contiguous
+// cache), keeps U loads of K and of V in flight per lane, reduces the dot
+// products with DPP inside rows of 16 lanes and runs the online softmax
+// (running max, running sum, rescaled accumulator: Slovak page, section 2;
+// Greek page, online-softmax section) in fp32.  The partial states of the
+// lanes and waves are merged with the same rule, and the chunk writes its
+// normalised output o_s and its log-sum-exp lse_s.
+//
+// Phase 1, grouped kernel (decode_group_kernel; 2 <= H/Hkv <= 32): see its
+// own comment below.
 //
 // Phase 2 (merge kernel): M = max_s lse_s, lse = M + ln sum_s exp(lse_s - M),
 // O = sum_s exp(lse_s - lse) o_s, the online-softmax rescaling applied to

@@ -11,8 +11,9 @@
 // sequences fill the chip ("Flash Attention uitgelegd", FA2 section on
 // parallelism over the sequence length).
 //
-// bf16 path (d = 64 or 128): four waves, 32 query rows each, two
-// workgroups per CU.  Per key tile of BC = 64 keys a wave computes
+// bf16 path (d = 64, 128 or 256): four waves, 32 query rows each, two
+// workgroups per CU (one at d = 256, whose tiles and accumulators are twice
+// as large).  Per key tile of BC = 64 keys a wave computes
 // S^T = K Q^T (keys x queries) with v_mfma_f32_32x32x16_bf16: K comes from
 // LDS, Q^T stays in registers for the whole kernel.  In the C layout each lane
 // then holds one query row and 16 of the tile's keys, so row max and row sum
@@ -20,11 +21,14 @@
 // rounded to bf16, are already a valid B operand of O^T += V^T P^T; the V^T A
 // operand is read from the row-major V tile with the transposing LDS read.
 // O^T again gives each lane one query row.  K and V tiles are copied
-// global -> LDS without passing through registers, double-buffered.  The scale
-// is folded into the exp2 argument, the running max is only raised when it
-// grows by more than 2^8 (exact: the same reference max is used for the
-// numerator and the denominator), and O is normalised once at the end (the
-// FA2 point about minimising non-matmul work).
+// global -> LDS by buffer DMA without passing through registers,
+// double-buffered, and a fixed instruction schedule keeps LDS operand reads
+// ahead of the MFMAs.  The scale is folded into the exp2 argument, the
+// reference max is only raised when a tile's max exceeds it by more than 8 in
+// log2 units (exact: the same reference is used for the numerator and the
+// denominator), and O is normalised once at the end (the FA2 point about
+// minimising non-matmul work).  With grouped-query attention (Hkv < H K/V
+// heads) query head h reads K/V head h / (H / Hkv).
 //
 // fp32 path: same structure on v_mfma_f32_32x32x2_f32 with BC = 32; V needs no
 // transpose because each fp32 K-slot holds a single key.
