@@ -76,11 +76,11 @@ decode_split_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ Kc,
     const int k_begin = s * chunk;
     const int k_end = min(Lb, k_begin + chunk);   // may be <= k_begin: an empty chunk
 
-    // element offset of cached row `key` of this head; `ok` is false for a
-    // key on a page outside the pool (such keys are skipped)
-    auto row_of = [&](int key, bool& ok) __attribute__((always_inline)) -> size_t {
+    // element offset of cached row `key` of this head, given (paged) the
+    // block-table entry of its page; `ok` is false for a key on a page
+    // outside the pool (such keys are skipped)
+    auto row_of = [&](int key, int page, bool& ok) __attribute__((always_inline)) -> size_t {
         if constexpr (PAGED) {
-            const int page = pg.block_table[(size_t)b * pg.max_pages + (key >> pg.ps_log2)];
             ok = page >= 0 && page < pg.num_pages;
             const size_t prow = (((size_t)(ok ? page : 0) * pg.Hkv + hk) << pg.ps_log2) +
                                 (size_t)(key & ((1 << pg.ps_log2) - 1));
@@ -88,6 +88,16 @@ decode_split_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ Kc,
         } else {
             ok = true;
             return ((size_t)gkv * L + key) * D;
+        }
+    };
+    // block-table entries of this lane's keys of the iteration at `base`
+    // (fetched one iteration ahead, so the table lookup is off the path of
+    // the K/V loads that depend on it)
+    auto fetch_pages = [&](int base, int* pgs) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < DEC_UNROLL; ++u) {
+            const int key = base + u * (64 / (D / 8)) + slot;
+            pgs[u] = (key < k_end) ? pg.block_table[(size_t)b * pg.max_pages + (key >> pg.ps_log2)] : -1;
         }
     };
 
@@ -111,9 +121,14 @@ decode_split_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ Kc,
 #pragma unroll
     for (int j = 0; j < 8; ++j) o[j] = 0.f;
 
+    int pg_next[U] = {};
+    if constexpr (PAGED) fetch_pages(k_begin + w * STEP, pg_next);
     for (int base = k_begin + w * STEP; base < k_end; base += DEC_WAVES * STEP) {
         uint4 kr[U], vr[U];
         bool live[U];
+        int pg_cur[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) pg_cur[u] = pg_next[u];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int key = base + u * KPL + slot;
@@ -121,13 +136,14 @@ decode_split_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ Kc,
             vr[u] = kr[u];
             live[u] = false;
             if (key < k_end) {
-                const size_t r = row_of(key, live[u]);
+                const size_t r = row_of(key, pg_cur[u], live[u]);
                 if (live[u]) {
                     kr[u] = load_stream16(Kl + r);
                     vr[u] = load_stream16(Vl + r);
                 }
             }
         }
+        if constexpr (PAGED) fetch_pages(base + DEC_WAVES * STEP, pg_next);
         float x[U];
         float mx = -INFINITY;
 #pragma unroll
