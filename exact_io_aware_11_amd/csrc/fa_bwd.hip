@@ -151,28 +151,17 @@ bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, cons
     const __bf16* Kh = K + kvoff;
     const __bf16* Vh = V + kvoff;
 
-    // query head r of the group: its Q, dO (N * ROWB bytes < 2^32, checked by
-    // the host), LSE and D
-    auto head_rsrc = [&](int r, __amdgpu_buffer_rsrc_t& q_rs, __amdgpu_buffer_rsrc_t& do_rs,
-                         __amdgpu_buffer_rsrc_t& lse_rs, __amdgpu_buffer_rsrc_t& d_rs)
-        __attribute__((always_inline)) {
-        const size_t qh = (size_t)kvh * G + r;
-        q_rs = make_rsrc(Q + qh * N * D, (uint32_t)N * ROWB);
-        do_rs = make_rsrc(dO + qh * N * D, (uint32_t)N * ROWB);
-        lse_rs = make_rsrc(LSE + qh * N, (uint32_t)N * 4);
-        d_rs = make_rsrc(delta + qh * N, (uint32_t)N * 4);
-    };
-
-    // copy rows [r0, r0 + rows) of a [N, D] tensor into an LDS tile
-    // (segments seg0 .. seg0+nseg-1); rows past the end are clamped to N-1
-    auto issue = [&](__amdgpu_buffer_rsrc_t src, int r0, char* dst, int seg0, int nseg) __attribute__((always_inline)) {
+    // Copy rows [r0, r0 + BR) of one head's [N, D] tensor (below 2^32 bytes,
+    // checked by the host) into an LDS tile.  Each lane's byte offsets inside
+    // the tile depend only on the lane; the tile is addressed by a buffer resource that
+    // starts at row r0 and ends at the end of the head, so rows past the end
+    // read as zero (they are masked).
+    auto issue = [&](const __bf16* head, int r0, char* dst) __attribute__((always_inline)) {
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(head + (size_t)r0 * D, (uint32_t)(N - r0) * ROWB);
 #pragma unroll
-        for (int i = 0; i < nseg; ++i) {
-            const int seg = seg0 + i;
-            const int row = seg * RPS + lane / CPR;
-            const int pc = lane % CPR;
-            const uint32_t grow = (uint32_t)min(r0 + row, N - 1) * ROWB;
-            b2lds16(src, grow + 16 * (pc ^ rt_swz<D>(row)), dst + seg * 1024);
+        for (int i = 0; i < QSPW; ++i) {
+            const int row = (w * QSPW + i) * RPS + lane / CPR;
+            b2lds16(rs, (uint32_t)(row * ROWB + 16 * ((lane % CPR) ^ rt_swz<D>(row))), dst + (w * QSPW + i) * 1024);
         }
     };
 
@@ -228,21 +217,35 @@ bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, cons
     const int n_items = G * nq;
 
     // buffer layout: Q tile | dO tile | LSE[BR] | D[BR].  LSE (wave 0) and D
-    // (wave 1) are one row per lane; rows past the end are clamped (and
-    // masked later).
-    auto fill = [&](int it, char* b) __attribute__((always_inline)) {
-        __amdgpu_buffer_rsrc_t q_rs, do_rs, lse_rs, d_rs;
-        head_rsrc(it / nq, q_rs, do_rs, lse_rs, d_rs);
-        const int r0 = (qt_begin + it % nq) * BR;
-        issue(q_rs, r0, b, w * QSPW, QSPW);
-        issue(do_rs, r0, b + QTB, w * QSPW, QSPW);
-        const uint32_t row = (uint32_t)min(r0 + lane, N - 1);
-        if (w == 0 && lane < BR) b2lds4(lse_rs, 4 * row, reinterpret_cast<float*>(b + 2 * QTB));
-        if (w == 1 && lane < BR) b2lds4(d_rs, 4 * row, reinterpret_cast<float*>(b + 2 * QTB + 4 * BR));
+    // (wave 1) are one row per lane; rows past the end read as zero (and are
+    // masked).  Work item (r, q): query head r of the group, query tile
+    // qt_begin + q.
+    auto fill = [&](int r, int q, char* b) __attribute__((always_inline)) {
+        const size_t qh = (size_t)kvh * G + r;
+        const int r0 = (qt_begin + q) * BR;
+        issue(Q + qh * N * D, r0, b);
+        issue(dO + qh * N * D, r0, b + QTB);
+        const uint32_t nb = (uint32_t)(N - r0) * 4;
+        if (w == 0 && lane < BR)
+            b2lds4(make_rsrc(LSE + qh * N + r0, nb), 4 * lane, reinterpret_cast<float*>(b + 2 * QTB));
+        if (w == 1 && lane < BR)
+            b2lds4(make_rsrc(delta + qh * N + r0, nb), 4 * lane, reinterpret_cast<float*>(b + 2 * QTB + 4 * BR));
+    };
+    // running (r, q) of the item being computed and of the next one to copy,
+    // in the order it = r * nq + q
+    int cur_q = 0, nxt_r = 0, nxt_q = 0;
+    auto advance = [&](int& r, int& q) __attribute__((always_inline)) {
+        if (++q == nq) {
+            q = 0;
+            ++r;
+        }
     };
 
     // prologue: the first work item
-    if (n_items > 0) fill(0, buf0);
+    if (n_items > 0) {
+        fill(0, 0, buf0);
+        advance(nxt_r, nxt_q);
+    }
     FA_WAIT_VMCNT(0);
 
     auto tile = [&](int it, const char* cur, char* nxt) __attribute__((always_inline)) {
@@ -250,12 +253,16 @@ bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, cons
         const char* os = cur + QTB;
         const float* ls = reinterpret_cast<const float*>(cur + 2 * QTB);
         const float* ds_ = reinterpret_cast<const float*>(cur + 2 * QTB + 4 * BR);
-        const int q0 = (qt_begin + it % nq) * BR;
+        const int q0 = (qt_begin + cur_q) * BR;
+        if (++cur_q == nq) cur_q = 0;
         // copies of this tile have landed, and every wave is done with the
         // previous tile, so its buffers may be refilled
         FA_WAIT_VMCNT(0);
         __builtin_amdgcn_s_barrier();
-        if (it + 1 < n_items) fill(it + 1, nxt);
+        if (it + 1 < n_items) {
+            fill(nxt_r, nxt_q, nxt);
+            advance(nxt_r, nxt_q);
+        }
 
         // a wave whose keys see none of the tile's queries has nothing to add
         const bool wave_dead = (CAUSAL && wk0 > q0 + BR - 1) || wk0 >= N;
@@ -417,7 +424,7 @@ bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const 
     __shared__ __attribute__((aligned(1024))) char vb1[TILEB];
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, w = tid >> 6;
+    const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, g = lane >> 5;
 
     // heavy (late) query tiles first; within one sweep over the heads the G
@@ -458,18 +465,26 @@ bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const 
     const int nkt_w = (wrow0 >= N) ? 0 : (CAUSAL ? min(nkt, (wrow0 + 31) / BC + 1) : nkt);
 
     // K is read both ways (rows for S^T, transposed for K^T): rt_swz.
-    // V is only read by rows (dP^T = V dO^T): k_swz.
-    const __amdgpu_buffer_rsrc_t k_rs = make_rsrc(Kh, (uint32_t)N * ROWB);
-    const __amdgpu_buffer_rsrc_t v_rs = make_rsrc(Vh, (uint32_t)N * ROWB);
+    // V is only read by rows (dP^T = V dO^T): k_swz.  Per-lane offsets inside
+    // a tile are fixed; each tile is addressed by a buffer resource from its
+    // first row to the end of the head, so rows past the end read as zero
+    // (masked).
+    uint32_t k_dma[SPW], v_dma[SPW];
+#pragma unroll
+    for (int i = 0; i < SPW; ++i) {
+        const int row = (w * SPW + i) * RPS + lane / CPR;
+        const int pc = lane % CPR;
+        k_dma[i] = (uint32_t)(row * ROWB + 16 * (pc ^ rt_swz<D>(row)));
+        v_dma[i] = (uint32_t)(row * ROWB + 16 * (pc ^ k_swz<D>(row)));
+    }
     auto issue = [&](int kt, char* kdst, char* vdst) __attribute__((always_inline)) {
+        const uint32_t nb = (uint32_t)(N - kt * BC) * ROWB;
+        const __amdgpu_buffer_rsrc_t k_rs = make_rsrc(Kh + (size_t)kt * BC * D, nb);
+        const __amdgpu_buffer_rsrc_t v_rs = make_rsrc(Vh + (size_t)kt * BC * D, nb);
 #pragma unroll
         for (int i = 0; i < SPW; ++i) {
-            const int seg = w * SPW + i;
-            const int row = seg * RPS + lane / CPR;
-            const int pc = lane % CPR;
-            const uint32_t grow = (uint32_t)min(kt * BC + row, N - 1) * ROWB;
-            b2lds16(k_rs, grow + 16 * (pc ^ rt_swz<D>(row)), kdst + seg * 1024);
-            b2lds16(v_rs, grow + 16 * (pc ^ k_swz<D>(row)), vdst + seg * 1024);
+            b2lds16(k_rs, k_dma[i], kdst + (w * SPW + i) * 1024);
+            b2lds16(v_rs, v_dma[i], vdst + (w * SPW + i) * 1024);
         }
     };
 

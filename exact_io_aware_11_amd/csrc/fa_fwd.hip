@@ -45,8 +45,6 @@ constexpr int FWD_BC32 = 32;    // keys per K/V tile, fp32 path
 // instruction schedule of the bf16 tile loop (measured best on MI355X)
 constexpr int QK_AHEAD = 6;        // K-operand LDS reads kept ahead of the S MFMAs
 constexpr int PV_AHEAD = 4;        // V^T operands read ahead of the O MFMAs
-constexpr int PV_VALU_FIRST = 24;  // exponent work placed before the first O MFMA
-constexpr int PV_VALU_EACH = 5;    // and between the following ones
 constexpr int FWD_THREADS = 256;
 
 // Map the flat block id to (query head, query tile).  One sweep of BH
@@ -81,7 +79,7 @@ fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     constexpr int RPS = 1024 / ROWB;         // rows per 1 KiB copy segment
     constexpr int SPW = TILEB / 1024 / 4;    // copy segments per wave per tile
     constexpr int NKB = BC / 32;             // 32-key blocks per tile
-    constexpr float TAU = 8.f;               // lazy-rescale threshold, log2 units
+    constexpr float P_MAX = 256.f;           // largest tile row sum kept without rescaling
     static_assert(SPW >= 1, "tile too small for four waves");
 
     // Two buffer pairs (K tile, V tile): the copies of tile kt+1 run while
@@ -94,7 +92,8 @@ fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     __shared__ __attribute__((aligned(1024))) char vb1[TILEB];
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, w = tid >> 6;
+    // wave index made wave-uniform, so per-wave bounds and branches stay scalar
+    const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, g = lane >> 5;
 
     int bh, qt;
@@ -122,21 +121,25 @@ fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     // tiles this wave computes on (a causal wave stops at its diagonal)
     const int nkt_w = (wrow0 >= N) ? 0 : (CAUSAL ? min(nkt, (wrow0 + 31) / BC + 1) : nkt);
 
-    // Copy K or V tile kt into an LDS buffer.  Rows past the end are clamped
-    // to row N-1: they are masked (K) or weighted by 0 (V).
-    // one head's K or V (N * ROWB bytes < 2^32, checked by the host)
-    const __amdgpu_buffer_rsrc_t k_rs = make_rsrc(Kh, (uint32_t)N * ROWB);
-    const __amdgpu_buffer_rsrc_t v_rs = make_rsrc(Vh, (uint32_t)N * ROWB);
-    auto issue = [&](int kt, char* dst, bool is_v) __attribute__((always_inline)) {
+    // Copy K or V tile kt into an LDS buffer.  Each lane's byte offsets inside
+    // a tile (row and swizzled chunk) are fixed for the whole kernel; the tile
+    // is addressed by a buffer resource that starts at the tile and ends at
+    // the end of the head, so the per-tile work is scalar and rows past the
+    // end read as zero (they are masked for K and weighted by 0 for V).
+    // One head's K or V is below 2^32 bytes (checked by the host).
+    uint32_t k_dma[SPW], v_dma[SPW];
 #pragma unroll
-        for (int i = 0; i < SPW; ++i) {
-            const int seg = w * SPW + i;
-            const int row = seg * RPS + lane / CPR;
-            const int pc = lane % CPR;
-            const uint32_t grow = (uint32_t)min(kt * BC + row, N - 1) * ROWB;
-            const int lc = pc ^ (is_v ? v_swz<D>(row) : k_swz<D>(row));
-            b2lds16(is_v ? v_rs : k_rs, grow + 16 * lc, dst + seg * 1024);
-        }
+    for (int i = 0; i < SPW; ++i) {
+        const int row = (w * SPW + i) * RPS + lane / CPR;
+        const int pc = lane % CPR;
+        k_dma[i] = (uint32_t)(row * ROWB + 16 * (pc ^ k_swz<D>(row)));
+        v_dma[i] = (uint32_t)(row * ROWB + 16 * (pc ^ v_swz<D>(row)));
+    }
+    auto issue = [&](int kt, char* dst, bool is_v) __attribute__((always_inline)) {
+        const __bf16* base = (is_v ? Vh : Kh) + (size_t)kt * BC * D;
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(base, (uint32_t)(N - kt * BC) * ROWB);
+#pragma unroll
+        for (int i = 0; i < SPW; ++i) b2lds16(rs, is_v ? v_dma[i] : k_dma[i], dst + (w * SPW + i) * 1024);
     };
 
     // Per-lane LDS byte offsets, fixed for the whole kernel (the swizzles only
@@ -181,37 +184,19 @@ fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
         }
         __builtin_amdgcn_sched_group_barrier(0x008, QK_AHEAD, 0);
     };
-    // mask tile kt of S (branch-free; lim is large when nothing is hidden) and
-    // return the row max in log2 units
-    auto mask_max = [&](int kt, f32x16* s) __attribute__((always_inline)) -> float {
+    // mask tile kt of S (branch-free; lim is large when nothing is hidden)
+    auto mask = [&](int kt, f32x16* s) __attribute__((always_inline)) {
         const int lim = last_visible - kt * BC - 4 * g;
-        float mx = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
+            for (int r = 0; r < 16; ++r)
                 s[kb][r] = (32 * kb + 8 * (r >> 2) + (r & 3) > lim) ? -INFINITY : s[kb][r];
-                mx = fmaxf(mx, s[kb][r]);
-            }
-        return xor32_max(mx) * c;
     };
-    // Lazy rescaling: the exponentials use a reference max that is only raised
-    // when the row max exceeds it by more than TAU (so p <= 2^TAU).
-    auto rescale = [&](float mx) __attribute__((always_inline)) {
-        if (__any(mx > m_ref + TAU)) {
-            const float m_new = fmaxf(m_ref, mx);
-            const float alpha = exp2_fast(m_ref - m_new);   // 0 on the first tile
-            m_ref = m_new;
-            l_run *= alpha;
-#pragma unroll
-            for (int mb = 0; mb < D / 32; ++mb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) oacc[mb][r] *= alpha;
-        }
-    };
-    // P (bf16) laid out as the B operand of O^T += V^T P^T.  The row sum adds
-    // the same bf16-rounded values the PV product uses (dot2 against 1).
-    auto probs = [&](const f32x16* s, bf16x8* pb) __attribute__((always_inline)) {
+    // P = 2^(c*S - m_ref) (bf16) laid out as the B operand of O^T += V^T P^T;
+    // returns this lane's sum of the same bf16-rounded values the PV product
+    // uses (dot2 against 1).
+    auto probs = [&](const f32x16* s, bf16x8* pb) __attribute__((always_inline)) -> float {
         const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
         float psum[2] = {0.f, 0.f};
 #pragma unroll
@@ -228,7 +213,37 @@ fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                 }
                 pb[2 * kb + h] = as_bf16x8(make_uint4(pk[0], pk[1], pk[2], pk[3]));
             }
-        l_run += psum[0] + psum[1];
+        return psum[0] + psum[1];
+    };
+    // Lazy rescaling without a per-tile max.  The tile's exponentials are
+    // first taken against the current reference m_ref.  Every probability is
+    // non-negative, so a lane sum of at most P_MAX bounds each of them by
+    // P_MAX, and the tile is kept.  Otherwise (some value overflowed or grew
+    // large, or the row has no reference yet) the tile's row max is taken,
+    // the reference is raised to it if larger -- O and l are rescaled by the
+    // same factor, so numerator and denominator stay consistent -- and the
+    // exponentials are recomputed.
+    auto softmax = [&](const f32x16* s, bf16x8* pb) __attribute__((always_inline)) {
+        float ps = probs(s, pb);
+        if (__any(!(ps <= P_MAX) || m_ref == -INFINITY)) {
+            float mx = -INFINITY;
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+            mx = xor32_max(mx) * c;
+            if (mx > m_ref) {
+                const float alpha = exp2_fast(m_ref - mx);   // 0 while the reference is -inf
+                m_ref = mx;
+                l_run *= alpha;
+#pragma unroll
+                for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) oacc[mb][r] *= alpha;
+            }
+            ps = probs(s, pb);
+        }
+        l_run += ps;
     };
     // O^T += V^T P^T ; V^T operand read transposed from the row-major tile
     auto pv = [&](const char* Vs, const bf16x8* pb) __attribute__((always_inline)) {
@@ -241,17 +256,13 @@ fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                 const bf16x8 a = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
                 oacc[mb] = mfma_bf16(a, pb[ks], oacc[mb]);
             }
-        // V^T reads for the first PV_AHEAD MFMAs are issued before the
-        // exponentials (which hide their latency); the remaining exponentials,
-        // later reads and MFMAs are interleaved.
+        // Keep the V^T reads of PV_AHEAD products in flight ahead of the MFMAs.
         constexpr int n = (BC / 16) * (D / 32);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2 * PV_AHEAD, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, PV_VALU_FIRST, 0);      // VALU
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * PV_AHEAD, 0);       // LDS reads
 #pragma unroll
         for (int i = 0; i < n - PV_AHEAD; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);               // MFMA
             __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, PV_VALU_EACH, 0);
         }
         __builtin_amdgcn_sched_group_barrier(0x008, PV_AHEAD, 0);
     };
@@ -268,21 +279,9 @@ fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
         if (kt >= nkt_w) return;
         f32x16 s[NKB];
         qk(kc, s);
-        float mx;
-        const bool need_mask = (kt * BC + BC > N) || (CAUSAL && kt * BC + BC - 1 > wrow0);
-        if (need_mask) {
-            mx = mask_max(kt, s);
-        } else {
-            mx = -INFINITY;
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-            mx = xor32_max(mx) * c;
-        }
-        rescale(mx);
+        if ((kt * BC + BC > N) || (CAUSAL && kt * BC + BC - 1 > wrow0)) mask(kt, s);
         bf16x8 pb[BC / 16];
-        probs(s, pb);
+        softmax(s, pb);
         pv(vcb, pb);
     };
     if (nkt > 0) {
@@ -333,7 +332,7 @@ fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
     __shared__ __attribute__((aligned(16))) float Vs[BC * VS];
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, w = tid >> 6;
+    const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, g = lane >> 5;
 
     int bh, qt;

@@ -156,6 +156,26 @@ def test_fwd_large_scores_stay_finite():
     assert np.max(np.abs(to64(lse) - lse_ref) / np.maximum(1.0, np.abs(lse_ref))) <= 2e-3
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fwd_rising_scores_rescale(causal, d):
+    # K rows scaled by a ramp growing along the keys: every later key tile
+    # raises the row maximum, so the output accumulated so far must be
+    # rescaled again and again (and some tiles overflow the kept-sum bound
+    # while each of their values alone would not).
+    fa = _fa()
+    B, H, N = 1, 2, 700
+    q, k, v = W.make_custom(B, H, N, d, "bf16", seed=79, device=DEV)
+    ramp = torch.linspace(1.0, 6.0, N, device=DEV).view(1, 1, N, 1)
+    k = (k.float() * ramp).to(torch.bfloat16)
+    say(f"fa_fwd rising scores causal={causal} d={d}")
+    o, lse = fa.attention(q, k, v, is_causal=causal)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = ref_fwd(to64(q), to64(k), to64(v), causal, 1 / math.sqrt(d))
+    assert_bf16_close(to64(o), o_ref, "O")
+    assert np.max(np.abs(to64(lse) - lse_ref) / np.maximum(1.0, np.abs(lse_ref))) <= 2e-3
+
+
 def test_fwd_deterministic_and_allocation_free():
     fa = _fa()
     q, k, v = W.make_custom(2, 4, 1000, 128, "bf16", seed=79, device=DEV)
