@@ -80,7 +80,7 @@ class Buffers:
         self.dq = torch.empty_like(self.q)
         self.dk = torch.empty_like(self.q)
         self.dv = torch.empty_like(self.q)
-        self.bwd_ws_bytes = fa.fa_bwd_workspace_bytes(t.B, t.H, t.N, t.d)
+        self.bwd_ws_bytes = fa.fa_bwd_workspace_bytes(t.B, t.H, t.H, t.N, t.d)
         self.bwd_ws = torch.empty((self.bwd_ws_bytes,), dtype=torch.uint8, device=dev)
         dcfg = self.w_dec
         self.dq_in, self.kc, self.vc = W.make_inputs(dcfg, dev)
@@ -130,7 +130,7 @@ def sweep(torch, fa, W, dev, iters=10):
         o = torch.empty_like(q)
         lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
         dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
-        nb = fa.fa_bwd_workspace_bytes(B, H, N, d)
+        nb = fa.fa_bwd_workspace_bytes(B, H, H, N, d)
         ws = torch.empty((nb,), dtype=torch.uint8, device=dev)
 
         def f():
@@ -207,7 +207,7 @@ def gqa_measure(torch, fa, W, dev, iters=20):
     o = torch.empty_like(q)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    nb = fa.fa_bwd_workspace_bytes(B, H, N, d)
+    nb = fa.fa_bwd_workspace_bytes(B, H, Hkv, N, d)
     ws = torch.empty((nb,), dtype=torch.uint8, device=dev)
 
     def f():

@@ -63,7 +63,7 @@ def _load() -> ctypes.CDLL:
     P, I, F, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     lib_.fa_fwd.argtypes = [P, P, P, P, I, P, I, I, I, I, I, I, I, F, P]
     lib_.fa_fwd.restype = I
-    lib_.fa_bwd_workspace_bytes.argtypes = [I, I, I, I]
+    lib_.fa_bwd_workspace_bytes.argtypes = [I, I, I, I, I]
     lib_.fa_bwd_workspace_bytes.restype = Z
     lib_.fa_bwd.argtypes = [P, P, P, P, I, P, P, P, P, P, P, Z, I, I, I, I, I, I, I, F, P]
     lib_.fa_bwd.restype = I
@@ -95,8 +95,8 @@ def fa_fwd(q, k, v, o, o_dtype, lse, B, H, Hkv, N, d, in_dtype, causal, scale, s
     return lib.fa_fwd(q, k, v, o, o_dtype, lse, B, H, Hkv, N, d, in_dtype, int(causal), scale, stream)
 
 
-def fa_bwd_workspace_bytes(B, H, N, d) -> int:
-    return lib.fa_bwd_workspace_bytes(B, H, N, d)
+def fa_bwd_workspace_bytes(B, H, Hkv, N, d) -> int:
+    return lib.fa_bwd_workspace_bytes(B, H, Hkv, N, d)
 
 
 def fa_bwd(q, k, v, o, o_dtype, lse, dout, dq, dk, dv, workspace, workspace_bytes,
@@ -211,7 +211,7 @@ def attention_backward(q, k, v, o, lse, do, is_causal: bool = False, scale: floa
     dq = torch.empty_like(q)
     dk = torch.empty_like(k)
     dv = torch.empty_like(v)
-    nbytes = fa_bwd_workspace_bytes(B, H, N, d)
+    nbytes = fa_bwd_workspace_bytes(B, H, Hkv, N, d)
     ws = torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=q.device)
     st = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), _dtype_code(o), lse.data_ptr(),
                 do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr(), nbytes,

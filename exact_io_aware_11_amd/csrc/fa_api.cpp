@@ -115,9 +115,17 @@ fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, fa_dtyp
     return from_hip(fa::launch_fwd(a));
 }
 
-size_t fa_bwd_workspace_bytes(int B, int H, int N, int d) {
-    if (!dims_ok(B, H, N) || d < 1 || !total_ok(B, H, N, d)) return 0;
-    return (size_t)B * H * N * sizeof(float);
+// workspace layout: D [B,H,N] fp32, padded to 256 bytes; then, when the
+// grouped-head split is taken, partial dK^T and dV^T rows [B,H,N,d] fp32 each
+static size_t bwd_delta_bytes(int B, int H, int N) {
+    return ((size_t)B * H * N * sizeof(float) + 255) & ~(size_t)255;
+}
+
+size_t fa_bwd_workspace_bytes(int B, int H, int Hkv, int N, int d) {
+    if (!dims_ok(B, H, N) || !kv_ok(H, Hkv) || d < 1 || !total_ok(B, H, N, d)) return 0;
+    size_t n = bwd_delta_bytes(B, H, N);
+    if (fa::bwd_split_heads(B, H, Hkv, N)) n += 2 * (size_t)B * H * N * d * sizeof(float);
+    return n;
 }
 
 fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, fa_dtype_t o_dtype,
@@ -132,12 +140,15 @@ fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, f
     const void* ptrs[] = {q, k, v, o, lse, dout, dq, dk, dv};
     for (const void* p : ptrs)
         if (!aligned16(p)) return FA_ERR_ALIGN;
-    const size_t need = fa_bwd_workspace_bytes(B, H, N, d);
+    const size_t need = fa_bwd_workspace_bytes(B, H, Hkv, N, d);
     if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
     if (!aligned16(workspace)) return FA_ERR_ALIGN;
     float* delta = static_cast<float*>(workspace);
-    fa::BwdArgs a{q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, Hkv, N, d, o_dtype == FA_BF16, causal != 0,
-                  scale, stream};
+    const bool split = fa::bwd_split_heads(B, H, Hkv, N);
+    float* pdk = split ? reinterpret_cast<float*>(static_cast<char*>(workspace) + bwd_delta_bytes(B, H, N)) : nullptr;
+    float* pdv = split ? pdk + (size_t)B * H * N * d : nullptr;
+    fa::BwdArgs a{q, k, v, o, lse, dout, dq, dk, dv, delta, pdk, pdv, split, B, H, Hkv, N, d,
+                  o_dtype == FA_BF16, causal != 0, scale, stream};
     return from_hip(fa::launch_bwd(a));
 }
 

@@ -18,6 +18,11 @@
 //                 LSE and D of the next query tile are copied global -> LDS by
 //                 buffer DMA while the current one is computed.  dK^T and dV^T
 //                 accumulate in registers and are stored once.
+//                 With grouped heads and a grid of few workgroups the causal
+//                 imbalance between key tiles would decide the run time; then
+//                 each query head gets its own workgroup, which stores fp32
+//                 partial dK^T / dV^T rows, and bwd_kv_reduce sums them over
+//                 the group in head order (a fourth launch).
 //   3. bwd_dq:    one workgroup per tile of 128 query rows, streaming the K/V
 //                 tiles of its head like the forward pass: it recomputes S, P
 //                 and dP, forms dS and accumulates dQ^T = K^T dS^T in
@@ -44,7 +49,7 @@ namespace fa {
 namespace {
 
 constexpr int BWD_BR = 64;       // query rows per inner step
-constexpr int BWD_BC = 128;      // keys per workgroup (4 waves x 32)
+constexpr int BWD_BC = kBwdKeyTile;   // keys per workgroup (4 waves x 32)
 constexpr int BWD_THREADS = 256;
 
 // ---------------------------------------------------------------------------
@@ -114,12 +119,16 @@ bwd_prep_kernel(const void* __restrict__ O, const __bf16* __restrict__ dO, float
     __builtin_amdgcn_s_waitcnt((((n) & 15) | (((n) >> 4) << 14)) | (7 << 4) | (15 << 8))
 #define FA_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4))
 
-template <int D, bool CAUSAL>
+// SPLIT: one workgroup per (query head, key tile) instead of per (K/V head,
+// key tile); the unscaled dK^T / dV^T rows of that query head go to the fp32
+// partial buffers pdk / pdv ([B*H, N, D]) and bwd_kv_reduce_kernel sums them.
+template <int D, bool CAUSAL, bool SPLIT>
 __global__ void __launch_bounds__(BWD_THREADS)
 bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
                 const __bf16* __restrict__ dO, const float* __restrict__ LSE,
                 const float* __restrict__ delta, __bf16* __restrict__ dK,
-                __bf16* __restrict__ dV, int BHkv, int G, int N, float c /* scale*log2e */, float scale) {
+                __bf16* __restrict__ dV, float* __restrict__ pdk, float* __restrict__ pdv,
+                int BHkv, int G, int N, float c /* scale*log2e */, float scale) {
     constexpr int BR = BWD_BR, BC = BWD_BC;
     constexpr int ROWB = 2 * D;                  // bytes per row of a Q/dO/K tile
     constexpr int CPR = D / 8;
@@ -144,8 +153,20 @@ bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, cons
     // One workgroup per (K/V head, key tile); heavy tiles first: key tile 0
     // sees every query tile.  The G query heads sharing this K/V head are
     // visited in turn, so dK and dV sum their contributions in registers.
-    const int kvh = blockIdx.x % BHkv;
-    const int kt = blockIdx.x / BHkv;
+    // SPLIT: one workgroup per (query head, key tile), in the forward's block
+    // order (the G heads of a K/V head NG = B*Hkv ids apart).
+    const int NHG = SPLIT ? 1 : G;                // query heads this workgroup visits
+    int kvh, kt, head0;                           // K/V head, key tile, first query head
+    if constexpr (SPLIT) {
+        const int BH = BHkv * G, j = blockIdx.x % BH;
+        kt = blockIdx.x / BH;
+        head0 = (j % BHkv) * G + j / BHkv;
+        kvh = head0 / G;
+    } else {
+        kvh = blockIdx.x % BHkv;
+        kt = blockIdx.x / BHkv;
+        head0 = kvh * G;
+    }
     const int k0 = kt * BC;
     const size_t kvoff = (size_t)kvh * (size_t)N * D;
     const __bf16* Kh = K + kvoff;
@@ -211,17 +232,17 @@ bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, cons
     const int nqt = (N + BR - 1) / BR;
     const int qt_begin = CAUSAL ? (k0 / BR) : 0;
 
-    // Work items: (query head r of the group, query tile qt) for r = 0..G-1
-    // and qt = qt_begin..nqt-1, flattened to it = r * nq + (qt - qt_begin).
+    // Work items: (query head head0 + r, query tile qt) for r < NHG and
+    // qt = qt_begin..nqt-1, flattened to it = r * nq + (qt - qt_begin).
     const int nq = nqt - qt_begin;
-    const int n_items = G * nq;
+    const int n_items = NHG * nq;
 
     // buffer layout: Q tile | dO tile | LSE[BR] | D[BR].  LSE (wave 0) and D
     // (wave 1) are one row per lane; rows past the end read as zero (and are
     // masked).  Work item (r, q): query head r of the group, query tile
     // qt_begin + q.
     auto fill = [&](int r, int q, char* b) __attribute__((always_inline)) {
-        const size_t qh = (size_t)kvh * G + r;
+        const size_t qh = (size_t)head0 + r;
         const int r0 = (qt_begin + q) * BR;
         issue(Q + qh * N * D, r0, b);
         issue(dO + qh * N * D, r0, b + QTB);
@@ -374,7 +395,21 @@ bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, cons
     }
 
     // dV = (dV^T)^T, dK = scale (dK^T)^T: lane holds key `key`, dims in runs of 4
-    if (key_live) {
+    if (SPLIT && key_live) {
+        float* pkrow = pdk + ((size_t)head0 * N + key) * D;
+        float* pvrow = pdv + ((size_t)head0 * N + key) * D;
+#pragma unroll
+        for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb) {
+                const int d0 = 32 * mb + 8 * rb + 4 * g;
+                *reinterpret_cast<float4*>(pvrow + d0) =
+                    make_float4(dvt[mb][4 * rb], dvt[mb][4 * rb + 1], dvt[mb][4 * rb + 2], dvt[mb][4 * rb + 3]);
+                *reinterpret_cast<float4*>(pkrow + d0) =
+                    make_float4(dkt[mb][4 * rb], dkt[mb][4 * rb + 1], dkt[mb][4 * rb + 2], dkt[mb][4 * rb + 3]);
+            }
+    }
+    if (!SPLIT && key_live) {
         __bf16* dvrow = dV + kvoff + (size_t)key * D;
         __bf16* dkrow = dK + kvoff + (size_t)key * D;
 #pragma unroll
@@ -390,6 +425,39 @@ bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, cons
                                pack_bf16x2(scale * dkt[mb][4 * rb + 2], scale * dkt[mb][4 * rb + 3]));
             }
     }
+}
+
+// ---------------------------------------------------------------------------
+// Sum of the split dK/dV partials over the G query heads of each K/V head,
+// in head order (deterministic); dK is scaled here.  Eight elements per
+// thread.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ void __launch_bounds__(256)
+bwd_kv_reduce_kernel(const float* __restrict__ pdk, const float* __restrict__ pdv, __bf16* __restrict__ dK,
+                     __bf16* __restrict__ dV, long long n8, int G, int N, float scale) {
+    const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n8) return;
+    const long long e = 8 * i;                          // element of [B*Hkv, N, D]
+    const long long per_head = (long long)N * D;
+    const long long kvh = e / per_head, rem = e - kvh * per_head;
+    float sk[8] = {}, sv[8] = {};
+    for (int r = 0; r < G; ++r) {
+        const size_t src = (size_t)((kvh * G + r) * per_head + rem);
+        const float4 k0 = *reinterpret_cast<const float4*>(pdk + src);
+        const float4 k1 = *reinterpret_cast<const float4*>(pdk + src + 4);
+        const float4 v0 = *reinterpret_cast<const float4*>(pdv + src);
+        const float4 v1 = *reinterpret_cast<const float4*>(pdv + src + 4);
+        sk[0] += k0.x; sk[1] += k0.y; sk[2] += k0.z; sk[3] += k0.w;
+        sk[4] += k1.x; sk[5] += k1.y; sk[6] += k1.z; sk[7] += k1.w;
+        sv[0] += v0.x; sv[1] += v0.y; sv[2] += v0.z; sv[3] += v0.w;
+        sv[4] += v1.x; sv[5] += v1.y; sv[6] += v1.z; sv[7] += v1.w;
+    }
+    *reinterpret_cast<uint4*>(dK + e) =
+        make_uint4(pack_bf16x2(scale * sk[0], scale * sk[1]), pack_bf16x2(scale * sk[2], scale * sk[3]),
+                   pack_bf16x2(scale * sk[4], scale * sk[5]), pack_bf16x2(scale * sk[6], scale * sk[7]));
+    *reinterpret_cast<uint4*>(dV + e) = make_uint4(pack_bf16x2(sv[0], sv[1]), pack_bf16x2(sv[2], sv[3]),
+                                                   pack_bf16x2(sv[4], sv[5]), pack_bf16x2(sv[6], sv[7]));
 }
 
 // ---------------------------------------------------------------------------
@@ -616,9 +684,22 @@ hipError_t launch_kernels(const BwdArgs& a) {
     if (e != hipSuccess) return e;
     const int nkt = (a.N + BWD_BC - 1) / BWD_BC;
     const int G = a.H / a.Hkv, BHkv = a.B * a.Hkv;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)(nkt * BHkv)), dim3(BWD_THREADS), 0, st,
-                       (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (const __bf16*)a.dout, a.lse,
-                       a.delta, (__bf16*)a.dk, (__bf16*)a.dv, BHkv, G, a.N, a.scale * kLog2e, a.scale);
+    if (a.split) {
+        hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, true>), dim3((unsigned)(nkt * BH)), dim3(BWD_THREADS), 0,
+                           st, (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (const __bf16*)a.dout,
+                           a.lse, a.delta, (__bf16*)a.dk, (__bf16*)a.dv, a.pdk, a.pdv, BHkv, G, a.N,
+                           a.scale * kLog2e, a.scale);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        const long long n8 = (long long)BHkv * a.N * (D / 8);
+        hipLaunchKernelGGL((bwd_kv_reduce_kernel<D>), dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st,
+                           a.pdk, a.pdv, (__bf16*)a.dk, (__bf16*)a.dv, n8, G, a.N, a.scale);
+    } else {
+        hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, false>), dim3((unsigned)(nkt * BHkv)), dim3(BWD_THREADS), 0,
+                           st, (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (const __bf16*)a.dout,
+                           a.lse, a.delta, (__bf16*)a.dk, (__bf16*)a.dv, nullptr, nullptr, BHkv, G, a.N,
+                           a.scale * kLog2e, a.scale);
+    }
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int nqt = (a.N + DQ_BR - 1) / DQ_BR;

@@ -32,6 +32,9 @@ struct BwdArgs {
     void* dk;
     void* dv;
     float* delta;    // workspace: [B,H,N] fp32, rowsum(dO * O)
+    float* pdk;      // workspace when split: [B,H,N,d] fp32 partial dK^T rows per query head
+    float* pdv;      // workspace when split: [B,H,N,d] fp32 partial dV^T rows per query head
+    bool split;      // bwd_split_heads(B, H, Hkv, N)
     int B, H, Hkv, N, d;
     bool o_bf16;
     bool causal;
@@ -70,6 +73,22 @@ struct DecodeArgs {
 // Decode takes the grouped-query kernel (each cache head read once for all
 // the query heads sharing it) when 2 <= H/Hkv <= kDecodeMaxGroup; otherwise
 // the per-query-head kernel.
+// Backward with grouped heads: the dK/dV kernel normally sums the G query
+// heads of a K/V head inside one workgroup (one per K/V head and 128-key
+// tile).  When that grid is small -- below two workgroups per CU -- the
+// uneven causal work of the key tiles decides the run time, so each query head
+// gets a workgroup of its own, writing fp32 partial dK/dV that a second kernel
+// sums over the group in a fixed order.  (Measured on MI355X with 4 query
+// heads per K/V head: the split gains 13% at 256 workgroups and loses 18-29%
+// at 512, where the partials' extra traffic outweighs the better balance.)
+constexpr int kBwdKeyTile = 128;
+constexpr long long kBwdSplitBelow = 512;
+inline bool bwd_split_heads(int B, int H, int Hkv, int N) {
+    if (Hkv >= H) return false;
+    const long long nkt = (N + kBwdKeyTile - 1) / kBwdKeyTile;
+    return nkt * B * Hkv < kBwdSplitBelow;
+}
+
 constexpr int kDecodeMaxGroup = 32;
 inline bool decode_group_path(int H, int Hkv) {
     const int G = H / Hkv;

@@ -90,11 +90,15 @@ fa_status_t fa_fwd(const void* q, const void* k, const void* v,
                    int causal, float scale, void* stream);
 
 /*
- * fa_bwd_workspace_bytes -- bytes of workspace fa_bwd needs: the fp32 row
- * statistic D = rowsum(dO * O), [B,H,N].  Returns 0 if a size is < 1 or the
- * total overflows.
+ * fa_bwd_workspace_bytes -- bytes of workspace fa_bwd needs for this shape:
+ * the fp32 row statistic D = rowsum(dO * O), [B,H,N], padded to 256 bytes.
+ * With grouped heads (Hkv < H) and fewer than 512 (K/V head, 128-key tile)
+ * pairs, fa_bwd gives every query head its own dK/dV workgroups and the
+ * workspace also holds their fp32 partial dK and dV, [B,H,N,d] each, summed
+ * over each group by a second kernel.  Returns 0 if a size is < 1, Hkv does
+ * not divide H or the total overflows.
  */
-size_t fa_bwd_workspace_bytes(int B, int H, int N, int d);
+size_t fa_bwd_workspace_bytes(int B, int H, int Hkv, int N, int d);
 
 /*
  * fa_bwd -- backward pass with recomputation ("Flash Attention uitgelegd",
@@ -113,8 +117,9 @@ size_t fa_bwd_workspace_bytes(int B, int H, int N, int d);
  *                  sum over the H/Hkv query heads that use it.  fp32
  *                  accumulation inside; no atomics, so the results are
  *                  bitwise reproducible.
- *   workspace      device memory of at least fa_bwd_workspace_bytes(); its
- *                  contents on entry do not matter and are clobbered.
+ *   workspace      device memory of at least fa_bwd_workspace_bytes(B, H,
+ *                  Hkv, N, d), 16-byte aligned; its contents on entry do not
+ *                  matter and are clobbered.
  *
  * As for fa_fwd, N*d*2 must be below 2^32 bytes (else FA_ERR_UNSUPPORTED).
  */

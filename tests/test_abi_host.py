@@ -104,7 +104,7 @@ def test_fwd_rejects(kw, status):
 
 def bwd(ws_bytes=None, **kw):
     B, H, N, d = kw.get("B", 1), kw.get("H", 4), kw.get("N", 16), kw.get("d", 64)
-    need = fa.fa_bwd_workspace_bytes(B, H, N, d)
+    need = fa.fa_bwd_workspace_bytes(B, H, kw.get("Hkv", 2), N, d)
     args = dict(q=A, k=A, v=A, o=A, o_dtype=fa.FA_BF16, lse=A, dout=A, dq=A, dk=A, dv=A, ws=A,
                 B=B, H=H, Hkv=2, N=N, d=d, in_dtype=fa.FA_BF16, causal=1, scale=0.125)
     args.update(kw)
@@ -135,15 +135,37 @@ def test_bwd_rejects(kw, status):
 
 
 def test_bwd_rejects_small_workspace():
-    need = fa.fa_bwd_workspace_bytes(1, 4, 16, 64)
+    need = fa.fa_bwd_workspace_bytes(1, 4, 2, 16, 64)
     assert bwd(ws_bytes=need - 1) == fa.FA_ERR_WORKSPACE
+    # the fp32 row statistic alone is not enough when the grouped-head split is taken
+    assert bwd(ws_bytes=256) == fa.FA_ERR_WORKSPACE
 
 
 def test_bwd_workspace_size():
     # one fp32 row statistic D = rowsum(dO * O) per query row: O(N), no N^2 term
     B, H, N, d = 2, 16, 4096, 128
-    assert fa.fa_bwd_workspace_bytes(B, H, N, d) == B * H * N * 4
-    assert fa.fa_bwd_workspace_bytes(0, 1, 1, 64) == 0
+    assert fa.fa_bwd_workspace_bytes(B, H, H, N, d) == B * H * N * 4
+    assert fa.fa_bwd_workspace_bytes(1, 3, 3, 5, 64) == 256          # padded to 256 bytes
+    assert fa.fa_bwd_workspace_bytes(0, 1, 1, 1, 64) == 0
+    assert fa.fa_bwd_workspace_bytes(1, 4, 3, 16, 64) == 0           # Hkv must divide H
+
+
+@pytest.mark.parametrize("B,H,Hkv,N,split", [
+    (4, 16, 4, 2048, True),      # 16 key tiles x 16 K/V heads = 256 workgroups
+    (4, 32, 8, 2048, False),     # 512: enough workgroups, sum in registers
+    (64, 16, 8, 256, False),     # 2 key tiles x 512 = 1024
+    (63, 16, 8, 128, True),      # 1 key tile x 504
+    (64, 16, 8, 128, False),     # 1 key tile x 512
+    (21, 16, 8, 384, True),      # 3 key tiles x 168 = 504
+    (21, 16, 8, 385, False),     # ragged: 4 key tiles x 168 = 672
+    (4, 16, 16, 2048, False),    # no grouping: never split
+])
+def test_bwd_workspace_grouped_split(B, H, Hkv, N, split):
+    # the grouped-head split adds fp32 partial dK and dV, [B,H,N,d] each
+    d = 64
+    delta = (B * H * N * 4 + 255) // 256 * 256
+    want = delta + (2 * B * H * N * d * 4 if split else 0)
+    assert fa.fa_bwd_workspace_bytes(B, H, Hkv, N, d) == want
 
 
 def dec(ws_bytes=None, **kw):

@@ -384,6 +384,29 @@ def test_bwd_gqa(B, H, Hkv, N, d, causal):
     assert_grad_close(to64(dv), rv, "dV")
 
 
+def test_bwd_gqa_large_grid_sums_in_registers():
+    # 2 key tiles x 512 K/V heads = 1024 dK/dV workgroups: enough work for the
+    # kernel to sum each group in registers (the workspace has no partials).
+    # The small grouped shapes above take the per-query-head split instead.
+    fa = _fa()
+    B, H, Hkv, N, d = 64, 16, 8, 256, 64
+    G = H // Hkv
+    assert fa.fa_bwd_workspace_bytes(B, H, Hkv, N, d) == B * H * N * 4
+    q, k, v, do = W.make_gqa(B, H, Hkv, N, d, "bf16", seed=4300, with_dout=True, device=DEV)
+    scale = 1.0 / math.sqrt(d)
+    say(f"fa_bwd gqa large grid B{B} H{H} Hkv{Hkv} N{N} d{d} causal")
+    o, lse = fa.attention(q, k, v, is_causal=True, scale=scale)
+    dq, dk, dv = fa.attention_backward(q, k, v, o, lse, do, is_causal=True, scale=scale)
+    torch.cuda.synchronize()
+    for b, hk in [(0, 0), (17, 5), (63, 7)]:
+        qs = (slice(b, b + 1), slice(hk * G, hk * G + G))
+        ks = (slice(b, b + 1), slice(hk, hk + 1))
+        rq, rk, rv = ref_bwd(to64(q[qs]), to64(k[ks]), to64(v[ks]), to64(do[qs]), True, scale)
+        assert_grad_close(to64(dq[qs]), rq, f"dQ {(b, hk)}")
+        assert_grad_close(to64(dk[ks]), rk, f"dK {(b, hk)}")
+        assert_grad_close(to64(dv[ks]), rv, f"dV {(b, hk)}")
+
+
 def test_bwd_gqa_deterministic():
     fa = _fa()
     q, k, v, do = W.make_gqa(1, 8, 2, 600, 128, "bf16", seed=4200, with_dout=True, device=DEV)
