@@ -6,13 +6,15 @@ things, device memory (``torch.empty``) and the current HIP stream.  There is
 no fallback: if the library is missing, importing this package fails.
 
 Entry points with the C names (raw pointers, sizes, stream handle):
-``fa_fwd``, ``fa_bwd``, ``fa_bwd_workspace_bytes``, ``fa_decode``,
+``fa_fwd``, ``fa_fwd_fp8``, ``fa_bwd``, ``fa_bwd_workspace_bytes``, ``fa_decode``,
 ``fa_decode_workspace_bytes``, ``fa_decode_num_splits``, ``fa_decode_paged``,
 ``fa_status_string``.
 
 Tensor-level helpers with the same semantics:
 ``attention(q, k, v, is_causal=False, scale=None, out_dtype=None) -> (o, lse)``
 (the call shape of PyTorch's scaled_dot_product_attention that the pages show),
+``attention_fp8(q, k, vt, q_scale, k_scale, v_scale, is_causal=False,
+scale=None, out_dtype=None) -> (o, lse)`` on e4m3 inputs,
 ``attention_backward(q, k, v, o, lse, do, is_causal=False, scale=None)``
 ``-> (dq, dk, dv)`` and ``decode(q, k_cache, v_cache, scale=None,
 num_splits=0) -> (o, lse)`` and ``decode_paged(q, k_pool, v_pool, block_table,
@@ -28,9 +30,9 @@ import os
 __all__ = [
     "LIB_PATH", "FA_OK", "FA_ERR_NULL", "FA_ERR_ARG", "FA_ERR_UNSUPPORTED", "FA_ERR_ALIGN",
     "FA_ERR_WORKSPACE", "FA_ERR_HIP", "FA_FP32", "FA_BF16", "FaError",
-    "fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_decode", "fa_decode_workspace_bytes",
+    "fa_fwd", "fa_fwd_fp8", "fa_bwd", "fa_bwd_workspace_bytes", "fa_decode", "fa_decode_workspace_bytes",
     "fa_decode_num_splits", "fa_decode_paged", "fa_status_string",
-    "attention", "attention_backward", "decode", "decode_paged", "lib",
+    "attention", "attention_fp8", "attention_backward", "decode", "decode_paged", "lib",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
@@ -63,6 +65,8 @@ def _load() -> ctypes.CDLL:
     P, I, F, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     lib_.fa_fwd.argtypes = [P, P, P, P, I, P, I, I, I, I, I, I, I, F, P]
     lib_.fa_fwd.restype = I
+    lib_.fa_fwd_fp8.argtypes = [P, P, P, F, F, F, P, I, P, I, I, I, I, I, I, F, P]
+    lib_.fa_fwd_fp8.restype = I
     lib_.fa_bwd_workspace_bytes.argtypes = [I, I, I, I, I]
     lib_.fa_bwd_workspace_bytes.restype = Z
     lib_.fa_bwd.argtypes = [P, P, P, P, I, P, P, P, P, P, P, Z, I, I, I, I, I, I, I, F, P]
@@ -93,6 +97,12 @@ def fa_status_string(status: int) -> str:
 
 def fa_fwd(q, k, v, o, o_dtype, lse, B, H, Hkv, N, d, in_dtype, causal, scale, stream=0) -> int:
     return lib.fa_fwd(q, k, v, o, o_dtype, lse, B, H, Hkv, N, d, in_dtype, int(causal), scale, stream)
+
+
+def fa_fwd_fp8(q, k, vt, q_scale, k_scale, v_scale, o, o_dtype, lse, B, H, Hkv, N, d, causal, scale,
+               stream=0) -> int:
+    return lib.fa_fwd_fp8(q, k, vt, q_scale, k_scale, v_scale, o, o_dtype, lse, B, H, Hkv, N, d, int(causal),
+                          scale, stream)
 
 
 def fa_bwd_workspace_bytes(B, H, Hkv, N, d) -> int:
@@ -188,6 +198,35 @@ def attention(q, k, v, is_causal: bool = False, scale: float | None = None, out_
     st = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), _dtype_code(o), lse.data_ptr(),
                 B, H, Hkv, N, d, _dtype_code(q), is_causal, scale, _stream(q))
     _raise(st, "fa_fwd")
+    return o, lse
+
+
+def attention_fp8(q, k, vt, q_scale: float, k_scale: float, v_scale: float, is_causal: bool = False,
+                  scale: float | None = None, out_dtype=None):
+    """``attention`` on fp8 inputs, via ``fa_fwd_fp8``.
+
+    q: contiguous [B,H,N,d] ``torch.float8_e4m3fn`` GPU tensor; k: [B,Hkv,N,d];
+    vt: V transposed, [B,Hkv,d,N]; all e4m3.  The inputs' real values are
+    q_scale * q, k_scale * k, v_scale * v.  Returns (o [B,H,N,d] of
+    ``out_dtype`` (default bf16), lse [B,H,N] fp32).
+    """
+    torch = _torch()
+    _check(q, "q")
+    B, H, N, d = q.shape
+    _check(k, "k")
+    Hkv = k.shape[1]
+    _check(k, "k", (B, Hkv, N, d))
+    _check(vt, "vt", (B, Hkv, d, N))
+    for t, n in ((q, "q"), (k, "k"), (vt, "vt")):
+        if t.dtype != torch.float8_e4m3fn:
+            raise TypeError(f"{n} must be torch.float8_e4m3fn")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    out_dtype = torch.bfloat16 if out_dtype is None else out_dtype
+    o = torch.empty((B, H, N, d), dtype=out_dtype, device=q.device)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    st = fa_fwd_fp8(q.data_ptr(), k.data_ptr(), vt.data_ptr(), float(q_scale), float(k_scale), float(v_scale),
+                    o.data_ptr(), _dtype_code(o), lse.data_ptr(), B, H, Hkv, N, d, is_causal, scale, _stream(q))
+    _raise(st, "fa_fwd_fp8")
     return o, lse
 
 

@@ -22,7 +22,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libfa.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 
-SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_bwd.hip", "fa_decode.hip"]
+SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_fwd_fp8.hip", "fa_bwd.hip", "fa_decode.hip"]
 
 ARCH = "gfx950"
 

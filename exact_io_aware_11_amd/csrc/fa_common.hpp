@@ -149,6 +149,21 @@ __device__ __forceinline__ int perm16(int k) {
     return (k & ~15) | (pq << 2) | (k & 3);
 }
 
+// Map the flat block id to (query head, query tile).  One sweep of BH
+// consecutive ids covers every head once, so with a causal mask the most
+// expensive (last) query tiles of all heads are issued first.  Within a sweep
+// the G query heads that share a K/V head are NG = BH / G ids apart: the
+// hardware deals blocks round-robin to the 8 XCDs, so when NG is a multiple
+// of 8 a whole group -- and every tile of it -- runs on one XCD and shares
+// that XCD's L2 copy of its K/V.  G = 1 gives bh = id % BH.
+__device__ __forceinline__ void fwd_tile_of(int bid, int BH, int G, int nqt, bool causal,
+                                            int& bh, int& qt) {
+    const int j = bid % BH, NG = BH / G;
+    bh = (j % NG) * G + j / NG;
+    const int t = bid / BH;
+    qt = causal ? (nqt - 1 - t) : t;
+}
+
 // Max / sum of x over lanes l and l ^ 32, in every lane: v_permlane32_swap of
 // x with itself gives (x of lanes 0-31 twice, x of lanes 32-63 twice); the
 // max or sum of its two results is the xor-32 reduction (checked with an

@@ -47,21 +47,6 @@ constexpr int QK_AHEAD = 6;        // K-operand LDS reads kept ahead of the S MF
 constexpr int PV_AHEAD = 4;        // V^T operands read ahead of the O MFMAs
 constexpr int FWD_THREADS = 256;
 
-// Map the flat block id to (query head, query tile).  One sweep of BH
-// consecutive ids covers every head once, so with a causal mask the most
-// expensive (last) query tiles of all heads are issued first.  Within a sweep
-// the G query heads that share a K/V head are NG = BH / G ids apart: the
-// hardware deals blocks round-robin to the 8 XCDs, so when NG is a multiple
-// of 8 a whole group -- and every tile of it -- runs on one XCD and shares
-// that XCD's L2 copy of its K/V.  G = 1 gives bh = id % BH.
-__device__ __forceinline__ void fwd_tile_of(int bid, int BH, int G, int nqt, bool causal,
-                                            int& bh, int& qt) {
-    const int j = bid % BH, NG = BH / G;
-    bh = (j % NG) * G + j / NG;
-    const int t = bid / BH;
-    qt = causal ? (nqt - 1 - t) : t;
-}
-
 // K and V tiles live in LDS row-major without padding (2*D bytes per row) and
 // are filled by direct global->LDS copies; bank conflicts are avoided by
 // permuting the 16-byte chunks of each row with an XOR of the row index

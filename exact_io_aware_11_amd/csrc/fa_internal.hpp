@@ -21,6 +21,22 @@ struct FwdArgs {
     void* stream;
 };
 
+// fp8 (e4m3) forward: Q [B,H,N,d], K [B,Hkv,N,d], V transposed [B,Hkv,d,N];
+// real value = stored value * the tensor's scale
+struct Fp8FwdArgs {
+    const void* q;
+    const void* k;
+    const void* vt;
+    float q_scale, k_scale, v_scale;
+    void* o;
+    float* lse;
+    int B, H, Hkv, N, d;   // N a multiple of 64
+    bool out_bf16;
+    bool causal;
+    float scale;
+    void* stream;
+};
+
 struct BwdArgs {
     const void* q;
     const void* k;
@@ -96,6 +112,7 @@ inline bool decode_group_path(int H, int Hkv) {
 }
 
 hipError_t launch_fwd(const FwdArgs& a);
+hipError_t launch_fwd_fp8(const Fp8FwdArgs& a);
 hipError_t launch_bwd(const BwdArgs& a);
 hipError_t launch_decode(const DecodeArgs& a);
 

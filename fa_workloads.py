@@ -132,6 +132,28 @@ def make_gqa(B: int, H: int, Hkv: int, N: int, d: int, dtype: str, seed: int,
     return [t.to(device) for t in draw(shapes, seed, tdt, 1.0, device="cpu")]
 
 
+def make_fp8(B: int, H: int, Hkv: int, N: int, d: int, seed: int, sigma: float = 1.0, device="cpu",
+             gen_device: str = "cpu"):
+    """Seeded fp8 (e4m3) inputs for ``fa_fwd_fp8``.
+
+    Q [B,H,N,d], K and V [B,Hkv,N,d] are drawn like the other inputs (float32
+    N(0, sigma^2)); each tensor gets the per-tensor factor s = max|x| / 256 and
+    is stored as the e4m3 codes of x / s (torch's round-to-nearest cast), V
+    transposed to [B,Hkv,d,N].  Returns (q8, k8, vt8, q_scale, k_scale,
+    v_scale); the real inputs are s * codes.
+    """
+    q, k, v = draw([(B, H, N, d), (B, Hkv, N, d), (B, Hkv, N, d)], seed, torch.float32, sigma,
+                   device=gen_device)
+    out, scales = [], []
+    for x in (q, k, v):
+        s = float(x.abs().max()) / 256.0
+        out.append((x / s).to(torch.float8_e4m3fn))
+        scales.append(s)
+    q8, k8, v8 = out
+    vt8 = v8.transpose(-1, -2).contiguous()
+    return q8.to(device), k8.to(device), vt8.to(device), scales[0], scales[1], scales[2]
+
+
 def sample_rows(n: int, count: int, seed: int):
     """``count`` distinct query rows drawn uniformly from [0, n) with a seeded generator."""
     g = _gen(seed, "cpu")

@@ -90,6 +90,39 @@ fa_status_t fa_fwd(const void* q, const void* k, const void* v,
                    int causal, float scale, void* stream);
 
 /*
+ * fa_fwd_fp8 -- forward pass on fp8 inputs (the FP8 variant of FlashAttention
+ * named on "Flash Attention uitgelegd", FA3 section; gfx950's e4m3 matrix
+ * products run at twice the bf16 rate).  Computes the same O and LSE as
+ * fa_fwd for the real-valued inputs Q = q_scale * q, K = k_scale * k,
+ * V = v_scale * v.
+ *
+ *   q         [B,H,N,d] e4m3 (OCP FP8 E4M3: 1 sign, 4 exponent, 3 mantissa
+ *             bits, bias 7, largest finite 448, no infinities; one byte each).
+ *   k         [B,Hkv,N,d] e4m3, grouped as for fa_fwd.
+ *   vt        V transposed: [B,Hkv,d,N] e4m3 (for each head, d rows of N keys).
+ *   q_scale, k_scale, v_scale   per-tensor dequantisation factors, finite and
+ *             > 0 (else FA_ERR_ARG).
+ *   o         [B,H,N,d], o_dtype FA_BF16 or FA_FP32.
+ *   lse       [B,H,N] float32, natural log.
+ *
+ * Arithmetic: S accumulates exact e4m3 products in fp32.  The probabilities
+ * are taken against a reference max that is the running row max rounded up
+ * to an integer in base-2 units (so each is at most 1), multiplied by 2^8 and
+ * rounded to e4m3 (nearest even) for the second product; that rounding (3
+ * mantissa bits, relative error at most 2^-4) is the only approximation
+ * beyond fp32 accumulation.  The row sum and the LSE use the unrounded
+ * values.  Uses no workspace.
+ *
+ * d must be 64 or 128 and N a multiple of 64 (else FA_ERR_UNSUPPORTED); all
+ * pointers 16-byte aligned.
+ */
+fa_status_t fa_fwd_fp8(const void* q, const void* k, const void* vt,
+                       float q_scale, float k_scale, float v_scale,
+                       void* o, fa_dtype_t o_dtype, float* lse,
+                       int B, int H, int Hkv, int N, int d,
+                       int causal, float scale, void* stream);
+
+/*
  * fa_bwd_workspace_bytes -- bytes of workspace fa_bwd needs for this shape:
  * the fp32 row statistic D = rowsum(dO * O), [B,H,N], padded to 256 bytes.
  * With grouped heads (Hkv < H) and fewer than 512 (K/V head, 128-key tile)

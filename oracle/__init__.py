@@ -17,3 +17,11 @@ from .attention import (  # noqa: F401
     ref_fwd_tiled,
     ref_merge_partials,
 )
+from .fp8 import (  # noqa: F401
+    E4M3_MAX,
+    e4m3_decode,
+    e4m3_round,
+    fp8_dequantize,
+    fp8_p_rounding_sigma,
+    ref_fwd_fp8,
+)

@@ -1,0 +1,153 @@
+"""fp64 CPU oracle for the fp8 (e4m3) forward -- test infrastructure only.
+
+Only the test suite may import it.  It shares nothing with the HIP path.
+
+The pages name an FP8 variant of the method ("Flash Attention uitgelegd", FA3
+section: FP8 support, lower precision for more throughput) but give no
+rounding convention.  The readings used here, which the library follows:
+
+* Inputs are OCP FP8 E4M3 codes (1 sign bit, 4 exponent bits with bias 7, 3
+  mantissa bits; exponent field 0 holds subnormals of spacing 2^-9; the code
+  S.1111.111 is NaN; no infinities; largest finite 448), each tensor with a
+  dequantisation factor: the real inputs are Q = q_scale * q, K = k_scale * k,
+  V = v_scale * v.  ``e4m3_decode`` is that definition.
+* What the method should produce is still the exact result for those real
+  inputs: ``ref_fwd`` of the attention oracle on the decoded values.
+* The approximation is in the second product.  ``ref_fwd_fp8`` takes the
+  online-softmax steps of the tiled method ("FlashAttention (EL)", tiling and
+  online-softmax sections) over key tiles of ``bc`` keys, with two choices of
+  this build: the reference max is the running max rounded up to an integer
+  in base-2 units, so every probability is at most 1 and every rescale a power
+  of two; and the probabilities enter P V as e4m3 after multiplication by 2^8
+  (``e4m3_round``, nearest even).  The row sum and the LSE use the unrounded
+  values.
+* ``fp8_p_rounding_sigma`` bounds the RMS deviation from the exact result that
+  this rounding introduces: with relative rounding errors of at most half an
+  e4m3 spacing (spacing/value <= 2^-3 for normal numbers), each uniform, the
+  variance of output element (i, e) is at most
+      sum_j [ (2^-3)^2 / 12 * w_ij^2 + 4 * (2^-17)^2 / 12 / l_i^2 ] * v_je^2,
+  w_ij = softmax weight, l_i = sum_j 2^(s_ij - max_j s_ij) (log2 units); the
+  second term covers subnormal codes (spacing 2^-9 after the 2^8 scaling, and
+  a reference max at most one unit above the row max).
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+from .attention import _f64, causal_visible, kv_head
+
+__all__ = ["E4M3_MAX", "e4m3_decode", "e4m3_round", "ref_fwd_fp8", "fp8_p_rounding_sigma", "fp8_dequantize"]
+
+E4M3_MAX = 448.0
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """OCP FP8 E4M3 codes (uint8) -> float64 values, from the format definition."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2((e - 7).astype(np.float64)))
+    mag = np.where((e == 15) & (c & 0x7 == 7), np.nan, mag)
+    return sign * mag
+
+
+def e4m3_round(x) -> np.ndarray:
+    """Nearest E4M3 value of each element (ties to even), as float64.
+
+    Normal numbers in [2^e, 2^(e+1)), e >= -6, have spacing 2^(e-3); below 2^-6
+    the spacing is 2^-9 (subnormals).  Magnitudes above 448 are rejected.
+    """
+    x = _f64(x)
+    a = np.abs(x)
+    if np.any(a > E4M3_MAX):
+        raise ValueError("value beyond the largest finite e4m3 (448)")
+    with np.errstate(divide="ignore"):
+        e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    spacing = np.exp2(np.maximum(e, -6.0) - 3.0)
+    return np.sign(x) * (np.round(a / spacing) * spacing)    # np.round: half to even
+
+
+def fp8_dequantize(q8, k8, vt8, q_scale, k_scale, v_scale):
+    """Real-valued Q [B,H,N,d], K and V [B,Hkv,N,d] (V from its transpose) in float64."""
+    q = e4m3_decode(q8) * float(q_scale)
+    k = e4m3_decode(k8) * float(k_scale)
+    v = np.swapaxes(e4m3_decode(vt8), -1, -2) * float(v_scale)
+    return q, k, np.ascontiguousarray(v)
+
+
+def ref_fwd_fp8(q8, k8, vt8, q_scale, k_scale, v_scale, causal: bool, scale: float,
+                bc: int = 64, round_p: bool = True):
+    """The fp8 forward's steps in float64 (readings in the module docstring).
+
+    q8 [B,H,N,d], k8 [B,Hkv,N,d] and vt8 [B,Hkv,d,N] are e4m3 codes (uint8).
+    Per row, over key tiles of ``bc`` keys, in log2 units (s = scale q.k / ln 2):
+
+        m_new = max(m, ceil(rowmax(s_tile)))     # integer reference
+        alpha = 2^(m - m_new)
+        e     = 2^(s_tile - m_new + 8)           # 2^8 p, at most 2^8
+        l     = alpha l + rowsum(e)
+        acc   = alpha acc + e4m3(e) V_tile       # e unrounded if round_p is False
+
+    At the end O = acc / l and LSE = ln 2 (m - 8) + ln l.  Returns float64 O
+    [B,H,N,d] and LSE [B,H,N]; a row with nothing visible gives O = 0, LSE = -inf.
+    """
+    q, k, v = fp8_dequantize(q8, k8, vt8, q_scale, k_scale, v_scale)
+    B, H, N, d = q.shape
+    Hkv, nk = k.shape[1], k.shape[2]
+    o = np.zeros((B, H, N, d))
+    lse = np.full((B, H, N), -np.inf)
+    vis = causal_visible(np.arange(N), nk) if causal else None
+    rnd = e4m3_round if round_p else (lambda t: t)
+    for b in range(B):
+        for h in range(H):
+            g = kv_head(h, H, Hkv)
+            s = (scale / math.log(2.0)) * (q[b, h] @ k[b, g].T)
+            if vis is not None:
+                s = np.where(vis, s, -np.inf)
+            m = np.full(N, -np.inf)
+            l = np.zeros(N)
+            acc = np.zeros((N, d))
+            for c0 in range(0, nk, bc):
+                blk = s[:, c0:c0 + bc]
+                m_new = np.maximum(m, np.ceil(np.max(blk, axis=1)))
+                ref = np.where(np.isfinite(m_new), m_new, 0.0)
+                alpha = np.where(np.isfinite(m), np.exp2(m - ref), 0.0)
+                e = np.exp2(blk - ref[:, None] + 8.0)
+                l = alpha * l + np.sum(e, axis=1)
+                acc = alpha[:, None] * acc + rnd(e) @ v[b, g, c0:c0 + bc]
+                m = m_new
+            live = l > 0
+            o[b, h] = np.where(live[:, None], acc / np.where(live, l, 1.0)[:, None], 0.0)
+            lse[b, h] = np.where(live, math.log(2.0) * (m - 8.0) + np.log(np.where(live, l, 1.0)), -np.inf)
+    return o, lse
+
+
+def fp8_p_rounding_sigma(q8, k8, vt8, q_scale, k_scale, v_scale, causal: bool, scale: float) -> float:
+    """Upper model of the RMS (over all elements of O) of the deviation that
+    rounding 2^8 p to e4m3 causes (formula in the module docstring)."""
+    q, k, v = fp8_dequantize(q8, k8, vt8, q_scale, k_scale, v_scale)
+    B, H, N, d = q.shape
+    Hkv, nk = k.shape[1], k.shape[2]
+    vis = causal_visible(np.arange(N), nk) if causal else None
+    rel = (2.0 ** -3) ** 2 / 12.0
+    sub = 4.0 * (2.0 ** -17) ** 2 / 12.0
+    total = 0.0
+    for b in range(B):
+        for h in range(H):
+            g = kv_head(h, H, Hkv)
+            s = (scale / math.log(2.0)) * (q[b, h] @ k[b, g].T)
+            if vis is not None:
+                s = np.where(vis, s, -np.inf)
+            mx = np.max(s, axis=1, keepdims=True)
+            p = np.exp2(s - mx)                   # <= 1, exactly 1 at the max
+            l = np.sum(p, axis=1, keepdims=True)
+            w = p / l
+            v2 = v[b, g] ** 2
+            seen = np.ones_like(w) if vis is None else vis.astype(np.float64)
+            var = rel * ((w ** 2) @ v2) + (sub / l ** 2) * (seen @ v2)
+            total += float(np.sum(var))
+    return math.sqrt(total / (B * H * N * d))

@@ -32,7 +32,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
         "fa_bwd", "fa_bwd_workspace_bytes", "fa_decode", "fa_decode_num_splits", "fa_decode_paged",
-        "fa_decode_workspace_bytes", "fa_fwd", "fa_status_string"])
+        "fa_decode_workspace_bytes", "fa_fwd", "fa_fwd_fp8", "fa_status_string"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -100,6 +100,37 @@ def fwd(**kw):
 ])
 def test_fwd_rejects(kw, status):
     assert fwd(**kw) == status
+
+
+def fwd8(**kw):
+    args = dict(q=A, k=A, vt=A, qs=1.0, ks=1.0, vs=1.0, o=A, o_dtype=fa.FA_BF16, lse=A, B=1, H=4, Hkv=2, N=128,
+                d=128, causal=1, scale=0.125)
+    args.update(kw)
+    return fa.fa_fwd_fp8(args["q"], args["k"], args["vt"], args["qs"], args["ks"], args["vs"], args["o"],
+                         args["o_dtype"], args["lse"], args["B"], args["H"], args["Hkv"], args["N"], args["d"],
+                         args["causal"], args["scale"], 0)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=0), fa.FA_ERR_NULL),
+    (dict(vt=0), fa.FA_ERR_NULL),
+    (dict(lse=0), fa.FA_ERR_NULL),
+    (dict(Hkv=3), fa.FA_ERR_ARG),
+    (dict(B=0), fa.FA_ERR_ARG),
+    (dict(scale=float("inf")), fa.FA_ERR_ARG),
+    (dict(qs=0.0), fa.FA_ERR_ARG),
+    (dict(ks=-1.0), fa.FA_ERR_ARG),
+    (dict(vs=float("nan")), fa.FA_ERR_ARG),
+    (dict(N=100), fa.FA_ERR_UNSUPPORTED),       # N must be a multiple of 64
+    (dict(N=65), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=256), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=32), fa.FA_ERR_UNSUPPORTED),
+    (dict(o_dtype=5), fa.FA_ERR_UNSUPPORTED),
+    (dict(vt=MIS), fa.FA_ERR_ALIGN),
+    (dict(o=MIS), fa.FA_ERR_ALIGN),
+])
+def test_fwd_fp8_rejects(kw, status):
+    assert fwd8(**kw) == status
 
 
 def bwd(ws_bytes=None, **kw):
