@@ -16,7 +16,7 @@ bounded sample is reported as ``cpu_baseline``.
 
 After the sweep, ``next_rows`` reports grouped-query attention (decode with
 8 cache heads for 32 query heads, fwd/bwd with groups of 4), paged-cache
-decodes and head dim 256 (forward and decode).
+decodes, head dim 256 (forward and decode) and the fp8 (e4m3) forward.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-sweep]
                        [--no-next] [--no-cpu-baseline]
@@ -38,6 +38,7 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 flop/clk)
 PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
+PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA (spec)
 
 
 def fwd_flops(B, H, N, d, causal=True):
@@ -276,6 +277,40 @@ def paged_measure(torch, fa, dev, iters=20):
         log(f"paged decode {out[name]['workload']}: {ms:.4f} ms, {gbs:.1f} GB/s")
         del q, kp, vp, table, lens, o, lse, ws
         torch.cuda.empty_cache()
+    return out
+
+
+def fp8_measure(torch, fa, W, dev, iters=10):
+    """FP8 (e4m3) forward, causal, d = 128, at the 2K workload (B4 H16 N2048) and
+    the long-context one (B1 H32 N16384); same flop formula, against the fp8
+    MFMA peak."""
+    stream = torch.cuda.current_stream().cuda_stream
+    out = {}
+    for key, (B, H, N) in (("n2048", (4, 16, 2048)), ("n16384", (1, 32, 16384))):
+        d = 128
+        scale = 1.0 / math.sqrt(d)
+        q8, k8, vt8, qs, ks, vs = W.make_fp8(B, H, H, N, d, seed=50 + N // 2048, device=dev, gen_device=dev)
+        o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+
+        def f():
+            st = fa.fa_fwd_fp8(q8.data_ptr(), k8.data_ptr(), vt8.data_ptr(), qs, ks, vs, o.data_ptr(), fa.FA_BF16,
+                               lse.data_ptr(), B, H, H, N, d, 1, scale, stream)
+            assert st == fa.FA_OK, fa.fa_status_string(st)
+        f()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(iters):
+            f()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / iters
+        tf = fwd_flops(B, H, N, d) / (ms * 1e-3) / 1e12
+        out[key] = {"workload": f"B{B} H{H} N{N} d{d} causal, e4m3 in, bf16 out", "ms": round(ms, 4),
+                    "tflops": round(tf, 1), "bound": "mfma", "frac": round(tf / PEAK_FP8_TFLOPS, 4)}
+        log(f"fp8 fwd {out[key]['workload']}: {ms:.4f} ms, {tf:.1f} TFLOP/s")
+        del q8, k8, vt8, o, lse
     return out
 
 
@@ -626,6 +661,8 @@ def main():
         next_rows["paged_decode"] = paged_measure(torch, fa, dev)
         log("head dim 256")
         next_rows["head_dim_256"] = d256_measure(torch, fa, W, dev)
+        log("fp8 forward")
+        next_rows["fp8_forward"] = fp8_measure(torch, fa, W, dev)
 
     cpu = None
     if not args.no_cpu_baseline:
