@@ -58,9 +58,16 @@ __device__ __forceinline__ int pack_fp8x4(float a, float b, float c2, float d) {
     return __builtin_amdgcn_cvt_pk_fp8_f32(c2, d, lo, true);
 }
 
-// source dword (4 keys) of the 64-key tile row that lands at dword u of the
-// LDS row: u = 8g + 4kb + q holds keys kb*32 + 8q + 4g .. +3
+// source dword (4 keys) of the 64-key tile row that belongs at logical dword
+// u of the LDS row: u = 8g + 4kb + q holds keys kb*32 + 8q + 4g .. +3
 __device__ __forceinline__ int vt_src_dword(int u) { return ((u >> 2) & 1) * 8 + 2 * (u & 3) + (u >> 3); }
+
+// Bank spreading.  LDS rows narrower than 256 bytes (the 64 banks) start at
+// only a few bank offsets, so 16 consecutive rows read at equal offsets would
+// collide.  The 16-byte chunks of a row are XOR-permuted by the row's index
+// among rows of equal bank offset: 16 consecutive rows then cover all banks.
+template <int ROWB>
+__device__ __forceinline__ int chunk_swz(int row) { return (row / (256 / ROWB)) & (ROWB / 16 - 1); }
 
 template <int D, bool CAUSAL, bool OUT_BF16>
 __global__ void __launch_bounds__(F8_THREADS) __attribute__((amdgpu_waves_per_eu(2)))
@@ -114,8 +121,8 @@ fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, con
     const int wrow0 = q0 + 32 * w;
     const int nkt_w = (wrow0 >= N) ? 0 : (CAUSAL ? min(nkt, (wrow0 + 31) / BC + 1) : nkt);
 
-    // K tile: row-major, 16-byte chunks XOR-swizzled by the row; V^T tile: D
-    // rows of 64 bytes in the key order described above.  Each tile is
+    // K tile: row-major; V^T tile: D rows of 64 bytes in the key order
+    // described above; both with their chunks permuted by chunk_swz.  Each tile is
     // addressed by buffer resources starting at the tile, so the per-lane
     // offsets below are fixed.  N is a multiple of 64 (checked by the host):
     // every tile is whole.
@@ -124,12 +131,13 @@ fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, con
     for (int i = 0; i < KSPW; ++i) {
         const int row = (w * KSPW + i) * KRPS + lane / KCPR;
         const int slot = lane % KCPR;
-        k_dma[i] = (uint32_t)(row * D + 16 * (slot ^ (row & (KCPR - 1))));
+        k_dma[i] = (uint32_t)(row * D + 16 * (slot ^ chunk_swz<D>(row)));
     }
 #pragma unroll
     for (int i = 0; i < VSPW; ++i) {
         const int row = (w * VSPW + i) * 4 + lane / 16;            // dim
-        v_dma[i] = (uint32_t)((size_t)row * N + 4 * vt_src_dword(lane % 16));
+        const int u = ((lane % 16) ^ (chunk_swz<BC>(row) << 2));    // logical dword at this slot
+        v_dma[i] = (uint32_t)((size_t)row * N + 4 * vt_src_dword(u));
     }
     auto issue = [&](int kt, char* kdst, char* vdst) __attribute__((always_inline)) {
         const __amdgpu_buffer_rsrc_t krs = make_rsrc(Kh + (size_t)kt * BC * D, (uint32_t)(N - kt * BC) * D);
@@ -145,9 +153,11 @@ fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, con
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
-        for (int h = 0; h < 2; ++h) k_off[ks][h] = l32 * D + 16 * ((4 * ks + 2 * g + h) ^ (l32 & (KCPR - 1)));
-    //  V^T: dim row 32*mb + l32, bytes 32*g .. +31
-    const int v_off = l32 * BC + 32 * g;
+        for (int h = 0; h < 2; ++h) k_off[ks][h] = l32 * D + 16 * ((4 * ks + 2 * g + h) ^ chunk_swz<D>(l32));
+    //  V^T: dim row 32*mb + l32, logical chunks 2*g and 2*g + 1
+    int v_off[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) v_off[h] = l32 * BC + 16 * ((2 * g + h) ^ chunk_swz<BC>(l32));
 
     const int last_visible = CAUSAL ? min(qrow, N - 1) : N - 1;
 
@@ -220,9 +230,9 @@ fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, con
         // O^T += V^T P^T
 #pragma unroll
         for (int mb = 0; mb < D / 32; ++mb) {
-            const char* base = Vs + 32 * mb * BC + v_off;
-            const uint4 lo = *reinterpret_cast<const uint4*>(base);
-            const uint4 hi = *reinterpret_cast<const uint4*>(base + 16);
+            const char* base = Vs + 32 * mb * BC;
+            const uint4 lo = *reinterpret_cast<const uint4*>(base + v_off[0]);
+            const uint4 hi = *reinterpret_cast<const uint4*>(base + v_off[1]);
             oacc[mb] = mfma_f8(join8(lo, hi), pb, oacc[mb]);
         }
     };
