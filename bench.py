@@ -280,7 +280,7 @@ def paged_measure(torch, fa, dev, iters=20):
     return out
 
 
-def fp8_measure(torch, fa, W, dev, iters=10):
+def fp8_measure(torch, fa, W, dev, iters=30, warmup=10):
     """FP8 (e4m3) forward, causal, d = 128, at the 2K workload (B4 H16 N2048) and
     the long-context one (B1 H32 N16384); same flop formula, against the fp8
     MFMA peak."""
@@ -297,7 +297,8 @@ def fp8_measure(torch, fa, W, dev, iters=10):
             st = fa.fa_fwd_fp8(q8.data_ptr(), k8.data_ptr(), vt8.data_ptr(), qs, ks, vs, o.data_ptr(), fa.FA_BF16,
                                lse.data_ptr(), B, H, H, N, d, 1, scale, stream)
             assert st == fa.FA_OK, fa.fa_status_string(st)
-        f()
+        for _ in range(warmup):
+            f()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
