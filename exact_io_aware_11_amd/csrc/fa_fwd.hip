@@ -40,7 +40,11 @@ namespace fa {
 namespace {
 
 constexpr int FWD_BR = 128;     // query rows per workgroup (4 waves x 32)
-constexpr int FWD_BC = 64;      // keys per K/V tile, bf16 path
+constexpr int FWD_BC = 64;      // keys per K/V tile, bf16 path (d <= 128)
+// d = 256: 32-key tiles, so that S, P and the 256-column O accumulator fit the
+// 256 vector registers of two waves per SIMD
+template <int D>
+constexpr int fwd_bc() { return D == 256 ? 32 : FWD_BC; }
 constexpr int FWD_BC32 = 32;    // keys per K/V tile, fp32 path
 // instruction schedule of the bf16 tile loop (measured best on MI355X)
 constexpr int QK_AHEAD = 6;        // K-operand LDS reads kept ahead of the S MFMAs
@@ -53,11 +57,11 @@ constexpr int FWD_THREADS = 256;
 // (k_swz for K, read one chunk per lane by 32 consecutive rows; v_swz for V,
 // read with the transposing 8-byte read).
 template <int D, bool CAUSAL, bool OUT_BF16>
-__global__ void __launch_bounds__(FWD_THREADS) __attribute__((amdgpu_waves_per_eu(D == 256 ? 1 : 2)))
+__global__ void __launch_bounds__(FWD_THREADS) __attribute__((amdgpu_waves_per_eu(2)))
 fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                 const __bf16* __restrict__ V, void* __restrict__ O, float* __restrict__ LSE,
                 int BH, int G, int N, int nqt, float c /* scale * log2(e) */) {
-    constexpr int BR = FWD_BR, BC = FWD_BC;
+    constexpr int BR = FWD_BR, BC = fwd_bc<D>();
     constexpr int ROWB = 2 * D;              // bytes per K/V row in LDS
     constexpr int CPR = D / 8;               // 16-byte chunks per row
     constexpr int TILEB = BC * ROWB;         // bytes per K (or V) tile
