@@ -50,7 +50,7 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-next", action="store_true",
@@ -119,6 +119,28 @@ def run_decode(fa, b, stream):
         raise RuntimeError(fa.fa_status_string(st))
 
 
+def timed_ms(torch, fn, iters, warm_ms=50.0):
+    """Mean milliseconds per call of ``fn`` over ``iters`` back-to-back calls on
+    the current stream, after untimed calls worth at least ``warm_ms`` (the
+    chip's clocks need tens of milliseconds of load to settle)."""
+    fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    fn()
+    e1.record()
+    torch.cuda.synchronize()
+    for _ in range(min(500, max(3, math.ceil(warm_ms / max(e0.elapsed_time(e1), 1e-3))))):
+        fn()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(iters):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / iters
+
+
 def sweep(torch, fa, W, dev, iters=10):
     """fwd and bwd TFLOP/s at N = 2K..16K, H = 32, B = 16384/N, causal bf16, d = 128."""
     out = []
@@ -146,15 +168,7 @@ def sweep(torch, fa, W, dev, iters=10):
         res = {"N": N, "B": B, "H": H, "d": d}
         for name, fn, mult in (("fwd", f, 1.0), ("bwd", g, 2.5)):
             f()
-            fn()
-            torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            for _ in range(iters):
-                fn()
-            e1.record()
-            torch.cuda.synchronize()
-            ms = e0.elapsed_time(e1) / iters
+            ms = timed_ms(torch, fn, iters)
             tf = mult * fwd_flops(B, H, N, d) / (ms * 1e-3) / 1e12
             res[name] = {"ms": round(ms, 4), "tflops": round(tf, 1),
                          "frac_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
@@ -176,15 +190,7 @@ def gqa_measure(torch, fa, W, dev, iters=20):
     out = {}
 
     def timed(fn):
-        fn()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(iters):
-            fn()
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / iters
+        return timed_ms(torch, fn, iters)
 
     B, H, Hkv, L, d = 64, 32, 8, 8192, 128
     q, kc, vc = W.make_gqa(B, H, Hkv, 1, d, "bf16", seed=20, device=dev, Nk=L)
@@ -260,15 +266,7 @@ def paged_measure(torch, fa, dev, iters=20):
                                     L // ps, d, fa.FA_BF16, 0, scale, stream)
             if st != fa.FA_OK:
                 raise RuntimeError(fa.fa_status_string(st))
-        fn()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(iters):
-            fn()
-        e1.record()
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / iters
+        ms = timed_ms(torch, fn, iters)
         byt = 2.0 * B * Hkv * L * d * 2
         gbs = byt / (ms * 1e-3) / 1e9
         out[name] = {"workload": f"B{B} H{H} Hkv{Hkv} L{L} d{d} page{ps}", "ms": round(ms, 4),
@@ -280,7 +278,7 @@ def paged_measure(torch, fa, dev, iters=20):
     return out
 
 
-def fp8_measure(torch, fa, W, dev, iters=30, warmup=10):
+def fp8_measure(torch, fa, W, dev, iters=30):
     """FP8 (e4m3) forward, causal, d = 128, at the 2K workload (B4 H16 N2048) and
     the long-context one (B1 H32 N16384); same flop formula, against the fp8
     MFMA peak."""
@@ -297,16 +295,7 @@ def fp8_measure(torch, fa, W, dev, iters=30, warmup=10):
             st = fa.fa_fwd_fp8(q8.data_ptr(), k8.data_ptr(), vt8.data_ptr(), qs, ks, vs, o.data_ptr(), fa.FA_BF16,
                                lse.data_ptr(), B, H, H, N, d, 1, scale, stream)
             assert st == fa.FA_OK, fa.fa_status_string(st)
-        for _ in range(warmup):
-            f()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(iters):
-            f()
-        e1.record()
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / iters
+        ms = timed_ms(torch, f, iters)
         tf = fwd_flops(B, H, N, d) / (ms * 1e-3) / 1e12
         out[key] = {"workload": f"B{B} H{H} N{N} d{d} causal, e4m3 in, bf16 out", "ms": round(ms, 4),
                     "tflops": round(tf, 1), "bound": "mfma", "frac": round(tf / PEAK_FP8_TFLOPS, 4)}
@@ -322,15 +311,7 @@ def d256_measure(torch, fa, W, dev, iters=10):
     out = {}
 
     def timed(fn):
-        fn()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(iters):
-            fn()
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / iters
+        return timed_ms(torch, fn, iters)
 
     B, H, N, d = 4, 16, 4096, 256
     scale = 1.0 / math.sqrt(d)

@@ -231,6 +231,9 @@ decode_split_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ Kc,
 // merge kernel below combines the chunks.
 // ---------------------------------------------------------------------------
 constexpr int DG_BC = 32;          // keys per tile
+
+// s_waitcnt on vmcnt only (expcnt and lgkmcnt at their maximum)
+#define DG_WAIT_VMCNT0() __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8))
 static_assert(kDecodeMaxGroup <= 32, "one 32-column MFMA block of heads per unit");
 
 // waves (units) per workgroup: the d = 256 tiles are twice as large
@@ -257,7 +260,9 @@ decode_group_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ Kc,
     __shared__ __attribute__((aligned(1024))) char vb0[dg_waves<D>()][TILEB];
     __shared__ __attribute__((aligned(1024))) char vb1[dg_waves<D>()][TILEB];
 
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    // w is the same in every lane; saying so keeps the LDS destinations of the
+    // copies (M0) in scalar registers without a per-lane loop
+    const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int l32 = lane & 31, g = lane >> 5;
     const int unit = blockIdx.x * dg_waves<D>() + w;
     if (unit >= units) return;              // no barrier below: waves are independent
@@ -291,20 +296,39 @@ decode_group_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ Kc,
     const size_t hoff = (size_t)gkv * (size_t)L * D;
     __amdgpu_buffer_rsrc_t k_rs = make_rsrc(Kc + hoff, (uint32_t)L * ROWB);
     __amdgpu_buffer_rsrc_t v_rs = make_rsrc(Vc + hoff, (uint32_t)L * ROWB);
+    // Paged: the block-table entries of this unit's pages, 64 at a time, one
+    // per lane (lane i holds page pw0 + i of the sequence).  A tile takes its
+    // entry with readlane, so no table read (and no wait for it, which would
+    // also wait for the copies in flight) sits between two tiles; a new window
+    // is read once every 64 pages.
+    int pwin = -1, pw0 = 0;
+    auto load_window = [&](int first) __attribute__((always_inline)) {
+        pw0 = first;
+        const int pidx = first + lane;
+        pwin = (pidx <= ((k_end - 1) >> pg.ps_log2)) ? pg.block_table[(size_t)b * pg.max_pages + pidx] : -1;
+        DG_WAIT_VMCNT0();   // here, so the tiles that follow need not wait for it
+    };
+    if constexpr (PAGED) {
+        if (ntile > 0) load_window(k_begin >> pg.ps_log2);
+    }
     auto page_of = [&](int k0, bool& ok) __attribute__((always_inline)) -> size_t {
-        const int page = pg.block_table[(size_t)b * pg.max_pages + (k0 >> pg.ps_log2)];
+        const int pidx = k0 >> pg.ps_log2;
+        if (pidx - pw0 >= 64) load_window(pidx);
+        const int page = __builtin_amdgcn_readlane(pwin, pidx - pw0);
         ok = page >= 0 && page < pg.num_pages;
         return ((((size_t)(ok ? page : 0) * pg.Hkv + hk) << pg.ps_log2) +
                 (size_t)(k0 & ((1 << pg.ps_log2) - 1))) * D;
     };
     // copy the 32 rows of tile t; rows past the live keys repeat the last live
     // row (masked for K, weighted by 0 for V), so no unwritten cache row is read
+    bool ok_issued = true;                   // paged: the last issued tile's page is in the pool
     auto issue = [&](int t, char* kdst, char* vdst) __attribute__((always_inline)) {
         const int k0 = k_begin + t * DG_BC;
         int rbase = k0;                      // row of the resource where the tile starts
         if constexpr (PAGED) {
             bool ok;
             const size_t off = page_of(k0, ok);
+            ok_issued = ok;
             k_rs = make_rsrc(Kc + off, ok ? (uint32_t)(DG_BC * ROWB) : 0u);
             v_rs = make_rsrc(Vc + off, ok ? (uint32_t)(DG_BC * ROWB) : 0u);
             rbase = 0;
@@ -339,6 +363,7 @@ decode_group_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ Kc,
     auto step = [&](int t, const char* Ks, const char* Vs, char* kn, char* vn) __attribute__((always_inline)) {
         // this tile's copies have landed, and this wave's reads of the other
         // buffer pair (the previous tile) are complete before it is refilled
+        const bool ok_t = ok_issued;         // page of this tile (issued a step earlier)
         __builtin_amdgcn_s_waitcnt(0);
         if (t + 1 < ntile) issue(t + 1, kn, vn);
         // S^T = K q^T: keys x heads; lane holds head l32, keys 8(r/4) + 4g + r%4
@@ -347,11 +372,7 @@ decode_group_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ Kc,
         for (int ks = 0; ks < D / 16; ++ks)
             st = mfma_bf16(*reinterpret_cast<const bf16x8*>(Ks + k_off[ks]), qf[ks], st);
         int live_keys = k_end - (k_begin + t * DG_BC);
-        if constexpr (PAGED) {
-            bool ok;
-            (void)page_of(k_begin + t * DG_BC, ok);
-            if (!ok) live_keys = 0;
-        }
+        if (PAGED && !ok_t) live_keys = 0;
         const int lim = live_keys - 1 - 4 * g;   // last live key slot of this lane
         float mx = -INFINITY;
 #pragma unroll

@@ -506,6 +506,9 @@ PAGED = [
     (1, 6, 3, 1024, [3000], 128),
     (2, 8, 2, 64, [500, 33], 256),
     (2, 4, 4, 32, [100, 1], 256),
+    # one split: 132 and 65 pages in one chunk, so the grouped kernel's table
+    # window (64 entries) is read again at pages 64 and 128
+    (2, 8, 2, 32, [4200, 2080], 64),
 ]
 
 
@@ -555,18 +558,25 @@ def test_decode_paged_matches_contiguous():
     assert (o1.float() - o2.float()).abs().max().item() <= 2e-2
 
 
-def test_decode_paged_skips_pages_outside_the_pool():
+@pytest.mark.parametrize("n_pages,bad,splits", [
+    (5, [2], 0),
+    # one chunk of 140 pages: bad entries in the second and third 64-entry
+    # window of the grouped kernel's table read
+    (140, [70, 129, 139], 1),
+])
+def test_decode_paged_skips_pages_outside_the_pool(n_pages, bad, splits):
     # a page index outside [0, num_pages) is skipped: the result is the decode
     # over the remaining tokens
     fa = _fa()
     B, H, Hkv, ps, d = 1, 8, 2, 32, 128
-    lens = [32 * 5]
-    q, kp, vp, table, sl = _paged_inputs(B, H, Hkv, ps, lens, d, seed=5200)
-    keep = [0, 1, 3, 4]
+    lens = [32 * n_pages]
+    q, kp, vp, table, sl = _paged_inputs(B, H, Hkv, ps, lens, d, seed=5200 + n_pages)
+    keep = [j for j in range(n_pages) if j not in bad]
     table_bad = table.clone()
-    table_bad[0, 2] = kp.shape[0] + 7
-    say("fa_decode_paged with an out-of-pool page")
-    o, lse = fa.decode_paged(q.to(DEV), kp.to(DEV), vp.to(DEV), table_bad.to(DEV), sl.to(DEV))
+    for j in bad:
+        table_bad[0, j] = kp.shape[0] + 7 if j % 2 else -3
+    say(f"fa_decode_paged with out-of-pool pages {bad} of {n_pages}, splits={splits}")
+    o, lse = fa.decode_paged(q.to(DEV), kp.to(DEV), vp.to(DEV), table_bad.to(DEV), sl.to(DEV), num_splits=splits)
     torch.cuda.synchronize()
     kk = torch.cat([kp[int(table[0, j])] for j in keep], dim=1)[None]
     vv = torch.cat([vp[int(table[0, j])] for j in keep], dim=1)[None]
