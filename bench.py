@@ -16,7 +16,8 @@ bounded sample is reported as ``cpu_baseline``.
 
 After the sweep, ``next_rows`` reports grouped-query attention (decode with
 8 cache heads for 32 query heads, fwd/bwd with groups of 4), paged-cache
-decodes, head dim 256 (forward and decode) and the fp8 (e4m3) forward.
+decodes, batch-1 decode latency, head dim 256 (forward and decode) and the
+fp8 (e4m3) forward.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-sweep]
                        [--no-next] [--no-cpu-baseline]
@@ -301,6 +302,30 @@ def fp8_measure(torch, fa, W, dev, iters=30):
                     "tflops": round(tf, 1), "bound": "mfma", "frac": round(tf / PEAK_FP8_TFLOPS, 4)}
         log(f"fp8 fwd {out[key]['workload']}: {ms:.4f} ms, {tf:.1f} TFLOP/s")
         del q8, k8, vt8, o, lse
+    return out
+
+
+def small_batch_decode_measure(torch, fa, W, dev, iters=200):
+    """Decode steps at batch 1 (latency-bound: a few MB of cache), with 8
+    cache heads (grouped kernel) and 32 (per-head kernel), L = 4K and 16K."""
+    stream = torch.cuda.current_stream().cuda_stream
+    out = {}
+    for key, (Hkv, L) in (("gqa_l4096", (8, 4096)), ("gqa_l16384", (8, 16384)), ("mha_l16384", (32, 16384))):
+        B, H, d = 1, 32, 128
+        q, kc, vc = W.make_gqa(B, H, Hkv, 1, d, "bf16", seed=61 + L // 4096 + Hkv, device=dev, Nk=L)
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+        nb = fa.fa_decode_workspace_bytes(B, H, Hkv, L, d, 0)
+        ws = torch.empty((nb,), dtype=torch.uint8, device=dev)
+        scale = 1.0 / math.sqrt(d)
+        ms = timed_ms(torch, lambda: fa.fa_decode(q.data_ptr(), kc.data_ptr(), vc.data_ptr(), o.data_ptr(),
+                                                  lse.data_ptr(), ws.data_ptr(), nb, B, H, Hkv, L, d, fa.FA_BF16,
+                                                  0, scale, stream), iters)
+        byt = 2.0 * B * Hkv * L * d * 2
+        out[key] = {"workload": f"B{B} H{H} Hkv{Hkv} L{L} d{d}", "us": round(ms * 1e3, 2),
+                    "GBps": round(byt / (ms * 1e-3) / 1e9, 1),
+                    "splits": fa.fa_decode_num_splits(B, H, Hkv, L, d)}
+        log(f"small-batch decode {out[key]['workload']}: {out[key]['us']} us, {out[key]['GBps']} GB/s")
     return out
 
 
@@ -641,6 +666,8 @@ def main():
         next_rows = {"gqa": gqa_measure(torch, fa, W, dev)}
         log("paged KV cache")
         next_rows["paged_decode"] = paged_measure(torch, fa, dev)
+        log("small-batch decode")
+        next_rows["small_batch_decode"] = small_batch_decode_measure(torch, fa, W, dev)
         log("head dim 256")
         next_rows["head_dim_256"] = d256_measure(torch, fa, W, dev)
         log("fp8 forward")

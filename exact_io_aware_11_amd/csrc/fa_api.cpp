@@ -10,6 +10,7 @@
 
 #include "fa_internal.hpp"
 
+
 namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -40,26 +41,31 @@ fa_status_t from_hip(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP
 constexpr int kMaxSplits = 256;
 
 int auto_splits(int B, int H, int Hkv, int L) {
-    long long units, target, min_keys;
+    long long units, target, min_keys, max_s;
     if (fa::decode_group_path(H, Hkv)) {
         // grouped kernel: one wave per (b, cache head, chunk), four per
         // workgroup and one workgroup per CU (its tiles fill the LDS): aim
         // for ~1024 units, one round over the chip (measured better than two
-        // rounds of shorter chunks), with chunks of 256 keys or more
+        // rounds of shorter chunks).  Small batches split down to two 32-key
+        // tiles per chunk, but into at most 64 chunks: measured at B1 Hkv8,
+        // 64 chunks beat both 16 (L = 4K) and 128 (L = 16K).
         units = (long long)B * Hkv;
         target = 1024;
-        min_keys = 256;
+        min_keys = 64;
+        max_s = 64;
     } else {
         // per-head kernel: at least ~4096 workgroups so every CU holds
-        // several, chunks of 512 keys or more so the merge stays negligible
+        // several, with chunks of 512 keys or more (shorter chunks measured
+        // slower at batch 1-4)
         units = (long long)B * H;
         target = 4096;
         min_keys = 512;
+        max_s = kMaxSplits;
     }
     long long s = (target + units - 1) / units;
     const long long max_by_len = (L + min_keys - 1) / min_keys;
     if (s > max_by_len) s = max_by_len;
-    if (s > kMaxSplits) s = kMaxSplits;
+    if (s > max_s) s = max_s;
     if (s < 1) s = 1;
     return (int)s;
 }

@@ -441,7 +441,22 @@ decode_group_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ Kc,
     }
 }
 
-// One wave per (b, h); lane t handles dims t and t + 64 (d = 128) or t (d = 64).
+// One wave per (b, h).  The splits' LSEs are spread over the lanes (lane j
+// holds split j, j + 64, ...) and reduced across the wave, so the statistics
+// cost one load per 64 splits rather than a chain of dependent loads; each
+// lane then accumulates dims lane, lane + 64, ... of O, loading the partial
+// rows of eight splits before combining them.
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+    return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+    return x;
+}
+
 template <int D>
 __global__ void __launch_bounds__(DEC_THREADS)
 decode_merge_kernel(const float* __restrict__ Opart, const float* __restrict__ LSEpart,
@@ -451,20 +466,42 @@ decode_merge_kernel(const float* __restrict__ Opart, const float* __restrict__ L
     if (bh >= BH) return;
     const float* lp = LSEpart + (size_t)bh * S;
     float M = -INFINITY;
-    for (int s = 0; s < S; ++s) M = fmaxf(M, lp[s]);
+    for (int s = lane; s < S; s += 64) M = fmaxf(M, lp[s]);
+    M = wave_max(M);
     const float Mu = (M == -INFINITY) ? 0.f : M;
     float tot = 0.f;
-    for (int s = 0; s < S; ++s) tot += __expf(lp[s] - Mu);
+    for (int s = lane; s < S; s += 64) tot += __expf(lp[s] - Mu);
+    tot = wave_sum(tot);
     const float lse = (tot > 0.f) ? Mu + __logf(tot) : -INFINITY;
     constexpr int PER = D / 64;
+    constexpr int U = 8;
     float acc[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) acc[i] = 0.f;
-    for (int s = 0; s < S; ++s) {
-        const float wgt = (tot > 0.f) ? __expf(lp[s] - lse) : 0.f;
-        const float* op = Opart + ((size_t)bh * S + s) * D;
+    const float* orow = Opart + (size_t)bh * S * D + lane;
+    for (int s0 = 0; s0 < S; s0 += 64) {
+        // weight of split s0 + lane; split s0 + j's weight is read from lane j
+        const float wl = (s0 + lane < S && tot > 0.f) ? __expf(lp[s0 + lane] - lse) : 0.f;
+        const int n = min(64, S - s0);
+        int j = 0;
+        for (; j + U <= n; j += U) {
+            float v[U][PER];
 #pragma unroll
-        for (int i = 0; i < PER; ++i) acc[i] = fmaf(wgt, op[lane + 64 * i], acc[i]);
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int i = 0; i < PER; ++i) v[u][i] = orow[(size_t)(s0 + j + u) * D + 64 * i];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const float wu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), j + u));
+#pragma unroll
+                for (int i = 0; i < PER; ++i) acc[i] = fmaf(wu, v[u][i], acc[i]);
+            }
+        }
+        for (; j < n; ++j) {
+            const float wu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), j));
+#pragma unroll
+            for (int i = 0; i < PER; ++i) acc[i] = fmaf(wu, orow[(size_t)(s0 + j) * D + 64 * i], acc[i]);
+        }
     }
 #pragma unroll
     for (int i = 0; i < PER; ++i) O[(size_t)bh * D + lane + 64 * i] = (__bf16)acc[i];

@@ -262,6 +262,12 @@ def test_decode_split_plan_grouped():
             ((parts * 128 * 4 + 255) // 256) * 256 + parts * 4
     # 512 (batch, cache head) units of 8192 keys: 2 chunks of 4096
     assert fa.fa_decode_num_splits(64, 32, 8, 8192, 128) == 2
+    # batch 1, 8 cache heads: chunks down to 64 keys, at most 64 of them
+    assert fa.fa_decode_num_splits(1, 32, 8, 4096, 128) == 64
+    assert fa.fa_decode_num_splits(1, 32, 8, 16384, 128) == 64
+    assert fa.fa_decode_num_splits(1, 32, 8, 1000, 128) == 16
+    # the per-head path keeps chunks of 512 keys or more
+    assert fa.fa_decode_num_splits(1, 32, 32, 16384, 128) == 32
 
 
 def test_decode_rejects_cache_head_of_4gib():
