@@ -269,7 +269,7 @@ bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, cons
     }
     FA_WAIT_VMCNT(0);
 
-    auto tile = [&](int it, const char* cur, char* nxt, auto ragged) __attribute__((always_inline)) {
+    auto tile = [&](int it, const char* cur, char* nxt) __attribute__((always_inline)) {
         const char* qs = cur;
         const char* os = cur + QTB;
         const float* ls = reinterpret_cast<const float*>(cur + 2 * QTB);
@@ -375,9 +375,11 @@ bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, cons
                 dvdk(3);
             };
             // Causal: the unmasked copy serves every tile off the diagonal.
-            // Without a causal mask only a ragged end needs masking; which
-            // copy runs is decided once per launch (below), as both copies in
-            // one loop body would not fit the register budget.
+            // Without a causal mask no tile needs one: query rows past N
+            // read as zero (Q, dO, LSE and D), so P = 1 there while dO and
+            // dS vanish, and they add nothing to dK or dV; keys past N have
+            // zero K and V, and only their own dK/dV columns (never stored)
+            // see them.
             if constexpr (CAUSAL) {
                 const bool need_mask = (k0 + BC > N) || (q0 + BR > N) || (wk0 + 31 > q0);
                 if (need_mask)
@@ -385,30 +387,14 @@ bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, cons
                 else
                     pipeline(std::false_type{});
             } else {
-                pipeline(ragged);
+                pipeline(std::false_type{});
             }
         }
     };
 
-    if constexpr (CAUSAL) {
-        for (int it = 0; it < n_items; it += 2) {
-            tile(it, buf0, buf1, std::true_type{});
-            if (it + 1 < n_items) tile(it + 1, buf1, buf0, std::true_type{});
-        }
-    } else {
-        // Without a causal mask, only N off the tile grid needs the masked
-        // copy, and then for its last tiles only; the choice is the same for
-        // the whole launch, so each loop holds a single copy.
-        auto run = [&](auto ragged) __attribute__((always_inline)) {
-            for (int it = 0; it < n_items; it += 2) {
-                tile(it, buf0, buf1, ragged);
-                if (it + 1 < n_items) tile(it + 1, buf1, buf0, ragged);
-            }
-        };
-        if (N % BC != 0 || N % BR != 0)
-            run(std::true_type{});
-        else
-            run(std::false_type{});
+    for (int it = 0; it < n_items; it += 2) {
+        tile(it, buf0, buf1);
+        if (it + 1 < n_items) tile(it + 1, buf1, buf0);
     }
 
     // dV = (dV^T)^T, dK = scale (dK^T)^T: lane holds key `key`, dims in runs of 4

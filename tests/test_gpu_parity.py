@@ -239,6 +239,36 @@ def test_bwd_small_shapes(B, H, N, d, causal, o_dtype):
     assert_grad_close(to64(dv), rv, "dV")
 
 
+def test_bwd_noncausal_ragged_with_very_negative_scores():
+    # Scores around -181 (Q = -4 + N(0,1), K = 4 + N(0,1)), so LSE < -88.
+    # The non-causal dK/dV kernel runs unmasked: a key past N (zero K and V)
+    # gets P = exp(-LSE), which overflows to inf, but only in that key's own
+    # dK/dV columns, which are never stored.  The live keys' gradients must
+    # still match the oracle.  (The unit noise keeps dQ well conditioned: the
+    # constant part of K cancels from dQ exactly, since each row of dS sums
+    # to zero.)
+    fa = _fa()
+    B, H, N, d = 1, 2, 200, 128
+    g = torch.Generator().manual_seed(2500)
+    q = torch.full((B, H, N, d), -4.0) + torch.randn((B, H, N, d), generator=g)
+    k = torch.full((B, H, N, d), 4.0) + torch.randn((B, H, N, d), generator=g)
+    v = torch.randn((B, H, N, d), generator=g)
+    do = torch.randn((B, H, N, d), generator=g)
+    q, k, v, do = (t.to(torch.bfloat16).to(DEV) for t in (q, k, v, do))
+    scale = 1.0 / math.sqrt(d)
+    say("fa_bwd non-causal N200 with scores near -181")
+    o, lse = fa.attention(q, k, v, is_causal=False, scale=scale)
+    dq, dk, dv = fa.attention_backward(q, k, v, o, lse, do, is_causal=False, scale=scale)
+    torch.cuda.synchronize()
+    assert float(lse.max()) < -88.0
+    for t in (dq, dk, dv):
+        assert torch.isfinite(t.float()).all()
+    rq, rk, rv = ref_bwd(to64(q), to64(k), to64(v), to64(do), False, scale)
+    assert_grad_close(to64(dq), rq, "dQ")
+    assert_grad_close(to64(dk), rk, "dK")
+    assert_grad_close(to64(dv), rv, "dV")
+
+
 def test_bwd_causal_bf16_b2h16n4096d128_sampled_heads():
     fa = _fa()
     w = W.WORKLOADS["bwd_causal_bf16_b2h16n4096d128"]
@@ -369,6 +399,7 @@ GQA_BWD = [
     (1, 6, 3, 129, 128, True),
     (1, 4, 1, 700, 128, True),
     (1, 8, 4, 65, 64, True),
+    (1, 4, 2, 200, 128, False),
 ]
 
 
