@@ -412,21 +412,44 @@ bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, cons
                     make_float4(dkt[mb][4 * rb], dkt[mb][4 * rb + 1], dkt[mb][4 * rb + 2], dkt[mb][4 * rb + 3]);
             }
     }
-    if (!SPLIT && key_live) {
-        __bf16* dvrow = dV + kvoff + (size_t)key * D;
-        __bf16* dkrow = dK + kvoff + (size_t)key * D;
+    if constexpr (!SPLIT) {
+        // Each lane holds 8 bytes of 16 rows; stored directly, every store
+        // instruction would write 16 bytes into each of 32 rows, which held
+        // the waves for microseconds at the end of every workgroup.  The rows
+        // go through the (now free) tile buffers instead: dV in buf0, dK in
+        // buf1, row 32w + l32 of the tile, 16-byte chunks XOR-permuted by the
+        // row so the writes spread over the banks; then each store writes
+        // whole rows.
+        constexpr int CH = D / 8;                  // 16-byte chunks per row
+        static_assert(128 * ROWB <= BUFB, "dK/dV staging fits a tile buffer");
+        __syncthreads();                           // every wave is done with the tiles
+        const int srow = 32 * w + l32;
 #pragma unroll
         for (int mb = 0; mb < D / 32; ++mb)
 #pragma unroll
             for (int rb = 0; rb < 4; ++rb) {
-                const int d0 = 32 * mb + 8 * rb + 4 * g;
-                *reinterpret_cast<uint2*>(dvrow + d0) =
+                const int off = srow * ROWB + 16 * ((4 * mb + rb) ^ (srow % CH)) + 8 * g;
+                *reinterpret_cast<uint2*>(buf0 + off) =
                     make_uint2(pack_bf16x2(dvt[mb][4 * rb], dvt[mb][4 * rb + 1]),
                                pack_bf16x2(dvt[mb][4 * rb + 2], dvt[mb][4 * rb + 3]));
-                *reinterpret_cast<uint2*>(dkrow + d0) =
+                *reinterpret_cast<uint2*>(buf1 + off) =
                     make_uint2(pack_bf16x2(scale * dkt[mb][4 * rb], scale * dkt[mb][4 * rb + 1]),
                                pack_bf16x2(scale * dkt[mb][4 * rb + 2], scale * dkt[mb][4 * rb + 3]));
             }
+        // this wave's 32 rows back, 64 / CH rows per pass, one chunk per lane
+        constexpr int RPP = 64 / CH;
+#pragma unroll
+        for (int p = 0; p < 32 / RPP; ++p) {
+            const int r = 32 * w + RPP * p + lane / CH, ch = lane % CH;
+            const int off = r * ROWB + 16 * (ch ^ (r % CH));
+            const uint4 v4 = *reinterpret_cast<const uint4*>(buf0 + off);
+            const uint4 k4 = *reinterpret_cast<const uint4*>(buf1 + off);
+            if (k0 + r < N) {
+                const size_t g0 = kvoff + (size_t)(k0 + r) * D + 8 * ch;
+                *reinterpret_cast<uint4*>(dV + g0) = v4;
+                *reinterpret_cast<uint4*>(dK + g0) = k4;
+            }
+        }
     }
 }
 
@@ -656,7 +679,9 @@ bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const 
         if (kt + 1 < nkt) step(kt + 1, kb1, vb1, kb0, vb0);
     }
 
-    // dQ = scale * (dQ^T)^T: lane holds row qrow, dims in runs of 4
+    // dQ = scale * (dQ^T)^T: lane holds row qrow, dims in runs of 4.  (Staging
+    // the rows through LDS for whole-row stores, as the dK/dV kernel does,
+    // measured within noise here: two workgroups per CU hide the epilogue.)
     if (row_live) {
         __bf16* drow = dQ + hoff + (size_t)qrow * D;
 #pragma unroll
