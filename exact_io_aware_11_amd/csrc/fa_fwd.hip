@@ -283,8 +283,40 @@ fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     }
 
     const float l_tot = xor32_sum(l_run);
-    if (qrow < N) {
-        const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
+    const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
+    if constexpr (OUT_BF16 && D <= 128) {
+        // Each lane holds 8 bytes of 16 rows of O.  Stored directly, every
+        // store instruction would write 16 bytes into each of 32 rows; the
+        // rows go through the (now free) tile buffers instead -- wave w uses
+        // one of them, chunks XOR-permuted by the row -- and each store then
+        // writes whole rows.  (At d = 256 the extra registers would spill
+        // under the two-waves-per-SIMD budget, so it stores directly.)
+        constexpr int CH = D / 8;                  // 16-byte chunks per row
+        static_assert(32 * ROWB <= TILEB, "a wave's O rows fit one tile buffer");
+        __syncthreads();                           // every wave is done with the tiles
+        char* sb = w == 0 ? kb0 : w == 1 ? kb1 : w == 2 ? vb0 : vb1;
+#pragma unroll
+        for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb) {
+                const int off = l32 * ROWB + 16 * ((4 * mb + rb) ^ (l32 % CH)) + 8 * g;
+                *reinterpret_cast<uint2*>(sb + off) =
+                    make_uint2(pack_bf16x2(oacc[mb][4 * rb + 0] * inv, oacc[mb][4 * rb + 1] * inv),
+                               pack_bf16x2(oacc[mb][4 * rb + 2] * inv, oacc[mb][4 * rb + 3] * inv));
+            }
+        constexpr int RPP = 64 / CH < 1 ? 1 : 64 / CH;   // rows per pass
+        constexpr int LPR = CH < 64 ? CH : 64;           // lanes per row in a pass
+#pragma unroll
+        for (int p = 0; p < 32 / RPP; ++p)
+#pragma unroll
+            for (int c0 = 0; c0 < CH; c0 += LPR) {
+                const int r = RPP * p + lane / LPR, ch = c0 + lane % LPR;
+                const uint4 v4 = *reinterpret_cast<const uint4*>(sb + r * ROWB + 16 * (ch ^ (r % CH)));
+                if (wrow0 + r < N)
+                    *reinterpret_cast<uint4*>(static_cast<__bf16*>(O) + (size_t)bh * N * D +
+                                              (size_t)(wrow0 + r) * D + 8 * ch) = v4;
+            }
+    } else if (qrow < N) {
         const size_t orow = (size_t)bh * N * D + (size_t)qrow * D;
 #pragma unroll
         for (int mb = 0; mb < D / 32; ++mb)
@@ -300,9 +332,9 @@ fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                     *reinterpret_cast<float4*>(static_cast<float*>(O) + orow + d0) = make_float4(o0, o1, o2, o3);
                 }
             }
-        if (g == 0)
-            LSE[(size_t)bh * N + qrow] = (l_tot > 0.f) ? m_ref * kLn2 + __logf(l_tot) : -INFINITY;
     }
+    if (qrow < N && g == 0)
+        LSE[(size_t)bh * N + qrow] = (l_tot > 0.f) ? m_ref * kLn2 + __logf(l_tot) : -INFINITY;
 }
 
 template <int D, bool CAUSAL>
