@@ -243,7 +243,36 @@ fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, con
     }
 
     const float l_tot = xor32_sum(l_run);   // sum of 2^8 p over the row
-    if (qrow < N) {
+    if constexpr (OUT_BF16) {
+        // bf16 O rows through the (now free) tile buffers, one per wave, so
+        // each store writes whole rows (a direct store instruction would write
+        // 16 bytes into each of 32 rows); chunks XOR-permuted by the row
+        constexpr int ROWB = 2 * D, CH = D / 8;
+        static_assert(32 * ROWB <= KTB && 32 * ROWB <= VTB, "a wave's O rows fit one tile buffer");
+        const float inv = (l_tot > 0.f) ? v_scale / l_tot : 0.f;
+        __syncthreads();                           // every wave is done with the tiles
+        char* sb = w == 0 ? kb0 : w == 1 ? kb1 : w == 2 ? vb0 : vb1;
+#pragma unroll
+        for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb) {
+                const int off = l32 * ROWB + 16 * ((4 * mb + rb) ^ (l32 % CH)) + 8 * g;
+                *reinterpret_cast<uint2*>(sb + off) =
+                    make_uint2(pack_bf16x2(oacc[mb][4 * rb + 0] * inv, oacc[mb][4 * rb + 1] * inv),
+                               pack_bf16x2(oacc[mb][4 * rb + 2] * inv, oacc[mb][4 * rb + 3] * inv));
+            }
+        constexpr int RPP = 64 / CH;               // rows per pass, one chunk per lane
+#pragma unroll
+        for (int p = 0; p < 32 / RPP; ++p) {
+            const int r = RPP * p + lane / CH, ch = lane % CH;
+            const uint4 v4 = *reinterpret_cast<const uint4*>(sb + r * ROWB + 16 * (ch ^ (r % CH)));
+            if (wrow0 + r < N)
+                *reinterpret_cast<uint4*>(static_cast<__bf16*>(O) + (size_t)bh * N * D + (size_t)(wrow0 + r) * D +
+                                          8 * ch) = v4;
+        }
+        if (qrow < N && g == 0)
+            LSE[(size_t)bh * N + qrow] = (l_tot > 0.f) ? (m_ref - 8.f) * kLn2 + __logf(l_tot) : -INFINITY;
+    } else if (qrow < N) {
         const float inv = (l_tot > 0.f) ? v_scale / l_tot : 0.f;
         const size_t orow = (size_t)bh * N * D + (size_t)qrow * D;
 #pragma unroll
