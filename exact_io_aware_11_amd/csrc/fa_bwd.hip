@@ -398,19 +398,33 @@ bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, cons
     }
 
     // dV = (dV^T)^T, dK = scale (dK^T)^T: lane holds key `key`, dims in runs of 4
-    if (SPLIT && key_live) {
-        float* pkrow = pdk + ((size_t)head0 * N + key) * D;
-        float* pvrow = pdv + ((size_t)head0 * N + key) * D;
+    if constexpr (SPLIT) {
+        // The fp32 partial rows go through the free tile buffers too (waves
+        // 0 and 1 in buf0, 2 and 3 in buf1; dV, then dK in the same rows),
+        // so that each store writes whole rows rather than 16 bytes into each
+        // of 32 rows.
+        constexpr int RB = 4 * D;                  // bytes per fp32 row
+        constexpr int CHF = D / 4;                 // 16-byte chunks per row
+        constexpr int RPPF = 64 / CHF;             // rows per pass, one chunk per lane
+        static_assert(64 * RB <= BUFB, "two waves' fp32 rows fit a tile buffer");
+        __syncthreads();                           // every wave is done with the tiles
+        char* wb = (w < 2 ? buf0 : buf1) + (w & 1) * 32 * RB;
+        auto stagef = [&](const f32x16* acc, float* dst) __attribute__((always_inline)) {
 #pragma unroll
-        for (int mb = 0; mb < D / 32; ++mb)
+            for (int mb = 0; mb < D / 32; ++mb)
 #pragma unroll
-            for (int rb = 0; rb < 4; ++rb) {
-                const int d0 = 32 * mb + 8 * rb + 4 * g;
-                *reinterpret_cast<float4*>(pvrow + d0) =
-                    make_float4(dvt[mb][4 * rb], dvt[mb][4 * rb + 1], dvt[mb][4 * rb + 2], dvt[mb][4 * rb + 3]);
-                *reinterpret_cast<float4*>(pkrow + d0) =
-                    make_float4(dkt[mb][4 * rb], dkt[mb][4 * rb + 1], dkt[mb][4 * rb + 2], dkt[mb][4 * rb + 3]);
+                for (int rb = 0; rb < 4; ++rb)
+                    *reinterpret_cast<float4*>(wb + l32 * RB + 16 * ((8 * mb + 2 * rb + g) ^ (l32 % CHF))) =
+                        make_float4(acc[mb][4 * rb], acc[mb][4 * rb + 1], acc[mb][4 * rb + 2], acc[mb][4 * rb + 3]);
+#pragma unroll
+            for (int p = 0; p < 32 / RPPF; ++p) {
+                const int r = RPPF * p + lane / CHF, ch = lane % CHF;
+                const float4 v = *reinterpret_cast<const float4*>(wb + r * RB + 16 * (ch ^ (r % CHF)));
+                if (wk0 + r < N) *reinterpret_cast<float4*>(dst + ((size_t)head0 * N + wk0 + r) * D + 4 * ch) = v;
             }
+        };
+        stagef(dvt, pdv);
+        stagef(dkt, pdk);
     }
     if constexpr (!SPLIT) {
         // Each lane holds 8 bytes of 16 rows; stored directly, every store
