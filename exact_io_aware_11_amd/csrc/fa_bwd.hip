@@ -17,7 +17,8 @@
 //                 in registers.  K and V of the tile stay in registers; Q, dO,
 //                 LSE and D of the next query tile are copied global -> LDS by
 //                 buffer DMA while the current one is computed.  dK^T and dV^T
-//                 accumulate in registers and are stored once.
+//                 accumulate in registers and are stored once, staged through
+//                 the free tile buffers so that each store writes whole rows.
 //                 With grouped heads and a grid of few workgroups the causal
 //                 imbalance between key tiles would decide the run time; then
 //                 each query head gets its own workgroup, which stores fp32
