@@ -5,7 +5,8 @@ The shapes are drawn once from a fixed seed (so a failure names a
 reproducible case): batch 1-3, 1-8 query heads with a random divisor as the
 number of K/V heads, sequence lengths 1-700 (mostly off the tile grid),
 head dim 64 or 128, causal or not; decode with cache lengths 1-2000 and an
-automatic or random split count.
+automatic or random split count; paged decode with random page sizes and
+ragged lengths; the fp8 forward at random multiples of 64 tokens.
 """
 
 from __future__ import annotations
@@ -17,7 +18,7 @@ import pytest
 import torch
 
 import fa_workloads as W
-from oracle import ref_bwd, ref_decode, ref_fwd
+from oracle import ref_bwd, ref_decode, ref_decode_paged, ref_fwd
 from parity_util import assert_bf16_close, assert_grad_close, to64
 
 pytestmark = pytest.mark.gpu
@@ -85,3 +86,67 @@ def test_random_shape_decode(B, H, Hkv, L, d, splits):
     o_ref, lse_ref = ref_decode(to64(q), to64(kc), to64(vc), scale)
     assert_bf16_close(to64(o), o_ref, "O")
     assert_bf16_close(to64(lse), lse_ref, "LSE")
+
+
+def _draw_paged_cases(n, seed=9100):
+    rng = random.Random(seed)
+    cases = []
+    for _ in range(n):
+        H = rng.randint(1, 16)
+        Hkv = rng.choice([h for h in range(1, H + 1) if H % h == 0])
+        B = rng.randint(1, 4)
+        lens = [rng.choice([0, rng.randint(1, 40), rng.randint(1, 1500)]) for _ in range(B)]
+        cases.append((B, H, Hkv, rng.choice([32, 64, 128, 256]), tuple(lens), rng.choice([64, 128]),
+                      rng.choice([0, 0, 1, rng.randint(1, 20)])))
+    return cases
+
+
+@pytest.mark.parametrize("B,H,Hkv,ps,lens,d,splits", _draw_paged_cases(8))
+def test_random_shape_paged_decode(B, H, Hkv, ps, lens, d, splits):
+    fa = _fa()
+    g = torch.Generator().manual_seed(9200 + ps + sum(lens))
+    n_pg = [-(-n // ps) for n in lens]
+    pool = sum(n_pg) + 3
+    max_pages = max(max(n_pg), 1)
+    slots = torch.randperm(pool, generator=g).tolist()
+    q = torch.randn((B, H, 1, d), generator=g).to(torch.bfloat16)
+    kp = torch.randn((pool, Hkv, ps, d), generator=g).to(torch.bfloat16)
+    vp = torch.randn((pool, Hkv, ps, d), generator=g).to(torch.bfloat16)
+    table = torch.full((B, max_pages), -1, dtype=torch.int32)
+    i = 0
+    for b in range(B):
+        for j in range(n_pg[b]):
+            table[b, j] = slots[i]
+            i += 1
+    sl = torch.tensor(lens, dtype=torch.int32)
+    scale = 1.0 / math.sqrt(d)
+    say(f"sweep paged decode B{B} H{H} Hkv{Hkv} page{ps} lens{lens} d{d} splits={splits}")
+    o_ref, lse_ref = ref_decode_paged(to64(q), to64(kp), to64(vp), table.numpy(), sl.numpy(), scale)
+    o, lse = fa.decode_paged(q.to(DEV), kp.to(DEV), vp.to(DEV), table.to(DEV), sl.to(DEV), scale=scale,
+                             num_splits=min(splits, max_pages * ps))
+    torch.cuda.synchronize()
+    assert_bf16_close(to64(o), o_ref, "O")
+    assert_bf16_close(to64(lse), lse_ref, "LSE")
+
+
+def _draw_fp8_cases(n, seed=9300):
+    rng = random.Random(seed)
+    cases = []
+    for _ in range(n):
+        H = rng.randint(1, 6)
+        Hkv = rng.choice([h for h in range(1, H + 1) if H % h == 0])
+        cases.append((rng.randint(1, 2), H, Hkv, 64 * rng.randint(1, 8), rng.choice([64, 128]), rng.random() < 0.6))
+    return cases
+
+
+@pytest.mark.parametrize("B,H,Hkv,N,d,causal", _draw_fp8_cases(8))
+def test_random_shape_fp8_forward(B, H, Hkv, N, d, causal):
+    from test_gpu_fp8 import _check, _codes
+    fa = _fa()
+    q8, k8, vt8, qs, ks, vs = W.make_fp8(B, H, Hkv, N, d, seed=9400 + N + H, device=DEV)
+    scale = 1.0 / math.sqrt(d)
+    say(f"sweep fp8 fwd B{B} H{H} Hkv{Hkv} N{N} d{d} causal={causal}")
+    o, lse = fa.attention_fp8(q8, k8, vt8, qs, ks, vs, is_causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    _check(o.double().cpu().numpy(), lse.double().cpu().numpy(),
+           (_codes(q8), _codes(k8), _codes(vt8), qs, ks, vs), causal, scale, True)
