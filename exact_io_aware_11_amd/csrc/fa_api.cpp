@@ -42,7 +42,7 @@ constexpr int kMaxSplits = 256;
 
 int auto_splits(int B, int H, int Hkv, int L) {
     long long units, target, min_keys, max_s;
-    if (fa::decode_group_path(H, Hkv)) {
+    if (fa::decode_group_path(B, H, Hkv)) {
         // grouped kernel: one wave per (b, cache head, chunk), four per
         // workgroup and one workgroup per CU (its tiles fill the LDS): aim
         // for ~1024 units, one round over the chip (measured better than two
@@ -53,6 +53,15 @@ int auto_splits(int B, int H, int Hkv, int L) {
         target = 1024;
         min_keys = 64;
         max_s = 64;
+    } else if (fa::decode_small_group(B, H, Hkv) != 0) {
+        // small-group kernel: one workgroup per (b, cache head, chunk); about
+        // 1024 workgroups, chunks of at least 256 keys, at most 32 chunks
+        // (measured at B1-B64, Hkv 8 and 16, L = 8192: within 5% of the best
+        // forced split count everywhere but B16 Hkv8 at 2%)
+        units = (long long)B * Hkv;
+        target = 1024;
+        min_keys = 256;
+        max_s = 32;
     } else {
         // per-head kernel: at least ~4096 workgroups so every CU holds
         // several, with chunks of 512 keys or more (shorter chunks measured

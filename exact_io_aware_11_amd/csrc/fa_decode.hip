@@ -17,8 +17,9 @@
 // lanes and waves are merged with the same rule, and the chunk writes its
 // normalised output o_s and its log-sum-exp lse_s.
 //
-// Phase 1, grouped kernel (decode_group_kernel; 2 <= H/Hkv <= 32): see its
-// own comment below.
+// Phase 1, grouped kernels (2 <= H/Hkv <= 32; the choice between them is
+// made by decode_small_group): decode_small_group_kernel for groups of 2 and
+// 4, decode_group_kernel (MFMA) for the rest; see their own comments below.
 //
 // Phase 2 (merge kernel): M = max_s lse_s, lse = M + ln sum_s exp(lse_s - M),
 // O = sum_s exp(lse_s - lse) o_s, the online-softmax rescaling applied to
@@ -213,6 +214,237 @@ decode_split_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ Kc,
         const size_t pidx = (size_t)bh * S + s;
         Opart[pidx * D + tid] = (ll > 0.f) ? oo[0] / ll : 0.f;
         if (tid == 0) LSEpart[pidx] = (ll > 0.f) ? (mm + __log2f(ll)) * kLn2 : -INFINITY;
+    }
+}
+
+// v += (v moved across the lanes of its row by the DPP control CTL), for
+// every element of an array
+template <int CTL, int N>
+__device__ __forceinline__ void dpp_step_n(float* v) {
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+        v[i] += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v[i]), CTL, 0xF, 0xF, true));
+}
+
+// ---------------------------------------------------------------------------
+// Grouped-query decode for small groups (GH = H/Hkv query heads per cache
+// head, GH <= 4): the per-head kernel's streaming layout and online softmax,
+// with the GH query heads of a cache head carried by the same lanes, so each
+// cached key and value is loaded once for the group.  One workgroup per
+// (batch, cache head, chunk).  The scores are bf16 dot2 products of the key
+// with the unscaled query (a product of two bf16 values is exact in fp32),
+// reduced over the key's lanes; scale*log2(e) (c > 0) is applied inside the
+// exponent's FMA.  The value update is a bf16 dot2 over pairs of keys.
+// ---------------------------------------------------------------------------
+constexpr float kLazyRescale = 8.f;   // log2 of the largest term the sums may hold
+template <int D, int GH, bool PAGED>
+__global__ void __launch_bounds__(DEC_THREADS)
+decode_small_group_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ Kc,
+                          const __bf16* __restrict__ Vc, float* __restrict__ Opart,
+                          float* __restrict__ LSEpart, int L, int S, int chunk, float c, Paging pg) {
+    constexpr int LPK = D / 8;
+    constexpr int KPL = 64 / LPK;
+    constexpr int U = DEC_UNROLL;
+    constexpr int STEP = KPL * U;
+
+    __shared__ float sh_o[DEC_WAVES][GH][D];
+    __shared__ float sh_m[DEC_WAVES][GH], sh_l[DEC_WAVES][GH];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, w = tid >> 6;
+    const int slot = lane / LPK, dc = lane % LPK;
+    const int s = blockIdx.x % S;
+    const int gkv = blockIdx.x / S;         // b * Hkv + cache head
+    int Lb = L;
+    int b = 0, hk = 0;
+    if constexpr (PAGED) {
+        b = gkv / pg.Hkv;
+        hk = gkv % pg.Hkv;
+        Lb = min(max(pg.seq_lens[b], 0), L);
+    }
+    const int k_begin = s * chunk;
+    const int k_end = min(Lb, k_begin + chunk);
+
+    auto row_of = [&](int key, int page, bool& ok) __attribute__((always_inline)) -> size_t {
+        if constexpr (PAGED) {
+            ok = page >= 0 && page < pg.num_pages;
+            const size_t prow = (((size_t)(ok ? page : 0) * pg.Hkv + hk) << pg.ps_log2) +
+                                (size_t)(key & ((1 << pg.ps_log2) - 1));
+            return prow * D;
+        } else {
+            ok = true;
+            return ((size_t)gkv * L + key) * D;
+        }
+    };
+    auto fetch_pages = [&](int base, int* pgs) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int key = base + u * KPL + slot;
+            pgs[u] = (key < k_end) ? pg.block_table[(size_t)b * pg.max_pages + (key >> pg.ps_log2)] : -1;
+        }
+    };
+
+    // the GH query rows (query head gkv*GH + g), 8 packed bf16 dims per lane
+    bf16x2 qp[GH][4];
+#pragma unroll
+    for (int g = 0; g < GH; ++g) {
+        const uint4 u = *reinterpret_cast<const uint4*>(Q + ((size_t)gkv * GH + g) * D + 8 * dc);
+        qp[g][0] = __builtin_bit_cast(bf16x2, u.x);
+        qp[g][1] = __builtin_bit_cast(bf16x2, u.y);
+        qp[g][2] = __builtin_bit_cast(bf16x2, u.z);
+        qp[g][3] = __builtin_bit_cast(bf16x2, u.w);
+    }
+
+    const __bf16* Kl = Kc + 8 * dc;
+    const __bf16* Vl = Vc + 8 * dc;
+
+    float m[GH], l[GH], o[GH][8];
+#pragma unroll
+    for (int g = 0; g < GH; ++g) {
+        m[g] = -INFINITY;
+        l[g] = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) o[g][j] = 0.f;
+    }
+
+    int pg_next[U] = {};
+    if constexpr (PAGED) fetch_pages(k_begin + w * STEP, pg_next);
+    for (int base = k_begin + w * STEP; base < k_end; base += DEC_WAVES * STEP) {
+        uint4 kr[U], vr[U];
+        bool live[U];
+        int pg_cur[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) pg_cur[u] = pg_next[u];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int key = base + u * KPL + slot;
+            kr[u] = make_uint4(0, 0, 0, 0);
+            vr[u] = kr[u];
+            live[u] = false;
+            if (key < k_end) {
+                const size_t r = row_of(key, pg_cur[u], live[u]);
+                if (live[u]) {
+                    kr[u] = load_stream16(Kl + r);
+                    vr[u] = load_stream16(Vl + r);
+                }
+            }
+        }
+        if constexpr (PAGED) fetch_pages(base + DEC_WAVES * STEP, pg_next);
+        // scores: the dot2 partial sums of every (head, key) first, then the
+        // reductions over the key's lanes one step at a time across all of
+        // them, so consecutive DPP adds are independent
+        float x[GH][U];
+#pragma unroll
+        for (int g = 0; g < GH; ++g)
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                float dot = 0.f;
+                dot = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, kr[u].x), qp[g][0], dot, false);
+                dot = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, kr[u].y), qp[g][1], dot, false);
+                dot = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, kr[u].z), qp[g][2], dot, false);
+                x[g][u] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, kr[u].w), qp[g][3], dot, false);
+            }
+        dpp_step_n<0xB1, GH * U>(&x[0][0]);      // [1,0,3,2]
+        dpp_step_n<0x4E, GH * U>(&x[0][0]);      // [2,3,0,1]
+        dpp_step_n<0x141, GH * U>(&x[0][0]);     // half mirror
+        if constexpr (LPK >= 16) dpp_step_n<0x140, GH * U>(&x[0][0]);    // row mirror
+        if constexpr (LPK == 32) {     // d = 256: two rows per key
+#pragma unroll
+            for (int g = 0; g < GH; ++g)
+#pragma unroll
+                for (int u = 0; u < U; ++u) x[g][u] += __shfl_xor(x[g][u], 16);
+        }
+        float mxs[GH], mu[GH];
+        bool grow = false;
+#pragma unroll
+        for (int g = 0; g < GH; ++g) {
+            float mx = -INFINITY;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                x[g][u] = live[u] ? x[g][u] : -INFINITY;
+                mx = fmaxf(mx, x[g][u]);
+            }
+            mxs[g] = mx * c;
+            grow = grow || mxs[g] > m[g] + kLazyRescale;
+        }
+        // m is a reference value, raised only when a score exceeds it by more
+        // than 2^kLazyRescale (decided per wave, so the branch is uniform); l
+        // and o are sums of 2^(c*x - m) for any such reference
+        if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+#pragma unroll
+            for (int g = 0; g < GH; ++g) {
+                const float mn = fmaxf(m[g], mxs[g]);
+                const float alpha = exp2_fast(m[g] - ((mn == -INFINITY) ? 0.f : mn));
+                m[g] = mn;
+                l[g] *= alpha;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) o[g][j] *= alpha;
+            }
+        }
+#pragma unroll
+        for (int g = 0; g < GH; ++g) mu[g] = (m[g] == -INFINITY) ? 0.f : m[g];
+        // values, two keys at a time: v_perm gathers dim j of keys u and u+1
+        // into one bf16 pair, p of the two keys is packed to bf16 (as the
+        // PV products of the forward use it) and o_j += dot2(p, v_j); the
+        // running sum adds the same rounded p
+#pragma unroll
+        for (int u = 0; u < U; u += 2) {
+            const uint32_t* v0 = reinterpret_cast<const uint32_t*>(&vr[u]);
+            const uint32_t* v1 = reinterpret_cast<const uint32_t*>(&vr[u + 1]);
+            bf16x2 vv[8];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                vv[2 * j] = __builtin_bit_cast(bf16x2, __builtin_amdgcn_perm(v1[j], v0[j], 0x05040100u));
+                vv[2 * j + 1] = __builtin_bit_cast(bf16x2, __builtin_amdgcn_perm(v1[j], v0[j], 0x07060302u));
+            }
+#pragma unroll
+            for (int g = 0; g < GH; ++g) {
+                const uint32_t pp = pack_bf16x2(exp2_fast(fmaf(x[g][u], c, -mu[g])),
+                                                exp2_fast(fmaf(x[g][u + 1], c, -mu[g])));
+                l[g] = sum_bf16x2(pp, l[g]);
+                const bf16x2 pb = __builtin_bit_cast(bf16x2, pp);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) o[g][j] = __builtin_amdgcn_fdot2_f32_bf16(vv[j], pb, o[g][j], false);
+            }
+        }
+    }
+
+    // merge the KPL key slots of the wave, then the waves through LDS
+#pragma unroll
+    for (int off = LPK; off < 64; off <<= 1) {
+#pragma unroll
+        for (int g = 0; g < GH; ++g) {
+            const float mb = __shfl_xor(m[g], off), lb = __shfl_xor(l[g], off);
+            float ob[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) ob[j] = __shfl_xor(o[g][j], off);
+            merge_state<8>(m[g], l[g], o[g], mb, lb, ob);
+        }
+    }
+    if (slot == 0) {
+#pragma unroll
+        for (int g = 0; g < GH; ++g) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) sh_o[w][g][8 * dc + j] = o[g][j];
+            if (dc == 0) {
+                sh_m[w][g] = m[g];
+                sh_l[w][g] = l[g];
+            }
+        }
+    }
+    __syncthreads();
+    for (int i = tid; i < GH * D; i += DEC_THREADS) {
+        const int g = i / D, dd = i % D;
+        float mm = sh_m[0][g], ll = sh_l[0][g];
+        float oo[1] = {sh_o[0][g][dd]};
+#pragma unroll
+        for (int ww = 1; ww < DEC_WAVES; ++ww) {
+            const float ob[1] = {sh_o[ww][g][dd]};
+            merge_state<1>(mm, ll, oo, sh_m[ww][g], sh_l[ww][g], ob);
+        }
+        const size_t pidx = ((size_t)gkv * GH + g) * S + s;
+        Opart[pidx * D + dd] = (ll > 0.f) ? oo[0] / ll : 0.f;
+        if (dd == 0) LSEpart[pidx] = (ll > 0.f) ? (mm + __log2f(ll)) * kLn2 : -INFINITY;
     }
 }
 
@@ -513,7 +745,18 @@ hipError_t launch_d(const DecodeArgs& a) {
     const int BH = a.B * a.H;
     const int G = a.H / a.Hkv;
     hipStream_t st = (hipStream_t)a.stream;
-    if (decode_group_path(a.H, a.Hkv)) {
+    if (decode_small_group(a.B, a.H, a.Hkv) != 0) {
+        const dim3 grid((unsigned)(a.B * a.Hkv * a.splits));
+        if (G == 2) {
+            hipLaunchKernelGGL((decode_small_group_kernel<D, 2, PAGED>), grid, dim3(DEC_THREADS), 0, st,
+                               (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, a.o_part,
+                               a.lse_part, a.L, a.splits, a.chunk, a.scale * kLog2e, a.paging);
+        } else {
+            hipLaunchKernelGGL((decode_small_group_kernel<D, 4, PAGED>), grid, dim3(DEC_THREADS), 0, st,
+                               (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, a.o_part,
+                               a.lse_part, a.L, a.splits, a.chunk, a.scale * kLog2e, a.paging);
+        }
+    } else if (decode_group_path(a.B, a.H, a.Hkv)) {
         const int units = a.B * a.Hkv * a.splits;
         constexpr int WV = dg_waves<D>();
         hipLaunchKernelGGL((decode_group_kernel<D, PAGED>), dim3((unsigned)((units + WV - 1) / WV)),

@@ -86,9 +86,6 @@ struct DecodeArgs {
                      // paged: L = max_pages * page_size
 };
 
-// Decode takes the grouped-query kernel (each cache head read once for all
-// the query heads sharing it) when 2 <= H/Hkv <= kDecodeMaxGroup; otherwise
-// the per-query-head kernel.
 // Backward with grouped heads: the dK/dV kernel normally sums the G query
 // heads of a K/V head inside one workgroup (one per K/V head and 128-key
 // tile).  When that grid is small -- below two workgroups per CU -- the
@@ -105,10 +102,25 @@ inline bool bwd_split_heads(int B, int H, int Hkv, int N) {
     return nkt * B * Hkv < kBwdSplitBelow;
 }
 
+// Decode kernels by group size G = H/Hkv:
+//  - G = 2, and G = 4 over at least 64 (batch, cache head) pairs: the
+//    small-group kernel (the per-head kernel's streaming layout with the
+//    group's heads on the same lanes).  Measured on MI355X at L = 8192 it
+//    streams 6.3-6.9 TB/s from batch 16 up, against 5.5-6.0 for the MFMA
+//    grouped kernel; with G = 4 at batch 1-4 and 8 cache heads the MFMA
+//    kernel's shorter chunks were 1-11% faster.
+//  - other G in [2, 32]: the MFMA grouped kernel;
+//  - G = 1 or G > 32: the per-query-head kernel.
 constexpr int kDecodeMaxGroup = 32;
-inline bool decode_group_path(int H, int Hkv) {
+inline int decode_small_group(int B, int H, int Hkv) {
     const int G = H / Hkv;
-    return G >= 2 && G <= kDecodeMaxGroup;
+    if (G == 2) return 2;
+    if (G == 4 && (long long)B * Hkv >= 64) return 4;
+    return 0;
+}
+inline bool decode_group_path(int B, int H, int Hkv) {
+    const int G = H / Hkv;
+    return G >= 2 && G <= kDecodeMaxGroup && decode_small_group(B, H, Hkv) == 0;
 }
 
 hipError_t launch_fwd(const FwdArgs& a);

@@ -260,9 +260,14 @@ def test_decode_split_plan_grouped():
         parts = B * H * s
         assert fa.fa_decode_workspace_bytes(B, H, Hkv, L, 128, 0) == \
             ((parts * 128 * 4 + 255) // 256) * 256 + parts * 4
-    # 512 (batch, cache head) units of 8192 keys: 2 chunks of 4096
+    # small-group kernel (groups of 2; of 4 from 64 (batch, cache head)
+    # pairs): about 1024 workgroups, chunks of 256 keys or more, at most 32
     assert fa.fa_decode_num_splits(64, 32, 8, 8192, 128) == 2
-    # batch 1, 8 cache heads: chunks down to 64 keys, at most 64 of them
+    assert fa.fa_decode_num_splits(16, 32, 8, 8192, 128) == 8
+    assert fa.fa_decode_num_splits(1, 32, 16, 8192, 128) == 32
+    assert fa.fa_decode_num_splits(1, 32, 16, 1000, 128) == 4
+    # MFMA grouped kernel, batch 1, 8 cache heads (groups of 4): chunks down
+    # to 64 keys, at most 64 of them
     assert fa.fa_decode_num_splits(1, 32, 8, 4096, 128) == 64
     assert fa.fa_decode_num_splits(1, 32, 8, 16384, 128) == 64
     assert fa.fa_decode_num_splits(1, 32, 8, 1000, 128) == 16

@@ -455,8 +455,13 @@ def test_bwd_gqa_deterministic():
 
 
 GQA_DEC = [
-    # (B, H, Hkv, L, d): groups of 2..32 take the grouped kernel; G = 1 and
-    # G > 32 the per-head kernel
+    # (B, H, Hkv, L, d): groups of 2, and of 4 over at least 64 (batch, cache
+    # head) pairs, take the small-group kernel; other groups up to 32 the MFMA
+    # grouped kernel; G = 1 and G > 32 the per-head kernel
+    (8, 32, 8, 700, 64),
+    (4, 16, 8, 513, 256),
+    (2, 4, 2, 65, 64),
+    (16, 8, 4, 1029, 128),
     (3, 8, 2, 1000, 128),
     (2, 8, 1, 777, 64),
     (1, 32, 8, 4097, 128),
@@ -481,6 +486,29 @@ def test_decode_gqa(B, H, Hkv, L, d):
             continue
         say(f"fa_decode gqa B{B} H{H} Hkv{Hkv} L{L} d{d} splits={s}")
         o, lse = fa.decode(q, kc, vc, scale=scale, num_splits=s)
+        torch.cuda.synchronize()
+        assert_bf16_close(to64(o), o_ref, f"O splits={s}")
+        assert_bf16_close(to64(lse), lse_ref, f"LSE splits={s}")
+
+
+@pytest.mark.parametrize("B,H,Hkv,L,d,rising", [(16, 8, 4, 3000, 128, True), (8, 32, 8, 1500, 64, True),
+                                                  (16, 8, 4, 3000, 128, False)])
+def test_decode_small_groups_with_drifting_scores(B, H, Hkv, L, d, rising):
+    # keys carry a common offset that ramps over the cache and every query a
+    # positive mean, so the scores drift by about +-3*sqrt(d) along the keys:
+    # rising, the small-group kernel's reference maximum is raised many times
+    # inside one chunk; falling, the early keys dominate
+    fa = _fa()
+    g = torch.Generator().manual_seed(4350 + L + H)
+    q = (torch.randn((B, H, 1, d), generator=g) + 1.0).to(torch.bfloat16)
+    ramp = torch.linspace(-3.0, 3.0, L) if rising else torch.linspace(3.0, -3.0, L)
+    kc = (torch.randn((B, Hkv, L, d), generator=g) + ramp[:, None]).to(torch.bfloat16)
+    vc = torch.randn((B, Hkv, L, d), generator=g).to(torch.bfloat16)
+    scale = 1.0 / math.sqrt(d)
+    o_ref, lse_ref = ref_decode(to64(q), to64(kc), to64(vc), scale)
+    for s in (0, 1, 3):
+        say(f"fa_decode drifting scores B{B} H{H} Hkv{Hkv} L{L} d{d} rising={rising} splits={s}")
+        o, lse = fa.decode(q.to(DEV), kc.to(DEV), vc.to(DEV), scale=scale, num_splits=s)
         torch.cuda.synchronize()
         assert_bf16_close(to64(o), o_ref, f"O splits={s}")
         assert_bf16_close(to64(lse), lse_ref, f"LSE splits={s}")
@@ -531,8 +559,11 @@ def _paged_inputs(B, H, Hkv, ps, lens, d, seed, extra_pages=5):
 
 
 PAGED = [
-    # (B, H, Hkv, page_size, lens, d): grouped kernel for 2 <= H/Hkv <= 32,
+    # (B, H, Hkv, page_size, lens, d): grouped kernels for 2 <= H/Hkv <= 32
+    # (the small-group one for groups of 2, and of 4 from B*Hkv = 64),
     # per-head kernel otherwise
+    (8, 32, 8, 32, [100, 0, 1, 33, 257, 64, 500, 31], 128),
+    (3, 8, 4, 64, [300, 129, 2], 64),
     (3, 8, 2, 32, [1000, 1, 33], 128),
     (2, 8, 8, 64, [700, 64], 128),
     (4, 32, 8, 256, [4097, 0, 31, 2048], 128),
