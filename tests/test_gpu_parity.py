@@ -462,6 +462,7 @@ GQA_DEC = [
     (4, 16, 8, 513, 256),
     (2, 4, 2, 65, 64),
     (16, 8, 4, 1029, 128),
+    (8, 32, 8, 300, 256),
     (3, 8, 2, 1000, 128),
     (2, 8, 1, 777, 64),
     (1, 32, 8, 4097, 128),
@@ -564,6 +565,8 @@ PAGED = [
     # per-head kernel otherwise
     (8, 32, 8, 32, [100, 0, 1, 33, 257, 64, 500, 31], 128),
     (3, 8, 4, 64, [300, 129, 2], 64),
+    (16, 16, 4, 64, [70, 0, 1, 640, 63, 64, 65, 300, 2, 129, 31, 500, 7, 256, 1000, 33], 64),
+    (2, 4, 2, 32, [300, 77], 256),
     (3, 8, 2, 32, [1000, 1, 33], 128),
     (2, 8, 8, 64, [700, 64], 128),
     (4, 32, 8, 256, [4097, 0, 31, 2048], 128),

@@ -88,6 +88,25 @@ def test_random_shape_decode(B, H, Hkv, L, d, splits):
     assert_bf16_close(to64(lse), lse_ref, "LSE")
 
 
+def _draw_small_group_cases(n, seed=9600):
+    # groups of 2 or 4 with enough (batch, cache head) pairs for the
+    # small-group decode kernel (B * Hkv >= 64 for groups of 4)
+    rng = random.Random(seed)
+    cases = []
+    for _ in range(n):
+        G = rng.choice([2, 4])
+        Hkv = rng.choice([4, 8, 16])
+        B = max(rng.randint(1, 8), -(-64 // Hkv)) if G == 4 else rng.randint(1, 8)
+        cases.append((B, G * Hkv, Hkv, rng.randint(1, 1500), rng.choice([64, 128, 256]),
+                      rng.choice([0, 0, 1, rng.randint(1, 40)])))
+    return cases
+
+
+@pytest.mark.parametrize("B,H,Hkv,L,d,splits", _draw_small_group_cases(8))
+def test_random_shape_small_group_decode(B, H, Hkv, L, d, splits):
+    test_random_shape_decode(B, H, Hkv, L, d, splits)
+
+
 def _draw_paged_cases(n, seed=9100):
     rng = random.Random(seed)
     cases = []
