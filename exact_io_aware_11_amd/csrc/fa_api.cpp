@@ -40,7 +40,7 @@ fa_status_t from_hip(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP
 
 constexpr int kMaxSplits = 256;
 
-int auto_splits(int B, int H, int Hkv, int L) {
+int auto_splits(int B, int H, int Hkv, int L, bool paged) {
     long long units, target, min_keys, max_s;
     if (fa::decode_group_path(B, H, Hkv)) {
         // grouped kernel: one wave per (b, cache head, chunk), four per
@@ -55,11 +55,13 @@ int auto_splits(int B, int H, int Hkv, int L) {
         max_s = 64;
     } else if (fa::decode_small_group(B, H, Hkv) != 0) {
         // small-group kernel: one workgroup per (b, cache head, chunk); about
-        // 1024 workgroups, chunks of at least 256 keys, at most 32 chunks
-        // (measured at B1-B64, Hkv 8 and 16, L = 8192: within 5% of the best
-        // forced split count everywhere but B16 Hkv8 at 2%)
+        // 512 workgroups, chunks of at least 256 keys, at most 32 chunks
+        // (measured at B1-B64, groups of 2-4, L = 8192: within 3% of the best
+        // forced split count).  Paged: about 1024 workgroups, which hide the
+        // block-table lookups better (B64 H32 Hkv8 with 64-token pages: 6.39
+        // TB/s with 2 splits, 6.11 with 1).
         units = (long long)B * Hkv;
-        target = 1024;
+        target = paged ? 1024 : 512;
         min_keys = 256;
         max_s = 32;
     } else {
@@ -185,14 +187,17 @@ int fa_decode_num_splits(int B, int H, int Hkv, int L, int d) {
     (void)d;
     if (!dims_ok(B, H, L) || !kv_ok(H, Hkv)) return 1;
     int splits, chunk;
-    split_plan(L, auto_splits(B, H, Hkv, L), splits, chunk);
+    split_plan(L, auto_splits(B, H, Hkv, L, false), splits, chunk);
     return splits;
 }
 
 size_t fa_decode_workspace_bytes(int B, int H, int Hkv, int L, int d, int num_splits) {
     if (!dims_ok(B, H, L) || !kv_ok(H, Hkv) || d < 1 || num_splits < 0 || !total_ok(B, H, L, d)) return 0;
     int splits, chunk;
-    split_plan(L, num_splits == 0 ? auto_splits(B, H, Hkv, L) : (num_splits > L ? L : num_splits), splits, chunk);
+    // num_splits = 0: room for the automatic plans of both fa_decode and
+    // fa_decode_paged (the paged one never has fewer splits)
+    split_plan(L, num_splits == 0 ? auto_splits(B, H, Hkv, L, true) : (num_splits > L ? L : num_splits), splits,
+               chunk);
     const size_t parts = (size_t)B * H * splits;
     const size_t o_bytes = parts * (size_t)d * sizeof(float);
     return ((o_bytes + 255) & ~(size_t)255) + parts * sizeof(float);
@@ -212,7 +217,7 @@ fa_status_t fa_decode(const void* q, const void* k_cache, const void* v_cache, v
     if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
     if (!aligned16(workspace)) return FA_ERR_ALIGN;
     int splits, chunk;
-    split_plan(L, num_splits == 0 ? auto_splits(B, H, Hkv, L) : num_splits, splits, chunk);
+    split_plan(L, num_splits == 0 ? auto_splits(B, H, Hkv, L, false) : num_splits, splits, chunk);
     const size_t parts = (size_t)B * H * splits;
     float* o_part = static_cast<float*>(workspace);
     float* lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) +
@@ -243,7 +248,7 @@ fa_status_t fa_decode_paged(const void* q, const void* k_pool, const void* v_poo
     if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
     if (!aligned16(workspace)) return FA_ERR_ALIGN;
     int splits, chunk;
-    split_plan(L, num_splits == 0 ? auto_splits(B, H, Hkv, L) : num_splits, splits, chunk);
+    split_plan(L, num_splits == 0 ? auto_splits(B, H, Hkv, L, true) : num_splits, splits, chunk);
     const size_t parts = (size_t)B * H * splits;
     float* o_part = static_cast<float*>(workspace);
     float* lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) +

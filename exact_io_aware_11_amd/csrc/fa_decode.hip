@@ -18,7 +18,7 @@
 // normalised output o_s and its log-sum-exp lse_s.
 //
 // Phase 1, grouped kernels (2 <= H/Hkv <= 32; the choice between them is
-// made by decode_small_group): decode_small_group_kernel for groups of 2 and
+// made by decode_small_group): decode_small_group_kernel for groups of 2 to
 // 4, decode_group_kernel (MFMA) for the rest; see their own comments below.
 //
 // Phase 2 (merge kernel): M = max_s lse_s, lse = M + ln sum_s exp(lse_s - M),
@@ -228,7 +228,7 @@ __device__ __forceinline__ void dpp_step_n(float* v) {
 
 // ---------------------------------------------------------------------------
 // Grouped-query decode for small groups (GH = H/Hkv query heads per cache
-// head, GH <= 4): the per-head kernel's streaming layout and online softmax,
+// head, GH = 2, 3 or 4): the per-head kernel's streaming layout and online softmax,
 // with the GH query heads of a cache head carried by the same lanes, so each
 // cached key and value is loaded once for the group.  One workgroup per
 // (batch, cache head, chunk).  The scores are bf16 dot2 products of the key
@@ -749,6 +749,10 @@ hipError_t launch_d(const DecodeArgs& a) {
         const dim3 grid((unsigned)(a.B * a.Hkv * a.splits));
         if (G == 2) {
             hipLaunchKernelGGL((decode_small_group_kernel<D, 2, PAGED>), grid, dim3(DEC_THREADS), 0, st,
+                               (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, a.o_part,
+                               a.lse_part, a.L, a.splits, a.chunk, a.scale * kLog2e, a.paging);
+        } else if (G == 3) {
+            hipLaunchKernelGGL((decode_small_group_kernel<D, 3, PAGED>), grid, dim3(DEC_THREADS), 0, st,
                                (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, a.o_part,
                                a.lse_part, a.L, a.splits, a.chunk, a.scale * kLog2e, a.paging);
         } else {

@@ -103,7 +103,7 @@ inline bool bwd_split_heads(int B, int H, int Hkv, int N) {
 }
 
 // Decode kernels by group size G = H/Hkv:
-//  - G = 2, and G = 4 over at least 64 (batch, cache head) pairs: the
+//  - G = 2 and 3, and G = 4 over at least 64 (batch, cache head) pairs: the
 //    small-group kernel (the per-head kernel's streaming layout with the
 //    group's heads on the same lanes).  Measured on MI355X at L = 8192 it
 //    streams 6.3-6.9 TB/s from batch 16 up, against 5.5-6.0 for the MFMA
@@ -114,7 +114,7 @@ inline bool bwd_split_heads(int B, int H, int Hkv, int N) {
 constexpr int kDecodeMaxGroup = 32;
 inline int decode_small_group(int B, int H, int Hkv) {
     const int G = H / Hkv;
-    if (G == 2) return 2;
+    if (G == 2 || G == 3) return G;
     if (G == 4 && (long long)B * Hkv >= 64) return 4;
     return 0;
 }

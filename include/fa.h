@@ -170,9 +170,10 @@ fa_status_t fa_bwd(const void* q, const void* k, const void* v,
 int fa_decode_num_splits(int B, int H, int Hkv, int L, int d);
 
 /*
- * fa_decode_workspace_bytes -- workspace of fa_decode: fp32 partial outputs
- * [B,H,S,d] and partial LSEs [B,H,S] for S splits (num_splits = 0 means the
- * library's choice).  Returns 0 if a size is < 1.
+ * fa_decode_workspace_bytes -- workspace of fa_decode and fa_decode_paged:
+ * fp32 partial outputs [B,H,S,d] and partial LSEs [B,H,S] for S splits
+ * (num_splits = 0: room for the library's choice of either call, which may
+ * differ between the two).  Returns 0 if a size is < 1.
  */
 size_t fa_decode_workspace_bytes(int B, int H, int Hkv, int L, int d, int num_splits);
 

@@ -257,13 +257,20 @@ def test_decode_split_plan_grouped():
         assert 1 <= s <= L
         chunk = -(-L // s)
         assert (s - 1) * chunk < L
-        parts = B * H * s
-        assert fa.fa_decode_workspace_bytes(B, H, Hkv, L, 128, 0) == \
-            ((parts * 128 * 4 + 255) // 256) * 256 + parts * 4
-    # small-group kernel (groups of 2; of 4 from 64 (batch, cache head)
-    # pairs): about 1024 workgroups, chunks of 256 keys or more, at most 32
-    assert fa.fa_decode_num_splits(64, 32, 8, 8192, 128) == 2
-    assert fa.fa_decode_num_splits(16, 32, 8, 8192, 128) == 8
+        # num_splits = 0 sizes room for both calls' automatic plans: at least
+        # fa_decode's, and exactly some split count's layout
+        auto = fa.fa_decode_workspace_bytes(B, H, Hkv, L, 128, 0)
+        assert auto >= fa.fa_decode_workspace_bytes(B, H, Hkv, L, 128, s)
+        assert any(auto == ((B * H * t * 128 * 4 + 255) // 256) * 256 + B * H * t * 4 for t in range(1, 257))
+    # small-group kernel (groups of 2 and 3; of 4 from 64 (batch, cache head)
+    # pairs): about 512 workgroups, chunks of 256 keys or more, at most 32
+    assert fa.fa_decode_num_splits(64, 32, 8, 8192, 128) == 1
+    # the paged call aims at about 1024 workgroups there (2 splits), and the
+    # automatic workspace has room for them
+    assert fa.fa_decode_workspace_bytes(64, 32, 8, 8192, 128, 0) == \
+        fa.fa_decode_workspace_bytes(64, 32, 8, 8192, 128, 2)
+    assert fa.fa_decode_num_splits(16, 32, 8, 8192, 128) == 4
+    assert fa.fa_decode_num_splits(4, 24, 8, 8192, 128) == 16
     assert fa.fa_decode_num_splits(1, 32, 16, 8192, 128) == 32
     assert fa.fa_decode_num_splits(1, 32, 16, 1000, 128) == 4
     # MFMA grouped kernel, batch 1, 8 cache heads (groups of 4): chunks down

@@ -455,7 +455,7 @@ def test_bwd_gqa_deterministic():
 
 
 GQA_DEC = [
-    # (B, H, Hkv, L, d): groups of 2, and of 4 over at least 64 (batch, cache
+    # (B, H, Hkv, L, d): groups of 2 and 3, and of 4 over at least 64 (batch, cache
     # head) pairs, take the small-group kernel; other groups up to 32 the MFMA
     # grouped kernel; G = 1 and G > 32 the per-head kernel
     (8, 32, 8, 700, 64),
@@ -463,6 +463,8 @@ GQA_DEC = [
     (2, 4, 2, 65, 64),
     (16, 8, 4, 1029, 128),
     (8, 32, 8, 300, 256),
+    (4, 24, 8, 1000, 128),
+    (2, 3, 1, 517, 256),
     (3, 8, 2, 1000, 128),
     (2, 8, 1, 777, 64),
     (1, 32, 8, 4097, 128),
@@ -561,12 +563,13 @@ def _paged_inputs(B, H, Hkv, ps, lens, d, seed, extra_pages=5):
 
 PAGED = [
     # (B, H, Hkv, page_size, lens, d): grouped kernels for 2 <= H/Hkv <= 32
-    # (the small-group one for groups of 2, and of 4 from B*Hkv = 64),
+    # (the small-group one for groups of 2 and 3, and of 4 from B*Hkv = 64),
     # per-head kernel otherwise
     (8, 32, 8, 32, [100, 0, 1, 33, 257, 64, 500, 31], 128),
     (3, 8, 4, 64, [300, 129, 2], 64),
     (16, 16, 4, 64, [70, 0, 1, 640, 63, 64, 65, 300, 2, 129, 31, 500, 7, 256, 1000, 33], 64),
     (2, 4, 2, 32, [300, 77], 256),
+    (3, 12, 4, 64, [500, 1, 130], 64),
     (3, 8, 2, 32, [1000, 1, 33], 128),
     (2, 8, 8, 64, [700, 64], 128),
     (4, 32, 8, 256, [4097, 0, 31, 2048], 128),
