@@ -228,13 +228,14 @@ __device__ __forceinline__ void dpp_step_n(float* v) {
 
 // ---------------------------------------------------------------------------
 // Grouped-query decode for small groups (GH = H/Hkv query heads per cache
-// head, GH = 2, 3 or 4): the per-head kernel's streaming layout and online softmax,
-// with the GH query heads of a cache head carried by the same lanes, so each
-// cached key and value is loaded once for the group.  One workgroup per
-// (batch, cache head, chunk).  The scores are bf16 dot2 products of the key
-// with the unscaled query (a product of two bf16 values is exact in fp32),
-// reduced over the key's lanes; scale*log2(e) (c > 0) is applied inside the
-// exponent's FMA.  The value update is a bf16 dot2 over pairs of keys.
+// head, GH = 2, 3 or 4): the per-head kernel's streaming layout and online
+// softmax, with the GH query heads of a cache head carried by the same lanes,
+// so each cached key and value is loaded once for the group.  One workgroup
+// per (batch, cache head, chunk).  The scores are bf16 dot2 products of the
+// key with the unscaled query (a product of two bf16 values is exact in
+// fp32), reduced over the key's lanes; scale*log2(e) (c > 0) is applied
+// inside the exponent's FMA.  The value update is a bf16 dot2 over pairs of
+// keys.
 // ---------------------------------------------------------------------------
 constexpr float kLazyRescale = 8.f;   // log2 of the largest term the sums may hold
 template <int D, int GH, bool PAGED>
