@@ -48,10 +48,13 @@ def _capture(fn):
     return g, out
 
 
-def test_decode_replays_in_a_graph():
+@pytest.mark.parametrize("Hkv", [8, 16])
+def test_decode_replays_in_a_graph(Hkv):
+    # Hkv = 8: groups of 4 at B*Hkv = 16 (MFMA grouped kernel); Hkv = 16:
+    # groups of 2 (small-group kernel)
     fa = _fa()
-    B, H, Hkv, L, d = 2, 32, 8, 1500, 128
-    q, kc, vc = W.make_gqa(B, H, Hkv, 1, d, "bf16", seed=7000, device=DEV, Nk=L)
+    B, H, L, d = 2, 32, 1500, 128
+    q, kc, vc = W.make_gqa(B, H, Hkv, 1, d, "bf16", seed=7000 + Hkv, device=DEV, Nk=L)
     qs = q.clone()
     say(f"graph: fa_decode B{B} H{H} Hkv{Hkv} L{L} d{d}")
     g, (o_g, lse_g) = _capture(lambda: fa.decode(qs, kc, vc))
