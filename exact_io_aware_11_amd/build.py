@@ -34,7 +34,6 @@ COMMON_FLAGS = [
 DEVICE_FLAGS = [
     f"--offload-arch={ARCH}",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-munsafe-fp-atomics",
 ]
 
 

@@ -15,18 +15,26 @@
  * ---------------------------------------
  *  - Every tensor pointer is a DEVICE pointer owned by the caller.  The
  *    library never allocates, frees or synchronises, and keeps no per-call
- *    state; it enqueues kernels on `stream` (a hipStream_t, NULL = the
- *    default stream) and returns at once.
+ *    state; it enqueues kernels on `stream` and returns at once.  `stream` is
+ *    a hipStream_t passed as void* (so that this header needs no HIP
+ *    include); NULL is the default stream.
  *  - Tensors are dense, row-major, [B, H, N, d] (d fastest).  LSE tensors
  *    are [B, H, N] float32 and hold the natural-log log-sum-exp of the
  *    scaled, masked scores of each query row.
+ *  - Grouped-query attention: every entry point takes Hkv, the number of K/V
+ *    heads, after H.  Hkv must divide H (FA_ERR_ARG otherwise); query head h
+ *    uses K/V head h / (H/Hkv).  Hkv = H is ordinary multi-head attention,
+ *    Hkv = 1 multi-query attention.
  *  - `scale` multiplies Q K^T; the pages' value is 1/sqrt(d).  It must be
  *    finite and > 0 (FA_ERR_ARG otherwise).
  *  - Causal masking (the decoder-only variant: Slovak page, section 5, and
  *    its is_causal usage example in section 6): key j is visible to query i
  *    iff j <= i (top-left aligned).
- *  - Supported: head dimension d in {64, 128}; any N >= 1 (ragged tails are
- *    masked inside the kernels); all offsets are 64-bit.
+ *  - Head dimension: d in {64, 128} for every entry point; d = 256 also for
+ *    the bf16 fa_fwd, fa_decode and fa_decode_paged (not for fp32 inputs,
+ *    fa_fwd_fp8 or fa_bwd).  Other values return FA_ERR_UNSUPPORTED.
+ *  - Any N >= 1 (ragged tails are masked inside the kernels); all offsets
+ *    are 64-bit.
  *  - Every pointer must be 16-byte aligned.
  *  - Errors: arguments are validated before anything is enqueued; on error
  *    nothing is launched and the status says why.  A failed launch returns

@@ -22,6 +22,4 @@ from .fp8 import (  # noqa: F401
     e4m3_decode,
     e4m3_round,
     fp8_dequantize,
-    fp8_p_rounding_sigma,
-    ref_fwd_fp8,
 )

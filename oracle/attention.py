@@ -195,12 +195,13 @@ def ref_fwd_tiled(q, k, v, causal: bool, scale: float, br: int, bc: int):
     """
     q64, k64, v64 = _f64(q), _f64(k), _f64(v)
     B, H, nq, _ = q64.shape
-    nk = k64.shape[2]
+    Hkv, nk = k64.shape[1], k64.shape[2]
     dv = v64.shape[-1]
     o = np.zeros((B, H, nq, dv), dtype=np.float64)
     lse = np.full((B, H, nq), -np.inf, dtype=np.float64)
     for b in range(B):
         for h in range(H):
+            g = kv_head(h, H, Hkv)
             for r0 in range(0, nq, br):
                 r1 = min(nq, r0 + br)
                 rows = np.arange(r0, r1)
@@ -209,7 +210,7 @@ def ref_fwd_tiled(q, k, v, causal: bool, scale: float, br: int, bc: int):
                 acc = np.zeros((r1 - r0, dv))
                 for c0 in range(0, nk, bc):
                     c1 = min(nk, c0 + bc)
-                    s = scale * (q64[b, h, r0:r1] @ k64[b, h, c0:c1].T)
+                    s = scale * (q64[b, h, r0:r1] @ k64[b, g, c0:c1].T)
                     if causal:
                         vis = np.arange(c0, c1)[None, :] <= rows[:, None]
                         s = np.where(vis, s, -np.inf)
@@ -220,7 +221,7 @@ def ref_fwd_tiled(q, k, v, causal: bool, scale: float, br: int, bc: int):
                     alpha = np.where(np.isfinite(m), np.exp(m - ref), 0.0)
                     p = np.exp(s - ref[:, None])
                     l = alpha * l + np.sum(p, axis=1)
-                    acc = alpha[:, None] * acc + p @ v64[b, h, c0:c1]
+                    acc = alpha[:, None] * acc + p @ v64[b, g, c0:c1]
                     m = m_new
                 live = l > 0
                 o[b, h, r0:r1] = np.where(live[:, None], acc / np.where(live, l, 1.0)[:, None], 0.0)

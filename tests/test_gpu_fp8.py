@@ -1,15 +1,16 @@
-"""GPU parity of the fp8 forward (fa_fwd_fp8) against the fp8 oracle.
+"""GPU parity of the fp8 forward (fa_fwd_fp8) against the exact oracle.
 
-Tolerances (derived in oracle/fp8.py and the design doc):
-* against the exact result of the fp8-valued inputs: RMS within the rounding
-  model sigma_p (plus the bf16 output rounding), and every element within the
-  worst-case bound max|V| (2^-4 + N 2^-17) (+ bf16 rounding);
-* against the method's own steps (ref_fwd_fp8, which rounds P exactly as the
-  kernel does): RMS within 0.35 sigma_p -- what is left are rare rounding
-  flips of P where the kernel's fp32 scores and the oracle's fp64 ones fall on
-  different sides of an e4m3 midpoint;
-* LSE: uses the unrounded row sum, so it matches the exact LSE to fp32
-  accuracy.
+The gate is the definition: ``ref_fwd`` of the oracle on the dequantised
+inputs.  Its tolerances come from the kernel's one rounding step (P rounded
+to e4m3 before the second product; the derivation is in tests/fp8_model.py):
+* RMS error over O within sigma_p, the rounding model's bound, combined with
+  the bf16 rounding of the output;
+* every element within the worst case max|V| (2^-4 + N 2^-17), plus the
+  output rounding (relative error 2^-4 of each weight, plus subnormal codes);
+* LSE: the kernel's row sum uses the unrounded probabilities, so the LSE
+  matches the exact one to fp32 accumulation error, 5e-4 relative.
+The distance to the kernel's own rounding recipe (``fp8_model.ref_fwd_fp8``)
+is printed as a diagnostic and is not a pass/fail criterion.
 """
 
 from __future__ import annotations
@@ -21,7 +22,8 @@ import pytest
 import torch
 
 import fa_workloads as W
-from oracle import fp8_dequantize, fp8_p_rounding_sigma, ref_fwd, ref_fwd_fp8
+from fp8_model import fp8_p_rounding_sigma, ref_fwd_fp8
+from oracle import fp8_dequantize, ref_fwd
 
 pytestmark = pytest.mark.gpu
 
@@ -42,7 +44,8 @@ def _codes(t):
 
 
 def _check(o, lse, args, causal, scale, out_bf16, heads=None):
-    """Compare kernel outputs (numpy, float64) with the exact and the method oracle."""
+    """Compare kernel outputs (numpy, float64) with the exact result; report the
+    distance to the kernel's rounding recipe."""
     q8, k8, vt8, qs, ks, vs = args
     if heads is not None:                     # sampled (b, h) pairs with their K/V heads
         H, Hkv = q8.shape[1], k8.shape[1]
@@ -63,7 +66,6 @@ def _check(o, lse, args, causal, scale, out_bf16, heads=None):
     say(f"  rms vs exact {rms_exact / sigma_p:.3f} sigma_p, vs the method {rms_method / sigma_p:.4f} sigma_p "
         f"(sigma_p {sigma_p:.2e}, bf16 output {sigma_out:.1e})")
     assert rms_exact <= math.sqrt(sigma_p ** 2 + sigma_out ** 2), (rms_exact, sigma_p, sigma_out)
-    assert rms_method <= 0.35 * sigma_p + 2.0 * sigma_out, (rms_method, sigma_p, sigma_out)
     n = k.shape[2]
     bound = np.max(np.abs(v)) * (2.0 ** -4 + n * 2.0 ** -17) + (2.0 ** -8 if out_bf16 else 1e-6) * np.abs(exact) + 1e-6
     assert np.all(np.abs(o - exact) <= bound)

@@ -19,7 +19,7 @@ import torch
 
 import fa_workloads as W
 from oracle import ref_bwd, ref_decode, ref_decode_paged, ref_fwd
-from parity_util import assert_bf16_close, assert_grad_close, to64
+from parity_util import assert_bf16_close, assert_grad_close, assert_lse_close, to64
 
 pytestmark = pytest.mark.gpu
 
@@ -67,7 +67,7 @@ def test_random_shape_forward_backward(B, H, Hkv, N, d, causal):
     torch.cuda.synchronize()
     o_ref, lse_ref = ref_fwd(to64(q), to64(k), to64(v), causal, scale)
     assert_bf16_close(to64(o), o_ref, "O")
-    assert_bf16_close(to64(lse), lse_ref, "LSE")
+    assert_lse_close(to64(lse), lse_ref, "LSE")
     rq, rk, rv = ref_bwd(to64(q), to64(k), to64(v), to64(do), causal, scale)
     assert_grad_close(to64(dq), rq, "dQ")
     assert_grad_close(to64(dk), rk, "dK")
@@ -85,7 +85,7 @@ def test_random_shape_decode(B, H, Hkv, L, d, splits):
     torch.cuda.synchronize()
     o_ref, lse_ref = ref_decode(to64(q), to64(kc), to64(vc), scale)
     assert_bf16_close(to64(o), o_ref, "O")
-    assert_bf16_close(to64(lse), lse_ref, "LSE")
+    assert_lse_close(to64(lse), lse_ref, "LSE")
 
 
 def _draw_small_group_cases(n, seed=9600):
@@ -145,7 +145,7 @@ def test_random_shape_paged_decode(B, H, Hkv, ps, lens, d, splits):
                              num_splits=min(splits, max_pages * ps))
     torch.cuda.synchronize()
     assert_bf16_close(to64(o), o_ref, "O")
-    assert_bf16_close(to64(lse), lse_ref, "LSE")
+    assert_lse_close(to64(lse), lse_ref, "LSE")
 
 
 def _draw_fp8_cases(n, seed=9300):

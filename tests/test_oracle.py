@@ -221,6 +221,16 @@ def pin_tiled_equals_naive(fwd, bwd):
                         o_t, l_t = ref_fwd_tiled(q, k, v, causal, 0.9, br, bc)
                         np.testing.assert_allclose(o_t, o_ref, atol=1e-12, rtol=0)
                         np.testing.assert_allclose(l_t, l_ref, atol=1e-12, rtol=0)
+    # with shared K/V heads the blockwise form reads each query head's own
+    # K/V head (groups of 2 and MQA), also for tiles that cut the rows
+    for (B, H, Hkv) in ((1, 4, 2), (2, 3, 1)):
+        q, k, v, _ = _gqa_inputs(70 + H, B, H, Hkv, 7, 3)
+        for causal in (False, True):
+            o_ref, l_ref = fwd(q, k, v, causal, 0.7)
+            for br, bc in ((1, 1), (3, 2), (7, 7), (2, 5)):
+                o_t, l_t = ref_fwd_tiled(q, k, v, causal, 0.7, br, bc)
+                np.testing.assert_allclose(o_t, o_ref, atol=1e-12, rtol=0)
+                np.testing.assert_allclose(l_t, l_ref, atol=1e-12, rtol=0)
 
 
 def _gqa_inputs(seed, B, H, Hkv, N, d):

@@ -1,12 +1,13 @@
-"""Pins of the fp8 oracle (oracle/fp8.py) against things other than itself.
+"""Pins of the fp8 oracle (oracle/fp8.py) and of the test-side rounding
+model (tests/fp8_model.py) against things other than themselves.
 
 * The e4m3 decoding and rounding against PyTorch's own float8_e4m3fn type
   (an independent implementation of the same OCP format).
-* The fp8 forward's online steps with the rounding of P switched off against
-  the exact attention definition (ref_fwd).
+* The model's online steps with the rounding of P switched off against the
+  exact attention definition (ref_fwd).
 * The rounding-noise model against the deviation the rounding actually
   causes, and its power to reject plausible mistakes (mutants planted in the
-  oracle on the CPU).
+  model on the CPU).
 """
 
 from __future__ import annotations
@@ -18,8 +19,10 @@ import pytest
 import torch
 
 import fa_workloads as W
-from oracle import e4m3_decode, e4m3_round, fp8_dequantize, fp8_p_rounding_sigma, ref_fwd, ref_fwd_fp8
+import fp8_model as M
 import oracle.fp8 as F8
+from fp8_model import fp8_p_rounding_sigma, ref_fwd_fp8
+from oracle import e4m3_decode, e4m3_round, fp8_dequantize, ref_fwd
 
 
 def _codes(t):
@@ -108,7 +111,7 @@ def test_fp8_noise_criterion_rejects_mutants(monkeypatch):
         r = real_round(t)
         return np.zeros_like(r) if calls["n"] % 8 == 3 else r
     monkeypatch.setattr(F8, "e4m3_round", drop_third_tile)
-    o_bad, _ = F8.ref_fwd_fp8(*args, True, scale)
+    o_bad, _ = M.ref_fwd_fp8(*args, True, scale)
     assert rms_of(o_bad) > 3.0 * sigma_p
 
     # 2. P rounded with two mantissa bits instead of three
@@ -118,5 +121,5 @@ def test_fp8_noise_criterion_rejects_mutants(monkeypatch):
         sp = np.exp2(np.maximum(e, -6.0) - 2.0)
         return np.sign(t) * np.round(a / sp) * sp
     monkeypatch.setattr(F8, "e4m3_round", coarse)
-    o_bad, _ = F8.ref_fwd_fp8(*args, True, scale)
+    o_bad, _ = M.ref_fwd_fp8(*args, True, scale)
     assert rms_of(o_bad) > 1.0 * sigma_p
