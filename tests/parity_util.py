@@ -5,15 +5,17 @@ Tolerances (stated for this method's outputs; the pages give none):
     for O and LSE;
   * fp32 inputs: max|x - x*| <= 1e-4;
   * gradients dQ, dK, dV: the same bounds applied to |g - g*| / max|g*|;
-  * LSE with bf16 inputs: |LSE - LSE*| <= 2.5e-3 + 2^-17 |LSE*|, derived from
+  * LSE with bf16 inputs: |LSE - LSE*| <= 4.5e-3 + 2^-17 |LSE*|, derived from
     the arithmetic rather than borrowed from O.  The kernels sum the same
-    bf16-rounded probabilities that enter P V; each has relative error at most
-    2^-9 and all are positive, so the row sum is off by a factor within
-    1 +- 2^-9, i.e. ln(1 + 2^-9) = 1.95e-3 in the LSE.  fp32 accumulation of
-    the sum (a lane chain of at most N/2 terms, N <= 16K: below 5e-4 relative)
-    and of the scores (exact bf16 products, d terms) add less than 5e-4 at
-    unit-variance inputs.  The relative term covers the fp32 rounding of the
-    running maximum and of m ln 2 + ln l for large |LSE|.
+    bf16-rounded probabilities that enter P V.  bf16 carries 8 significant
+    bits, so rounding to nearest has relative error at most 2^-8; all terms
+    are positive, so the row sum is off by a factor within 1 +- 2^-8, i.e. at
+    most ln(1 + 2^-8) = 3.90e-3 in the LSE (reached when one rounded term
+    dominates a row).  fp32 accumulation of the sum (a lane chain of at most
+    N/2 terms, N <= 16K: below 5e-4 relative) and of the scores (exact bf16
+    products, d terms) add less than 6e-4 at unit-variance inputs.  The
+    relative term covers the fp32 rounding of the running maximum and of
+    m ln 2 + ln l for large |LSE|.
 x* is the fp64 oracle evaluated on exactly the values the GPU received.
 """
 
@@ -23,7 +25,7 @@ import numpy as np
 
 BF16_MAX, BF16_MEAN = 2e-2, 2e-3
 FP32_MAX = 1e-4
-LSE_ABS, LSE_REL = 2.5e-3, 2.0 ** -17
+LSE_ABS, LSE_REL = 4.5e-3, 2.0 ** -17
 
 
 def to64(t) -> np.ndarray:
