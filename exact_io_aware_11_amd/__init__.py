@@ -7,8 +7,8 @@ no fallback: if the library is missing, importing this package fails.
 
 Entry points with the C names (raw pointers, sizes, stream handle):
 ``fa_fwd``, ``fa_fwd_fp8``, ``fa_bwd``, ``fa_bwd_workspace_bytes``, ``fa_decode``,
-``fa_decode_workspace_bytes``, ``fa_decode_num_splits``, ``fa_decode_paged``,
-``fa_status_string``.
+``fa_decode_workspace_bytes``, ``fa_decode_num_splits``, ``fa_decode_noalloc``,
+``fa_decode_paged``, ``fa_status_string``.
 
 Tensor-level helpers with the same semantics:
 ``attention(q, k, v, is_causal=False, scale=None, out_dtype=None) -> (o, lse)``
@@ -17,8 +17,10 @@ Tensor-level helpers with the same semantics:
 scale=None, out_dtype=None) -> (o, lse)`` on e4m3 inputs,
 ``attention_backward(q, k, v, o, lse, do, is_causal=False, scale=None)``
 ``-> (dq, dk, dv)`` and ``decode(q, k_cache, v_cache, scale=None,
-num_splits=0) -> (o, lse)`` and ``decode_paged(q, k_pool, v_pool, block_table,
-seq_lens, scale=None, num_splits=0) -> (o, lse)``.
+num_splits=0) -> (o, lse)``, ``decode_noalloc(q, k_cache, v_cache, o, lse,
+scale=None, num_splits=0)`` (writes the caller's o and lse, allocates nothing)
+and ``decode_paged(q, k_pool, v_pool, block_table, seq_lens, scale=None,
+num_splits=0) -> (o, lse)``.
 """
 
 from __future__ import annotations
@@ -29,15 +31,18 @@ import os
 
 __all__ = [
     "LIB_PATH", "FA_OK", "FA_ERR_NULL", "FA_ERR_ARG", "FA_ERR_UNSUPPORTED", "FA_ERR_ALIGN",
-    "FA_ERR_WORKSPACE", "FA_ERR_HIP", "FA_FP32", "FA_BF16", "FaError",
+    "FA_ERR_WORKSPACE", "FA_ERR_HIP", "FA_ERR_SCRATCH_LIMIT", "FA_NOALLOC_SCRATCH_BYTES", "FA_FP32", "FA_BF16",
+    "FaError",
     "fa_fwd", "fa_fwd_fp8", "fa_bwd", "fa_bwd_workspace_bytes", "fa_decode", "fa_decode_workspace_bytes",
-    "fa_decode_num_splits", "fa_decode_paged", "fa_status_string",
-    "attention", "attention_fp8", "attention_backward", "decode", "decode_paged", "lib",
+    "fa_decode_num_splits", "fa_decode_noalloc", "fa_decode_paged", "fa_status_string",
+    "attention", "attention_fp8", "attention_backward", "decode", "decode_noalloc", "decode_paged", "lib",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 
-FA_OK, FA_ERR_NULL, FA_ERR_ARG, FA_ERR_UNSUPPORTED, FA_ERR_ALIGN, FA_ERR_WORKSPACE, FA_ERR_HIP = range(7)
+(FA_OK, FA_ERR_NULL, FA_ERR_ARG, FA_ERR_UNSUPPORTED, FA_ERR_ALIGN, FA_ERR_WORKSPACE, FA_ERR_HIP,
+ FA_ERR_SCRATCH_LIMIT) = range(8)
+FA_NOALLOC_SCRATCH_BYTES = 16 << 20     # the static scratch array of fa_decode_noalloc (fa.h)
 FA_FP32, FA_BF16 = 0, 1
 
 
@@ -77,6 +82,8 @@ def _load() -> ctypes.CDLL:
     lib_.fa_decode_workspace_bytes.restype = Z
     lib_.fa_decode.argtypes = [P, P, P, P, P, P, Z, I, I, I, I, I, I, I, F, P]
     lib_.fa_decode.restype = I
+    lib_.fa_decode_noalloc.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, F, P]
+    lib_.fa_decode_noalloc.restype = I
     lib_.fa_decode_paged.argtypes = [P, P, P, P, P, P, P, P, Z, I, I, I, I, I, I, I, I, I, F, P]
     lib_.fa_decode_paged.restype = I
     lib_.fa_status_string.argtypes = [I]
@@ -127,6 +134,10 @@ def fa_decode(q, k_cache, v_cache, o, lse, workspace, workspace_bytes, B, H, Hkv
               num_splits, scale, stream=0) -> int:
     return lib.fa_decode(q, k_cache, v_cache, o, lse, workspace, workspace_bytes, B, H, Hkv, L, d,
                          dtype, num_splits, scale, stream)
+
+
+def fa_decode_noalloc(q, k_cache, v_cache, o, lse, B, H, Hkv, L, d, dtype, num_splits, scale, stream=0) -> int:
+    return lib.fa_decode_noalloc(q, k_cache, v_cache, o, lse, B, H, Hkv, L, d, dtype, num_splits, scale, stream)
 
 
 def fa_decode_paged(q, k_pool, v_pool, block_table, seq_lens, o, lse, workspace, workspace_bytes,
@@ -282,6 +293,40 @@ def decode(q, k_cache, v_cache, scale: float | None = None, num_splits: int = 0)
                    ws.data_ptr(), nbytes, B, H, Hkv, L, d, _dtype_code(q), num_splits, scale, _stream(q))
     _raise(st, "fa_decode")
     return o, lse
+
+
+def decode_noalloc(q, k_cache, v_cache, o, lse, scale: float | None = None, num_splits: int = 0):
+    """``decode`` into caller-provided outputs, via ``fa_decode_noalloc``.
+
+    Allocates nothing (no torch allocation either): the split partials live in
+    the library's static scratch array.  q [B,H,1,d], caches [B,Hkv,L,d], o
+    [B,H,1,d] bf16, lse [B,H] fp32 (or None).  Raises ``FaError`` with
+    FA_ERR_SCRATCH_LIMIT when the call needs more than
+    FA_NOALLOC_SCRATCH_BYTES of scratch.  Calls that overlap on one GPU race
+    on that array.
+    """
+    torch = _torch()
+    _check(q, "q")
+    B, H, one, d = q.shape
+    if one != 1:
+        raise ValueError("decode takes one query token per (batch, head)")
+    _check(k_cache, "k_cache")
+    Hkv, L = k_cache.shape[1], k_cache.shape[2]
+    _check(k_cache, "k_cache", (B, Hkv, L, d))
+    _check(v_cache, "v_cache", (B, Hkv, L, d))
+    _check(o, "o", (B, H, 1, d))
+    if o.dtype != q.dtype:
+        raise TypeError("o must have q's dtype")
+    lse_ptr = 0
+    if lse is not None:
+        _check(lse, "lse", (B, H))
+        if lse.dtype != torch.float32:
+            raise TypeError("lse must be float32")
+        lse_ptr = lse.data_ptr()
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    st = fa_decode_noalloc(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), o.data_ptr(), lse_ptr,
+                           B, H, Hkv, L, d, _dtype_code(q), num_splits, scale, _stream(q))
+    _raise(st, "fa_decode_noalloc")
 
 
 def decode_paged(q, k_pool, v_pool, block_table, seq_lens, scale: float | None = None, num_splits: int = 0):

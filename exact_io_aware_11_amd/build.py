@@ -22,7 +22,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libfa.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 
-SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_fwd_fp8.hip", "fa_bwd.hip", "fa_decode.hip"]
+SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_fwd_fp8.hip", "fa_bwd.hip", "fa_decode.hip", "fa_noalloc.hip"]
 
 ARCH = "gfx950"
 
@@ -59,7 +59,7 @@ def build(verbose: bool = False) -> str:
     """Compile every source and link ``libfa.so`` next to this file; returns its path."""
     with tempfile.TemporaryDirectory(prefix="fa_build_") as tmp:
         objs = [os.path.join(tmp, os.path.splitext(s)[0] + ".o") for s in SOURCES]
-        with ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
+        with ThreadPoolExecutor(max_workers=min(6, len(SOURCES))) as ex:
             list(ex.map(_compile, SOURCES, objs))
         out_tmp = LIB_PATH + ".tmp"
         cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", out_tmp] + objs

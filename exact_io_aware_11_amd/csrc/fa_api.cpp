@@ -112,6 +112,9 @@ const char* fa_status_string(fa_status_t s) {
         case FA_ERR_ALIGN: return "FA_ERR_ALIGN: a pointer is not 16-byte aligned";
         case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace missing or too small";
         case FA_ERR_HIP: return "FA_ERR_HIP: the HIP runtime reported an error";
+        case FA_ERR_SCRATCH_LIMIT:
+            return "FA_ERR_SCRATCH_LIMIT: the call needs more scratch than the library's static buffer "
+                   "(FA_NOALLOC_SCRATCH_BYTES) holds";
     }
     return "unknown fa_status_t";
 }
@@ -203,9 +206,14 @@ size_t fa_decode_workspace_bytes(int B, int H, int Hkv, int L, int d, int num_sp
     return ((o_bytes + 255) & ~(size_t)255) + parts * sizeof(float);
 }
 
-fa_status_t fa_decode(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
-                      void* workspace, size_t workspace_bytes, int B, int H, int Hkv, int L, int d,
-                      fa_dtype_t dtype, int num_splits, float scale, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Every check of fa_decode except the workspace's; nothing is enqueued.
+fa_status_t decode_validate(const void* q, const void* k_cache, const void* v_cache, const void* o,
+                            const float* lse, int B, int H, int Hkv, int L, int d, fa_dtype_t dtype,
+                            int num_splits, float scale) {
     if (!q || !k_cache || !v_cache || !o) return FA_ERR_NULL;
     if (!dims_ok(B, H, L) || !kv_ok(H, Hkv) || !scale_ok(scale) || num_splits < 0 || num_splits > L ||
         !total_ok(B, H, L, d))
@@ -213,9 +221,22 @@ fa_status_t fa_decode(const void* q, const void* k_cache, const void* v_cache, v
     if (!head_dim_ok_bf16(d) || dtype != FA_BF16 || !head_fits_u32(L, d)) return FA_ERR_UNSUPPORTED;
     if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o)) return FA_ERR_ALIGN;
     if (lse && !aligned16(lse)) return FA_ERR_ALIGN;
-    const size_t need = fa_decode_workspace_bytes(B, H, Hkv, L, d, num_splits);
-    if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
-    if (!aligned16(workspace)) return FA_ERR_ALIGN;
+    return FA_OK;
+}
+
+// Bytes of fp32 partials the contiguous-cache plan of this call needs (the
+// same carving decode_launch does).
+size_t decode_plan_bytes(int B, int H, int Hkv, int L, int d, int num_splits) {
+    int splits, chunk;
+    split_plan(L, num_splits == 0 ? auto_splits(B, H, Hkv, L, false) : num_splits, splits, chunk);
+    const size_t parts = (size_t)B * H * splits;
+    return ((parts * (size_t)d * sizeof(float) + 255) & ~(size_t)255) + parts * sizeof(float);
+}
+
+// Split plan, partial buffers carved from the workspace, launch.
+fa_status_t decode_launch(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                          void* workspace, int B, int H, int Hkv, int L, int d, int num_splits, float scale,
+                          void* stream) {
     int splits, chunk;
     split_plan(L, num_splits == 0 ? auto_splits(B, H, Hkv, L, false) : num_splits, splits, chunk);
     const size_t parts = (size_t)B * H * splits;
@@ -224,6 +245,33 @@ fa_status_t fa_decode(const void* q, const void* k_cache, const void* v_cache, v
                                                (((parts * (size_t)d * sizeof(float)) + 255) & ~(size_t)255));
     fa::DecodeArgs a{q, k_cache, v_cache, o, lse, o_part, lse_part, B, H, Hkv, L, d, splits, chunk, scale, stream};
     return from_hip(fa::launch_decode(a));
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status_t fa_decode(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                      void* workspace, size_t workspace_bytes, int B, int H, int Hkv, int L, int d,
+                      fa_dtype_t dtype, int num_splits, float scale, void* stream) {
+    const fa_status_t st = decode_validate(q, k_cache, v_cache, o, lse, B, H, Hkv, L, d, dtype, num_splits, scale);
+    if (st != FA_OK) return st;
+    const size_t need = fa_decode_workspace_bytes(B, H, Hkv, L, d, num_splits);
+    if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return FA_ERR_ALIGN;
+    return decode_launch(q, k_cache, v_cache, o, lse, workspace, B, H, Hkv, L, d, num_splits, scale, stream);
+}
+
+fa_status_t fa_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                              int B, int H, int Hkv, int L, int d, fa_dtype_t dtype, int num_splits, float scale,
+                              void* stream) {
+    const fa_status_t st = decode_validate(q, k_cache, v_cache, o, lse, B, H, Hkv, L, d, dtype, num_splits, scale);
+    if (st != FA_OK) return st;
+    if (decode_plan_bytes(B, H, Hkv, L, d, num_splits) > (size_t)FA_NOALLOC_SCRATCH_BYTES)
+        return FA_ERR_SCRATCH_LIMIT;
+    void* scratch = nullptr;
+    if (fa::decode_scratch(&scratch) != hipSuccess) return FA_ERR_HIP;
+    return decode_launch(q, k_cache, v_cache, o, lse, scratch, B, H, Hkv, L, d, num_splits, scale, stream);
 }
 
 fa_status_t fa_decode_paged(const void* q, const void* k_pool, const void* v_pool, const int32_t* block_table,

@@ -128,4 +128,8 @@ hipError_t launch_fwd_fp8(const Fp8FwdArgs& a);
 hipError_t launch_bwd(const BwdArgs& a);
 hipError_t launch_decode(const DecodeArgs& a);
 
+// Device address of the static scratch array (FA_NOALLOC_SCRATCH_BYTES) on
+// the current device; looked up once per device.
+hipError_t decode_scratch(void** ptr);
+
 }  // namespace fa

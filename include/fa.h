@@ -60,8 +60,14 @@ typedef enum {
                                bf16 head too large (N*d*2 >= 2^32 bytes)       */
     FA_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned                */
     FA_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required      */
-    FA_ERR_HIP = 6          /* the HIP runtime reported an error at launch     */
+    FA_ERR_HIP = 6,         /* the HIP runtime reported an error at launch     */
+    FA_ERR_SCRATCH_LIMIT = 7 /* fa_decode_noalloc: the call needs more scratch
+                               than FA_NOALLOC_SCRATCH_BYTES                   */
 } fa_status_t;
+
+/* Size of the static device scratch array behind fa_decode_noalloc (16 MiB
+ * per GPU the library runs on, held until the process ends). */
+#define FA_NOALLOC_SCRATCH_BYTES (16u << 20)
 
 typedef enum {
     FA_FP32 = 0,            /* IEEE binary32                                   */
@@ -207,6 +213,35 @@ fa_status_t fa_decode(const void* q, const void* k_cache, const void* v_cache,
                       void* workspace, size_t workspace_bytes,
                       int B, int H, int Hkv, int L, int d, fa_dtype_t dtype,
                       int num_splits, float scale, void* stream);
+
+/*
+ * fa_decode_noalloc -- fa_decode without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  It computes exactly what fa_decode
+ * computes with the same num_splits, and allocates nothing: the per-chunk
+ * partials (o_s, lse_s) go to a static device array of
+ * FA_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs on.
+ *
+ *   q, k_cache, v_cache, o, lse, B, H, Hkv, L, d, dtype, num_splits, scale,
+ *   stream            as for fa_decode.  The pointers and the stream must
+ *                     belong to the device current on the calling thread.
+ *
+ * Limit: the call's partials, 4*B*H*S*(d+1) bytes for S splits (plus padding
+ * to 256 bytes), must fit FA_NOALLOC_SCRATCH_BYTES; every call with
+ * fa_decode_workspace_bytes(B, H, Hkv, L, d, num_splits) <= that size does.
+ * Larger calls return FA_ERR_SCRATCH_LIMIT and launch nothing (a smaller
+ * num_splits shrinks the need).  Other errors as for fa_decode; FA_ERR_HIP if
+ * the scratch array's device address cannot be looked up.
+ *
+ * The array is shared by every call on one GPU and keeps the last call's
+ * contents (every partial is written before it is read, so nothing needs
+ * clearing).  Calls that overlap in time on one GPU race on it: issue them on
+ * one stream, or order them.
+ */
+fa_status_t fa_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                              void* o, float* lse,
+                              int B, int H, int Hkv, int L, int d, fa_dtype_t dtype,
+                              int num_splits, float scale, void* stream);
 
 /*
  * fa_decode_paged -- fa_decode against a paged KV cache.  The attention-backend

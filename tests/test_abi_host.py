@@ -31,7 +31,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
-        "fa_bwd", "fa_bwd_workspace_bytes", "fa_decode", "fa_decode_num_splits", "fa_decode_paged",
+        "fa_bwd", "fa_bwd_workspace_bytes", "fa_decode", "fa_decode_noalloc", "fa_decode_num_splits",
+        "fa_decode_paged",
         "fa_decode_workspace_bytes", "fa_fwd", "fa_fwd_fp8", "fa_status_string"])
 
 
@@ -55,8 +56,9 @@ def test_single_hip_runtime_in_process():
 
 
 def test_status_strings():
-    for s in range(7):
+    for s in range(8):
         assert fa.fa_status_string(s).startswith("FA_")
+    assert "FA_NOALLOC_SCRATCH_BYTES" in fa.fa_status_string(fa.FA_ERR_SCRATCH_LIMIT)
     assert "unknown" in fa.fa_status_string(99)
 
 
@@ -233,6 +235,40 @@ def test_decode_rejects(kw, status):
 def test_decode_rejects_small_workspace():
     need = fa.fa_decode_workspace_bytes(2, 2, 1, 100, 128, 4)
     assert dec(ws_bytes=need - 1, splits=4) == fa.FA_ERR_WORKSPACE
+
+
+def dec_noalloc(**kw):
+    args = dict(q=A, k=A, v=A, o=A, lse=A, B=2, H=2, Hkv=1, L=100, d=128, dtype=fa.FA_BF16, splits=0, scale=0.1)
+    args.update(kw)
+    return fa.fa_decode_noalloc(args["q"], args["k"], args["v"], args["o"], args["lse"], args["B"], args["H"],
+                                args["Hkv"], args["L"], args["d"], args["dtype"], args["splits"], args["scale"], 0)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=0), fa.FA_ERR_NULL),
+    (dict(v=0), fa.FA_ERR_NULL),
+    (dict(L=0), fa.FA_ERR_ARG),
+    (dict(Hkv=3), fa.FA_ERR_ARG),
+    (dict(splits=101), fa.FA_ERR_ARG),
+    (dict(scale=float("nan")), fa.FA_ERR_ARG),
+    (dict(dtype=fa.FA_FP32), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(o=MIS), fa.FA_ERR_ALIGN),
+    # partials of B*H*S*(d+1) floats beyond the 16 MiB static array: rejected
+    # before anything touches the device
+    (dict(B=64, H=32, Hkv=32, L=8192, splits=32), fa.FA_ERR_SCRATCH_LIMIT),
+    (dict(B=1, H=64, Hkv=64, L=1 << 20, d=256, splits=256), fa.FA_ERR_SCRATCH_LIMIT),
+])
+def test_decode_noalloc_rejects(kw, status):
+    assert dec_noalloc(**kw) == status
+
+
+def test_decode_noalloc_limit_matches_the_workspace_size():
+    # every call whose workspace fits the static array is accepted by the size
+    # check: with num_splits = S the scratch need equals fa_decode's workspace
+    cap = fa.FA_NOALLOC_SCRATCH_BYTES
+    assert fa.fa_decode_workspace_bytes(64, 32, 32, 8192, 128, 32) > cap
+    assert fa.fa_decode_workspace_bytes(64, 32, 32, 8192, 128, 8) <= cap
 
 
 def test_decode_split_plan():
