@@ -18,7 +18,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 bool dims_ok(int B, int H, int N) { return B >= 1 && H >= 1 && N >= 1; }
 
 bool head_dim_ok(int d) { return d == 64 || d == 128; }
-// bf16 forward and decode also run at d = 256 (fp32 forward and the backward do not)
+// the bf16 forward, backward and decodes also run at d = 256 (fp32 forward and fp8 do not)
 bool head_dim_ok_bf16(int d) { return head_dim_ok(d) || d == 256; }
 
 bool scale_ok(float s) { return std::isfinite(s) && s > 0.f; }
@@ -168,7 +168,7 @@ fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, f
                    float scale, void* stream) {
     if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_NULL;
     if (!dims_ok(B, H, N) || !kv_ok(H, Hkv) || !scale_ok(scale) || !total_ok(B, H, N, d)) return FA_ERR_ARG;
-    if (!head_dim_ok(d) || in_dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+    if (!head_dim_ok_bf16(d) || in_dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
     if (o_dtype != FA_BF16 && o_dtype != FA_FP32) return FA_ERR_UNSUPPORTED;
     if (!head_fits_u32(N, d)) return FA_ERR_UNSUPPORTED;
     const void* ptrs[] = {q, k, v, o, lse, dout, dq, dk, dv};

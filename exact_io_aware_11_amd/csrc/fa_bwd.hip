@@ -49,7 +49,12 @@ namespace fa {
 
 namespace {
 
-constexpr int BWD_BR = 64;       // query rows per inner step
+// Query rows per inner step of the dK/dV kernel: 64 (two 32-row halves whose
+// products and exponentials are interleaved) for d <= 128.  At d = 256 the
+// wave's K and V (128 VGPRs) and its dK^T/dV^T accumulators (256 registers)
+// leave room for one 32-row block only.
+template <int D>
+constexpr int bwd_br() { return D == 256 ? 32 : 64; }
 constexpr int BWD_BC = kBwdKeyTile;   // keys per workgroup (4 waves x 32)
 constexpr int BWD_THREADS = 256;
 
@@ -91,7 +96,12 @@ bwd_prep_kernel(const void* __restrict__ O, const __bf16* __restrict__ dO, float
             acc = fmaf(bf16_hi(dp[j]), ov[2 * j + 1], acc);
         }
     }
-    acc = (LPR == 16) ? dpp_sum16(acc) : dpp_sum8(acc);
+    if constexpr (LPR == 8) {
+        acc = dpp_sum8(acc);
+    } else {
+        acc = dpp_sum16(acc);
+        if constexpr (LPR == 32) acc += __shfl_xor(acc, 16);   // d = 256: two 16-lane rows per row
+    }
     if (live && part == 0) delta[row] = acc;
 }
 
@@ -130,7 +140,7 @@ bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, cons
                 const float* __restrict__ delta, __bf16* __restrict__ dK,
                 __bf16* __restrict__ dV, float* __restrict__ pdk, float* __restrict__ pdv,
                 int BHkv, int G, int N, float c /* scale*log2e */, float scale) {
-    constexpr int BR = BWD_BR, BC = BWD_BC;
+    constexpr int BR = bwd_br<D>(), BC = BWD_BC;
     constexpr int ROWB = 2 * D;                  // bytes per row of a Q/dO/K tile
     constexpr int CPR = D / 8;
     constexpr int QTB = BR * ROWB;               // bytes of a Q (or dO) tile
@@ -145,7 +155,7 @@ bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, cons
     constexpr int BUFB = 2 * QTB + 2 * BR * 4;
     __shared__ __attribute__((aligned(1024))) char buf0[BUFB];
     __shared__ __attribute__((aligned(1024))) char buf1[BUFB];
-    static_assert(BR == 64, "two 32-row halves per query tile; one wave copies a row statistic");
+    static_assert(BR == 64 || BR == 32, "one or two 32-row blocks per query tile; one wave copies a row statistic");
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
@@ -204,9 +214,14 @@ bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, cons
     }
 
     // per-lane LDS offsets.  Row-major chunk reads: row 32*b + l32, chunk 2*ks + g.
-    int rd_off[D / 16];
+    // The swizzle only permutes the low 4 bits of the chunk index, so at d = 256
+    // chunks 16..31 sit 256 bytes after chunks 0..15: eight offsets serve all
+    // K-steps (register pressure).
+    constexpr int NRO = D / 16 > 8 ? 8 : D / 16;
+    int rd_off_[NRO];
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) rd_off[ks] = l32 * ROWB + 16 * ((2 * ks + g) ^ rt_swz<D>(l32));
+    for (int ks = 0; ks < NRO; ++ks) rd_off_[ks] = l32 * ROWB + 16 * ((2 * ks + g) ^ rt_swz<D>(l32));
+    auto rd_off = [&](int ks) __attribute__((always_inline)) -> int { return rd_off_[ks % NRO] + 256 * (ks / NRO); };
     // Transposed reads: the 16-lane group of this lane reads rows r..r+3 and
     // columns 32*mb + ct .. +15, lane (rt, ct): row r + rt, 4 columns at ct.
     // Row offsets that are multiples of 16 leave the swizzle unchanged, so the
@@ -217,11 +232,15 @@ bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, cons
     auto tr_off = [&](int row, int col) __attribute__((always_inline)) -> int {
         return row * ROWB + 16 * ((col >> 3) ^ rt_swz<D>(row)) + 2 * (col & 7);
     };
-    int qt_off[2][D / 32];
+    constexpr int NTO = D / 32 > 4 ? 4 : D / 32;   // as above: columns 128.. sit 256 bytes on
+    int qt_off_[2][NTO];
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int mb = 0; mb < D / 32; ++mb) qt_off[h][mb] = tr_off(4 * g + 8 * h + rt, 32 * mb + ct);
+        for (int mb = 0; mb < NTO; ++mb) qt_off_[h][mb] = tr_off(4 * g + 8 * h + rt, 32 * mb + ct);
+    auto qt_off = [&](int h, int mb) __attribute__((always_inline)) -> int {
+        return qt_off_[h][mb % NTO] + 256 * (mb / NTO);
+    };
 
     f32x16 dvt[D / 32], dkt[D / 32];
 #pragma unroll
@@ -289,15 +308,18 @@ bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, cons
         // a wave whose keys see none of the tile's queries has nothing to add
         const bool wave_dead = (CAUSAL && wk0 > q0 + BR - 1) || wk0 >= N;
         if (!wave_dead) {
-            // LSE and D of this lane's 16 query rows per block (runs of 4)
+            // LSE and D of this lane's 16 query rows per block (runs of 4);
+            // at d = 256 they are read where they are used (register pressure)
             float4 lse4[NQB][4], dd4[NQB][4];
+            if constexpr (D != 256) {
 #pragma unroll
-            for (int qb = 0; qb < NQB; ++qb)
+                for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
-                for (int rb = 0; rb < 4; ++rb) {
-                    lse4[qb][rb] = *reinterpret_cast<const float4*>(ls + 32 * qb + 8 * rb + 4 * g);
-                    dd4[qb][rb] = *reinterpret_cast<const float4*>(ds_ + 32 * qb + 8 * rb + 4 * g);
-                }
+                    for (int rb = 0; rb < 4; ++rb) {
+                        lse4[qb][rb] = *reinterpret_cast<const float4*>(ls + 32 * qb + 8 * rb + 4 * g);
+                        dd4[qb][rb] = *reinterpret_cast<const float4*>(ds_ + 32 * qb + 8 * rb + 4 * g);
+                    }
+            }
 
             // The two 32-row halves of the tile are independent until they
             // meet in dV^T and dK^T, which lets one half's exponentials run in
@@ -310,9 +332,9 @@ bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, cons
                 dP[qb] = zero16();
 #pragma unroll
                 for (int ks = 0; ks < D / 16; ++ks) {
-                    const bf16x8 aq = *reinterpret_cast<const bf16x8*>(qs + 32 * qb * ROWB + rd_off[ks]);
+                    const bf16x8 aq = *reinterpret_cast<const bf16x8*>(qs + 32 * qb * ROWB + rd_off(ks));
                     sP[qb] = mfma_bf16(aq, kf[ks], sP[qb]);
-                    const bf16x8 ad = *reinterpret_cast<const bf16x8*>(os + 32 * qb * ROWB + rd_off[ks]);
+                    const bf16x8 ad = *reinterpret_cast<const bf16x8*>(os + 32 * qb * ROWB + rd_off(ks));
                     dP[qb] = mfma_bf16(ad, vf[ks], dP[qb]);
                 }
             };
@@ -328,7 +350,10 @@ bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, cons
 #pragma unroll
                         for (int u = 0; u < 2; ++u) {
                             const int r = 8 * h + j + u, rb = r >> 2, t = r & 3;
-                            const float4 l4 = lse4[qb][rb], d4 = dd4[qb][rb];
+                            const float4 l4 = D == 256 ? *reinterpret_cast<const float4*>(ls + 32 * qb + 8 * rb + 4 * g)
+                                                       : lse4[qb][rb];
+                            const float4 d4 = D == 256 ? *reinterpret_cast<const float4*>(ds_ + 32 * qb + 8 * rb + 4 * g)
+                                                       : dd4[qb][rb];
                             const float lv = t == 0 ? l4.x : t == 1 ? l4.y : t == 2 ? l4.z : l4.w;
                             const float dv = t == 0 ? d4.x : t == 1 ? d4.y : t == 2 ? d4.z : d4.w;
                             float p = exp2_fast(fmaf(sP[qb][r], c, -lv * kLog2e));
@@ -352,28 +377,36 @@ bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, cons
                 const int rk = 16 * ks * ROWB;
 #pragma unroll
                 for (int mb = 0; mb < D / 32; ++mb) {
-                    const uint2 dlo = lds_read_tr16x4(os + rk + qt_off[0][mb]);
-                    const uint2 dhi = lds_read_tr16x4(os + rk + qt_off[1][mb]);
+                    const uint2 dlo = lds_read_tr16x4(os + rk + qt_off(0, mb));
+                    const uint2 dhi = lds_read_tr16x4(os + rk + qt_off(1, mb));
                     dvt[mb] = mfma_bf16(as_bf16x8(make_uint4(dlo.x, dlo.y, dhi.x, dhi.y)), pb[ks], dvt[mb]);
-                    const uint2 qlo = lds_read_tr16x4(qs + rk + qt_off[0][mb]);
-                    const uint2 qhi = lds_read_tr16x4(qs + rk + qt_off[1][mb]);
+                    const uint2 qlo = lds_read_tr16x4(qs + rk + qt_off(0, mb));
+                    const uint2 qhi = lds_read_tr16x4(qs + rk + qt_off(1, mb));
                     dkt[mb] = mfma_bf16(as_bf16x8(make_uint4(qlo.x, qlo.y, qhi.x, qhi.y)), sb[ks], dkt[mb]);
                 }
             };
             auto pipeline = [&](auto masked) __attribute__((always_inline)) {
-                sdp(0);
-                __builtin_amdgcn_sched_barrier(0);
-                sdp(1);
-                pds(0, masked);
-                FA_INTERLEAVE(2 * D / 16, 2, 4);
-                __builtin_amdgcn_sched_barrier(0);
-                dvdk(0);
-                dvdk(1);
-                pds(1, masked);
-                FA_INTERLEAVE(4 * D / 32, 4, 4);
-                __builtin_amdgcn_sched_barrier(0);
-                dvdk(2);
-                dvdk(3);
+                if constexpr (NQB == 2) {
+                    sdp(0);
+                    __builtin_amdgcn_sched_barrier(0);
+                    sdp(1);
+                    pds(0, masked);
+                    FA_INTERLEAVE(2 * D / 16, 2, 4);
+                    __builtin_amdgcn_sched_barrier(0);
+                    dvdk(0);
+                    dvdk(1);
+                    pds(1, masked);
+                    FA_INTERLEAVE(4 * D / 32, 4, 4);
+                    __builtin_amdgcn_sched_barrier(0);
+                    dvdk(2);
+                    dvdk(3);
+                } else {
+                    // one 32-row block: S, dP | P, dS | dV, dK
+                    sdp(0);
+                    pds(0, masked);
+                    dvdk(0);
+                    dvdk(1);
+                }
             };
             // Causal: the unmasked copy serves every tile off the diagonal.
             // Without a causal mask no tile needs one: query rows past N
@@ -381,7 +414,12 @@ bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, cons
             // dS vanish, and they add nothing to dK or dV; keys past N have
             // zero K and V, and only their own dK/dV columns (never stored)
             // see them.
-            if constexpr (CAUSAL) {
+            if constexpr (D == 256) {
+                // one copy of the body, the masked one: at d = 256 the causal
+                // kernel with both copies spills, and the unmasked body alone
+                // still spills a few registers
+                pipeline(std::true_type{});
+            } else if constexpr (CAUSAL) {
                 const bool need_mask = (k0 + BC > N) || (q0 + BR > N) || (wk0 + 31 > q0);
                 if (need_mask)
                     pipeline(std::true_type{});
@@ -399,7 +437,34 @@ bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, cons
     }
 
     // dV = (dV^T)^T, dK = scale (dK^T)^T: lane holds key `key`, dims in runs of 4
-    if constexpr (SPLIT) {
+    if constexpr (D == 256) {
+        // d = 256: 128 rows of 512 bytes per tensor do not fit the two tile
+        // buffers, so every lane writes its 16-byte runs directly (the
+        // epilogue is small against the query loop at these sizes)
+        if (key_live) {
+#pragma unroll
+            for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+                for (int rb = 0; rb < 4; ++rb) {
+                    const int d0 = 32 * mb + 8 * rb + 4 * g;
+                    if constexpr (SPLIT) {
+                        const size_t o = ((size_t)head0 * N + key) * D + d0;
+                        *reinterpret_cast<float4*>(pdv + o) =
+                            make_float4(dvt[mb][4 * rb], dvt[mb][4 * rb + 1], dvt[mb][4 * rb + 2], dvt[mb][4 * rb + 3]);
+                        *reinterpret_cast<float4*>(pdk + o) =
+                            make_float4(dkt[mb][4 * rb], dkt[mb][4 * rb + 1], dkt[mb][4 * rb + 2], dkt[mb][4 * rb + 3]);
+                    } else {
+                        const size_t o = kvoff + (size_t)key * D + d0;
+                        *reinterpret_cast<uint2*>(dV + o) =
+                            make_uint2(pack_bf16x2(dvt[mb][4 * rb], dvt[mb][4 * rb + 1]),
+                                       pack_bf16x2(dvt[mb][4 * rb + 2], dvt[mb][4 * rb + 3]));
+                        *reinterpret_cast<uint2*>(dK + o) =
+                            make_uint2(pack_bf16x2(scale * dkt[mb][4 * rb], scale * dkt[mb][4 * rb + 1]),
+                                       pack_bf16x2(scale * dkt[mb][4 * rb + 2], scale * dkt[mb][4 * rb + 3]));
+                    }
+                }
+        }
+    } else if constexpr (SPLIT) {
         // The fp32 partial rows go through the free tile buffers too (waves
         // 0 and 1 in buf0, 2 and 3 in buf1; dV, then dK in the same rows),
         // so that each store writes whole rows rather than 16 bytes into each
@@ -427,7 +492,7 @@ bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, cons
         stagef(dvt, pdv);
         stagef(dkt, pdk);
     }
-    if constexpr (!SPLIT) {
+    if constexpr (!SPLIT && D != 256) {
         // Each lane holds 8 bytes of 16 rows; stored directly, every store
         // instruction would write 16 bytes into each of 32 rows, which held
         // the waves for microseconds at the end of every workgroup.  The rows
@@ -505,7 +570,11 @@ bwd_kv_reduce_kernel(const float* __restrict__ pdk, const float* __restrict__ pd
 // 3. dQ kernel: query-tile outer, K/V tiles streamed through LDS.
 // ---------------------------------------------------------------------------
 constexpr int DQ_BR = 128;       // query rows per workgroup (4 waves x 32)
-constexpr int DQ_BC = 64;        // keys per K/V tile
+// keys per K/V tile: 64, or 32 at d = 256 (as in the forward), where Q^T and
+// dO^T (128 VGPRs) and the dQ^T accumulator (128) already fill one wave's
+// budget at two waves per SIMD; d = 256 runs one wave per SIMD
+template <int D>
+constexpr int dq_bc() { return D == 256 ? 32 : 64; }
 
 // instruction schedule of the dQ tile loop (measured best on MI355X)
 constexpr int DQ_AHEAD = 2;         // K^T operands read ahead of the dQ MFMAs
@@ -513,11 +582,11 @@ constexpr int DQ_VALU_FIRST = 40;   // dS work placed before the first dQ MFMA
 constexpr int DQ_VALU_EACH = 8;     // and between the following ones
 
 template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 256 ? 1 : 2)))
 bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
               const __bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ delta,
               __bf16* __restrict__ dQ, int BH, int G, int N, int nqt, float c /* scale*log2e */, float scale) {
-    constexpr int BR = DQ_BR, BC = DQ_BC;
+    constexpr int BR = DQ_BR, BC = dq_bc<D>();
     constexpr int ROWB = 2 * D;
     constexpr int CPR = D / 8;
     constexpr int TILEB = BC * ROWB;
@@ -758,6 +827,7 @@ hipError_t launch_bwd(const BwdArgs& a) {
     const long long rows = (long long)a.B * a.H * a.N;
     if (rows * (a.d / 8) / 256 + 1 > 0x7fffffffLL) return hipErrorInvalidValue;
     if (a.d == 64) return a.causal ? launch_kernels<64, true>(a) : launch_kernels<64, false>(a);
+    if (a.d == 256) return a.causal ? launch_kernels<256, true>(a) : launch_kernels<256, false>(a);
     return a.causal ? launch_kernels<128, true>(a) : launch_kernels<128, false>(a);
 }
 

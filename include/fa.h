@@ -31,8 +31,9 @@
  *    its is_causal usage example in section 6): key j is visible to query i
  *    iff j <= i (top-left aligned).
  *  - Head dimension: d in {64, 128} for every entry point; d = 256 also for
- *    the bf16 fa_fwd, fa_decode and fa_decode_paged (not for fp32 inputs,
- *    fa_fwd_fp8 or fa_bwd).  Other values return FA_ERR_UNSUPPORTED.
+ *    the bf16 fa_fwd, fa_bwd, fa_decode, fa_decode_noalloc and fa_decode_paged
+ *    (not for fp32 inputs or fa_fwd_fp8).  Other values return
+ *    FA_ERR_UNSUPPORTED.
  *  - Any N >= 1 (ragged tails are masked inside the kernels); all offsets
  *    are 64-bit.
  *  - Every pointer must be 16-byte aligned.

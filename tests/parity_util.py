@@ -88,6 +88,22 @@ def assert_fp32_close(got, ref, what=""):
     return mx, mean
 
 
+def one_key_grad_bound(x, v, do, scale):
+    """Bound on |dQ| (x = K) or |dK| (x = Q) when every query sees one key.
+
+    Then P = 1 and dS = P (dP - D) is exactly 0, so the true dQ and dK vanish
+    and a bound relative to their max-abs scale is undefined.  On the GPU, dP
+    (a matrix product) and D = rowsum(dO * O) (O = V exactly, with one key) are
+    the same fp32 sum of d exact bf16 products in two orders; each is within
+    d 2^-24 sum_e |dO_e V_e| of the exact value, so |dS| <= 2 d 2^-24
+    max_i sum_e |dO_ie V_e|, and the gradient is at most scale |dS| max|x|
+    (times 1 + 2^-8 for its bf16 rounding)."""
+    x, v, do = (np.abs(np.asarray(t, dtype=np.float64)) for t in (x, v, do))
+    d = do.shape[-1]
+    ds = 2.0 * d * 2.0 ** -24 * float(np.max(np.sum(do * v, axis=-1)))
+    return (1 + 2.0 ** -8) * scale * ds * float(np.max(x))
+
+
 def assert_grad_close(got, ref, what="", max_tol=BF16_MAX, mean_tol=BF16_MEAN):
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)

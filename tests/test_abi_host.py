@@ -156,7 +156,9 @@ def bwd(ws_bytes=None, **kw):
     (dict(scale=float("nan")), fa.FA_ERR_ARG),
     (dict(in_dtype=fa.FA_FP32), fa.FA_ERR_UNSUPPORTED),
     (dict(d=32), fa.FA_ERR_UNSUPPORTED),
-    (dict(d=256), fa.FA_ERR_UNSUPPORTED),    # no backward at d = 256
+    (dict(d=512), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=256, in_dtype=fa.FA_FP32), fa.FA_ERR_UNSUPPORTED),
+    (dict(N=1 << 23, d=256), fa.FA_ERR_UNSUPPORTED),     # one bf16 head of 2^32 bytes
     (dict(o_dtype=3), fa.FA_ERR_UNSUPPORTED),
     (dict(N=1 << 24, d=128), fa.FA_ERR_UNSUPPORTED),
     (dict(dk=MIS), fa.FA_ERR_ALIGN),
