@@ -141,7 +141,7 @@ fa_status_t fa_fwd_fp8(const void* q, const void* k, const void* vt, float q_sca
     if (!q || !k || !vt || !o || !lse) return FA_ERR_NULL;
     if (!dims_ok(B, H, N) || !kv_ok(H, Hkv) || !scale_ok(scale) || !total_ok(B, H, N, d)) return FA_ERR_ARG;
     if (!scale_ok(q_scale) || !scale_ok(k_scale) || !scale_ok(v_scale)) return FA_ERR_ARG;
-    if (!head_dim_ok(d) || N % 64 != 0 || !head_fits_u32(N, d)) return FA_ERR_UNSUPPORTED;
+    if (!head_dim_ok(d) || !head_fits_u32(N, d)) return FA_ERR_UNSUPPORTED;
     if (o_dtype != FA_BF16 && o_dtype != FA_FP32) return FA_ERR_UNSUPPORTED;
     if (!aligned16(q) || !aligned16(k) || !aligned16(vt) || !aligned16(o) || !aligned16(lse)) return FA_ERR_ALIGN;
     fa::Fp8FwdArgs a{q, k, vt, q_scale, k_scale, v_scale, o, lse, B, H, Hkv, N, d, o_dtype == FA_BF16,

@@ -69,7 +69,9 @@ __device__ __forceinline__ int vt_src_dword(int u) { return ((u >> 2) & 1) * 8 +
 template <int ROWB>
 __device__ __forceinline__ int chunk_swz(int row) { return (row / (256 / ROWB)) & (ROWB / 16 - 1); }
 
-template <int D, bool CAUSAL, bool OUT_BF16>
+// VBYTE: V^T rows start at unaligned addresses (N not a multiple of 4), so the
+// V^T tiles are gathered byte by byte through registers instead of by 4-byte DMA.
+template <int D, bool CAUSAL, bool OUT_BF16, bool VBYTE>
 __global__ void __launch_bounds__(F8_THREADS) __attribute__((amdgpu_waves_per_eu(2)))
 fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, const uint8_t* __restrict__ VT,
                void* __restrict__ O, float* __restrict__ LSE, int BH, int G, int N, int nqt,
@@ -124,8 +126,10 @@ fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, con
     // K tile: row-major; V^T tile: D rows of 64 bytes in the key order
     // described above; both with their chunks permuted by chunk_swz.  Each tile is
     // addressed by buffer resources starting at the tile, so the per-lane
-    // offsets below are fixed.  N is a multiple of 64 (checked by the host):
-    // every tile is whole.
+    // offsets below are fixed.  In a ragged last tile, K rows past N read as
+    // zero (the resource ends with the head) and are masked; V^T keys past N
+    // read the first keys of the next dim row (or zero after the last row),
+    // finite values that meet P = 0.
     uint32_t k_dma[KSPW], v_dma[VSPW];
 #pragma unroll
     for (int i = 0; i < KSPW; ++i) {
@@ -139,13 +143,43 @@ fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, con
         const int u = ((lane % 16) ^ (chunk_swz<BC>(row) << 2));    // logical dword at this slot
         v_dma[i] = (uint32_t)((size_t)row * N + 4 * vt_src_dword(u));
     }
+    // VBYTE: each thread gathers VBD dwords of the V^T tile (physical slot p
+    // of dim row r), 4 keys each, byte by byte; keys past N are zero.
+    constexpr int VBD = VBYTE ? D * 16 / F8_THREADS : 1;
+    uint32_t vb_reg[VBD];
+    auto vbyte_load = [&](int kt) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < VBD; ++j) {
+            const int i = tid + F8_THREADS * j;
+            const int r = i / 16, p = i % 16;
+            const int u = p ^ (chunk_swz<BC>(r) << 2);
+            const int key0 = kt * BC + 4 * vt_src_dword(u);
+            const uint8_t* src = VTh + (size_t)r * N + key0;
+            uint32_t word = 0;
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+                if (key0 + b < N) word |= (uint32_t)src[b] << (8 * b);
+            vb_reg[j] = word;
+        }
+    };
+    auto vbyte_store = [&](char* vdst) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < VBD; ++j) {
+            const int i = tid + F8_THREADS * j;
+            *reinterpret_cast<uint32_t*>(vdst + (i / 16) * BC + 4 * (i % 16)) = vb_reg[j];
+        }
+    };
     auto issue = [&](int kt, char* kdst, char* vdst) __attribute__((always_inline)) {
         const __amdgpu_buffer_rsrc_t krs = make_rsrc(Kh + (size_t)kt * BC * D, (uint32_t)(N - kt * BC) * D);
-        const __amdgpu_buffer_rsrc_t vrs = make_rsrc(VTh + (size_t)kt * BC, (uint32_t)((size_t)D * N - kt * BC));
 #pragma unroll
         for (int i = 0; i < KSPW; ++i) b2lds16(krs, k_dma[i], kdst + (w * KSPW + i) * 1024);
+        if constexpr (VBYTE) {
+            vbyte_load(kt);
+        } else {
+            const __amdgpu_buffer_rsrc_t vrs = make_rsrc(VTh + (size_t)kt * BC, (uint32_t)((size_t)D * N - kt * BC));
 #pragma unroll
-        for (int i = 0; i < VSPW; ++i) b2lds4(vrs, v_dma[i], vdst + (w * VSPW + i) * 256);
+            for (int i = 0; i < VSPW; ++i) b2lds4(vrs, v_dma[i], vdst + (w * VSPW + i) * 256);
+        }
     };
 
     // per-lane LDS offsets: K row l32 of block kb, chunks 4*ks + 2*g (+1)
@@ -167,11 +201,7 @@ fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, con
     float m_ref = -INFINITY;   // integer reference max, log2 units
     float l_run = 0.f;         // this lane's share of sum 2^8 p
 
-    auto step = [&](int kt, const char* Ks, const char* Vs, char* kn, char* vn) __attribute__((always_inline)) {
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        if (kt + 1 < nkt) issue(kt + 1, kn, vn);
-        if (kt >= nkt_w) return;
+    auto compute = [&](int kt, const char* Ks, const char* Vs) __attribute__((always_inline)) {
         // S^T = K Q^T
         f32x16 s[NKB];
 #pragma unroll
@@ -236,7 +266,23 @@ fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, con
             oacc[mb] = mfma_f8(join8(lo, hi), pb, oacc[mb]);
         }
     };
-    if (nkt > 0) issue(0, kb0, vb0);
+    auto step = [&](int kt, const char* Ks, const char* Vs, char* kn, char* vn) __attribute__((always_inline)) {
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (kt + 1 < nkt) issue(kt + 1, kn, vn);
+        if constexpr (VBYTE) {
+            // the gathered V^T dwords of tile kt+1 go to LDS after this
+            // tile's work; the next step's wait and barrier order them
+            if (kt < nkt_w) compute(kt, Ks, Vs);
+            if (kt + 1 < nkt) vbyte_store(vn);
+        } else {
+            if (kt < nkt_w) compute(kt, Ks, Vs);
+        }
+    };
+    if (nkt > 0) {
+        issue(0, kb0, vb0);
+        if constexpr (VBYTE) vbyte_store(vb0);
+    }
     for (int kt = 0; kt < nkt; kt += 2) {
         step(kt, kb0, vb0, kb1, vb1);
         if (kt + 1 < nkt) step(kt + 1, kb1, vb1, kb0, vb0);
@@ -294,20 +340,25 @@ fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, con
     }
 }
 
-template <int D, bool CAUSAL, bool OUT_BF16>
+template <int D, bool CAUSAL, bool OUT_BF16, bool VBYTE>
 hipError_t launch(const Fp8FwdArgs& a) {
     const int BH = a.B * a.H;
     const int nqt = (a.N + F8_BR - 1) / F8_BR;
-    hipLaunchKernelGGL((fwd_fp8_kernel<D, CAUSAL, OUT_BF16>), dim3((unsigned)(nqt * BH)), dim3(F8_THREADS), 0,
+    hipLaunchKernelGGL((fwd_fp8_kernel<D, CAUSAL, OUT_BF16, VBYTE>), dim3((unsigned)(nqt * BH)), dim3(F8_THREADS), 0,
                        (hipStream_t)a.stream, (const uint8_t*)a.q, (const uint8_t*)a.k, (const uint8_t*)a.vt, a.o,
                        a.lse, BH, a.H / a.Hkv, a.N, nqt, a.scale * a.q_scale * a.k_scale * kLog2e, a.v_scale);
     return hipGetLastError();
 }
 
+template <int D, bool VBYTE>
+hipError_t dispatch_v(const Fp8FwdArgs& a) {
+    if (a.out_bf16) return a.causal ? launch<D, true, true, VBYTE>(a) : launch<D, false, true, VBYTE>(a);
+    return a.causal ? launch<D, true, false, VBYTE>(a) : launch<D, false, false, VBYTE>(a);
+}
+
 template <int D>
 hipError_t dispatch(const Fp8FwdArgs& a) {
-    if (a.out_bf16) return a.causal ? launch<D, true, true>(a) : launch<D, false, true>(a);
-    return a.causal ? launch<D, true, false>(a) : launch<D, false, false>(a);
+    return (a.N % 4 == 0) ? dispatch_v<D, false>(a) : dispatch_v<D, true>(a);
 }
 
 }  // namespace

@@ -30,7 +30,7 @@ struct Fp8FwdArgs {
     float q_scale, k_scale, v_scale;
     void* o;
     float* lse;
-    int B, H, Hkv, N, d;   // N a multiple of 64
+    int B, H, Hkv, N, d;
     bool out_bf16;
     bool causal;
     float scale;

@@ -128,8 +128,10 @@ fa_status_t fa_fwd(const void* q, const void* k, const void* v,
  * beyond fp32 accumulation.  The row sum and the LSE use the unrounded
  * values.  Uses no workspace.
  *
- * d must be 64 or 128 and N a multiple of 64 (else FA_ERR_UNSUPPORTED); all
- * pointers 16-byte aligned.
+ * d must be 64 or 128 (else FA_ERR_UNSUPPORTED); any N >= 1, the ragged tail
+ * masked as in fa_fwd.  The inputs must be finite (no e4m3 NaN codes): keys
+ * past N of a ragged last tile may read the next row of vt, which is then
+ * weighted by exactly zero.  All pointers 16-byte aligned.
  */
 fa_status_t fa_fwd_fp8(const void* q, const void* k, const void* vt,
                        float q_scale, float k_scale, float v_scale,

@@ -123,8 +123,8 @@ def fwd8(**kw):
     (dict(qs=0.0), fa.FA_ERR_ARG),
     (dict(ks=-1.0), fa.FA_ERR_ARG),
     (dict(vs=float("nan")), fa.FA_ERR_ARG),
-    (dict(N=100), fa.FA_ERR_UNSUPPORTED),       # N must be a multiple of 64
-    (dict(N=65), fa.FA_ERR_UNSUPPORTED),
+    (dict(N=0), fa.FA_ERR_ARG),
+    (dict(N=1 << 25, d=128), fa.FA_ERR_UNSUPPORTED),   # one head of 2^32 bytes or more
     (dict(d=256), fa.FA_ERR_UNSUPPORTED),
     (dict(d=32), fa.FA_ERR_UNSUPPORTED),
     (dict(o_dtype=5), fa.FA_ERR_UNSUPPORTED),

@@ -3,8 +3,14 @@
 The gate is the definition: ``ref_fwd`` of the oracle on the dequantised
 inputs.  Its tolerances come from the kernel's one rounding step (P rounded
 to e4m3 before the second product; the derivation is in tests/fp8_model.py):
-* RMS error over O within sigma_p, the rounding model's bound, combined with
-  the bf16 rounding of the output;
+* RMS error over O within sigma_p, the rounding model's expected RMS,
+  combined with the bf16 rounding of the output.  sigma_p is an expectation
+  over independent rounding events (one per visible query-key pair); with n
+  of them the mean square of a sample fluctuates by a relative sqrt(2/n)
+  (chi-square with n degrees of freedom), so the gate allows 4 such standard
+  deviations: about 1% at the smallest whole-tile case (N = 64, n = 2080),
+  and a factor 2.6 on a single key (N = 1, one event), where the worst-case
+  element-wise bound below is the sharper check;
 * every element within the worst case max|V| (2^-4 + N 2^-17), plus the
   output rounding (relative error 2^-4 of each weight, plus subnormal codes);
 * LSE: the kernel's row sum uses the unrounded probabilities, so the LSE
@@ -65,8 +71,11 @@ def _check(o, lse, args, causal, scale, out_bf16, heads=None):
     rms_method = math.sqrt(np.mean((o - method) ** 2))
     say(f"  rms vs exact {rms_exact / sigma_p:.3f} sigma_p, vs the method {rms_method / sigma_p:.4f} sigma_p "
         f"(sigma_p {sigma_p:.2e}, bf16 output {sigma_out:.1e})")
-    assert rms_exact <= math.sqrt(sigma_p ** 2 + sigma_out ** 2), (rms_exact, sigma_p, sigma_out)
     n = k.shape[2]
+    nq = q.shape[2]
+    events = q.shape[0] * q.shape[1] * (nq * (nq + 1) // 2 if causal else nq * n)
+    allow = 1.0 + 4.0 * math.sqrt(2.0 / events)
+    assert rms_exact <= math.sqrt(allow * sigma_p ** 2 + sigma_out ** 2), (rms_exact, sigma_p, sigma_out, events)
     bound = np.max(np.abs(v)) * (2.0 ** -4 + n * 2.0 ** -17) + (2.0 ** -8 if out_bf16 else 1e-6) * np.abs(exact) + 1e-6
     assert np.all(np.abs(o - exact) <= bound)
     assert np.max(np.abs(lse - lse_exact) / np.maximum(1.0, np.abs(lse_exact))) <= 5e-4
@@ -80,6 +89,15 @@ CASES = [
     (1, 8, 8, 320, 128, False, "bf16"),
     (1, 4, 1, 512, 128, True, "fp32"),
     (3, 2, 2, 128, 128, True, "bf16"),
+    # ragged N: tails masked; N % 4 != 0 takes the byte-gathered V^T path
+    (1, 1, 1, 1, 64, True, "bf16"),
+    (1, 1, 1, 1, 128, False, "fp32"),
+    (1, 2, 1, 65, 128, True, "bf16"),
+    (2, 4, 2, 100, 64, False, "fp32"),
+    (1, 2, 2, 130, 128, True, "bf16"),
+    (1, 4, 1, 333, 128, False, "bf16"),
+    (1, 2, 1, 1001, 64, True, "fp32"),
+    (1, 3, 3, 700, 128, True, "bf16"),
 ]
 
 

@@ -6,7 +6,7 @@ reproducible case): batch 1-3, 1-8 query heads with a random divisor as the
 number of K/V heads, sequence lengths 1-700 (mostly off the tile grid),
 head dim 64 or 128, causal or not; decode with cache lengths 1-2000 and an
 automatic or random split count; paged decode with random page sizes and
-ragged lengths; the fp8 forward at random multiples of 64 tokens.
+ragged lengths; the fp8 forward at random lengths (any residue mod 4 and 64).
 """
 
 from __future__ import annotations
@@ -154,7 +154,7 @@ def _draw_fp8_cases(n, seed=9300):
     for _ in range(n):
         H = rng.randint(1, 6)
         Hkv = rng.choice([h for h in range(1, H + 1) if H % h == 0])
-        cases.append((rng.randint(1, 2), H, Hkv, 64 * rng.randint(1, 8), rng.choice([64, 128]), rng.random() < 0.6))
+        cases.append((rng.randint(1, 2), H, Hkv, rng.randint(1, 520), rng.choice([64, 128]), rng.random() < 0.6))
     return cases
 
 
