@@ -10,17 +10,25 @@ HIP events on the library's stream time each call inside the step.
 the 2K workload (4*B*H*N^2*d, halved for causal; backward 2.5x that), taken
 over the fwd and bwd calls inside the timed steps.  The decode leg of the same
 steps is reported as achieved HBM GB/s (K and V read once: 2*B*H*L*d*2 bytes).
-A sweep over N = 2K..16K (H=32, B=16384/N, causal) reports forward and
-backward TFLOP/s as the metric's range asks, and the oracle's CPU time on a
-bounded sample is reported as ``cpu_baseline``.
 
-After the sweep, ``next_rows`` reports grouped-query attention (decode with
-8 cache heads for 32 query heads, fwd/bwd with groups of 4), paged-cache
-decodes, batch-1 decode latency, head dim 256 (forward and decode) and the
-fp8 (e4m3) forward.
+Every other measurement warms up for at least 50 ms, then times single calls
+with HIP events until at least 20 calls and 200 ms have passed, and reports
+the median and the minimum:
+  * ``configs``: the five workloads at their own shapes -- the fp32 128-token
+    forward (latency, us), the 16K-token forward against its target of
+    <= 1.75 ms, the 4K-token backward; the 2K forward/backward and the decode
+    come from the step;
+  * ``sweep``: forward and backward TFLOP/s at N = 2K..16K (H=32, B=16384/N);
+  * ``next_rows``: grouped-query attention, paged-cache and batch-1 decodes,
+    head dim 256 (forward, backward, decode) and the fp8 forward;
+  * ``ceilings``: what the chip delivers, from the probe library
+    (libfa_probe.so): MFMA loops on random and constant operands and with one
+    exponential per product, each with the shader clock it ran at, a streaming
+    read, and the clock the library's own forward kernel runs at;
+  * ``cpu_baseline``: the fp64 oracle on the host cores (bounded samples).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-sweep]
-                       [--no-next] [--no-cpu-baseline]
+                       [--no-next] [--no-configs] [--no-ceilings] [--no-cpu-baseline]
        python bench.py --reduce-counters DIR... [--write-traffic]   (host only)
 """
 
@@ -40,6 +48,8 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 flop/clk)
 PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
 PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA (spec)
+PEAK_FP32_MATRIX_TFLOPS = 157.3   # MI355X dense fp32 matrix (spec), for the fp32 workload only
+SPEC_CLOCK_GHZ = 2.4          # the clock the published peaks assume
 
 
 def fwd_flops(B, H, N, d, causal=True):
@@ -55,7 +65,9 @@ def parse():
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-next", action="store_true",
-                    help="skip the grouped-query, paged-cache and head-dim-256 measurements")
+                    help="skip the grouped-query, paged-cache, head-dim-256 and fp8 measurements")
+    ap.add_argument("--no-configs", action="store_true", help="skip the per-workload measurements")
+    ap.add_argument("--no-ceilings", action="store_true", help="skip the probe-library calibration")
     ap.add_argument("--reduce-counters", nargs="+", metavar="DIR",
                     help="host only: summarise rocprofv3 --pmc output of this script and exit")
     ap.add_argument("--write-traffic", action="store_true",
@@ -120,10 +132,16 @@ def run_decode(fa, b, stream):
         raise RuntimeError(fa.fa_status_string(st))
 
 
-def timed_ms(torch, fn, iters, warm_ms=50.0):
-    """Mean milliseconds per call of ``fn`` over ``iters`` back-to-back calls on
-    the current stream, after untimed calls worth at least ``warm_ms`` (the
-    chip's clocks need tens of milliseconds of load to settle)."""
+def timed_stats(torch, fn, min_calls=20, min_ms=200.0, max_calls=4000, warm_ms=50.0):
+    """Median and minimum milliseconds of single calls of ``fn``.
+
+    Untimed calls worth at least ``warm_ms`` come first (the clocks need tens of
+    milliseconds of load to settle).  Then each call is bracketed by its own
+    pair of HIP events on the current stream, in batches between host
+    synchronisations, until at least ``min_calls`` calls and ``min_ms``
+    milliseconds have been timed (at most ``max_calls``).
+    """
+    import statistics
     fn()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -131,18 +149,77 @@ def timed_ms(torch, fn, iters, warm_ms=50.0):
     fn()
     e1.record()
     torch.cuda.synchronize()
-    for _ in range(min(500, max(3, math.ceil(warm_ms / max(e0.elapsed_time(e1), 1e-3))))):
+    est = max(e0.elapsed_time(e1), 1e-3)
+    for _ in range(min(500, max(3, math.ceil(warm_ms / est)))):
         fn()
     torch.cuda.synchronize()
-    e0.record()
-    for _ in range(iters):
-        fn()
-    e1.record()
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / iters
+    times = []
+    while len(times) < max_calls and (len(times) < min_calls or sum(times) < min_ms):
+        batch = min(64, max_calls - len(times))
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(batch)]
+        for a, b in evs:
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        times += [a.elapsed_time(b) for a, b in evs]
+    return {"median_ms": statistics.median(times), "min_ms": min(times), "calls": len(times)}
 
 
-def sweep(torch, fa, W, dev, iters=10):
+def rate_entry(st, work, unit, peak, workload, **extra):
+    """A measurement record: median and min time, the rate at both, and the
+    fraction of ``peak`` at the median.  ``work`` is flops (unit TFLOP/s) or
+    bytes (unit GB/s)."""
+    scale = 1e12 if unit == "TFLOP/s" else 1e9
+    med = work / (st["median_ms"] * 1e-3) / scale
+    best = work / (st["min_ms"] * 1e-3) / scale
+    key = "tflops" if unit == "TFLOP/s" else "GBps"
+    return {"workload": workload, "ms": round(st["median_ms"], 4), "ms_min": round(st["min_ms"], 4),
+            "calls": st["calls"], key: round(med, 1), key + "_best": round(best, 1),
+            "frac": round(med / peak, 4), **extra}
+
+
+def _ok(fa, st):
+    if st != fa.FA_OK:
+        raise RuntimeError(fa.fa_status_string(st))
+
+
+def _fwd_bwd_calls(torch, fa, q, k, v, do, causal, scale, stream):
+    """Closures calling fa_fwd and fa_bwd through the C ABI on resident buffers."""
+    B, H, N, d = q.shape
+    Hkv = k.shape[1]
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    nb = fa.fa_bwd_workspace_bytes(B, H, Hkv, N, d)
+    ws = torch.empty((max(nb, 1),), dtype=torch.uint8, device=q.device)
+
+    def f():
+        _ok(fa, fa.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), fa.FA_BF16, lse.data_ptr(),
+                          B, H, Hkv, N, d, fa.FA_BF16, int(causal), scale, stream))
+
+    def g():
+        _ok(fa, fa.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), fa.FA_BF16, lse.data_ptr(),
+                          do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr(), nb,
+                          B, H, Hkv, N, d, fa.FA_BF16, int(causal), scale, stream))
+    return f, g
+
+
+def _decode_call(torch, fa, q, kc, vc, scale, stream):
+    B, H, _, d = q.shape
+    Hkv, L = kc.shape[1], kc.shape[2]
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    nb = fa.fa_decode_workspace_bytes(B, H, Hkv, L, d, 0)
+    ws = torch.empty((max(nb, 1),), dtype=torch.uint8, device=q.device)
+
+    def f():
+        _ok(fa, fa.fa_decode(q.data_ptr(), kc.data_ptr(), vc.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                             ws.data_ptr(), nb, B, H, Hkv, L, d, fa.FA_BF16, 0, scale, stream))
+    return f
+
+
+def sweep(torch, fa, W, dev):
     """fwd and bwd TFLOP/s at N = 2K..16K, H = 32, B = 16384/N, causal bf16, d = 128."""
     out = []
     stream = torch.cuda.current_stream().cuda_stream
@@ -151,36 +228,67 @@ def sweep(torch, fa, W, dev, iters=10):
         scale = 1.0 / math.sqrt(d)
         seed = 10 + int(math.log2(N // 1024))
         q, k, v, do = W.draw([(B, H, N, d)] * 4, seed, torch.bfloat16, device=dev)
-        o = torch.empty_like(q)
-        lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
-        dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
-        nb = fa.fa_bwd_workspace_bytes(B, H, H, N, d)
-        ws = torch.empty((nb,), dtype=torch.uint8, device=dev)
-
-        def f():
-            fa.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), fa.FA_BF16, lse.data_ptr(),
-                      B, H, H, N, d, fa.FA_BF16, 1, scale, stream)
-
-        def g():
-            fa.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), fa.FA_BF16, lse.data_ptr(),
-                      do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr(), nb,
-                      B, H, H, N, d, fa.FA_BF16, 1, scale, stream)
-
+        f, g = _fwd_bwd_calls(torch, fa, q, k, v, do, True, scale, stream)
         res = {"N": N, "B": B, "H": H, "d": d}
+        wl = f"B{B} H{H} N{N} d{d} causal"
+        f()
         for name, fn, mult in (("fwd", f, 1.0), ("bwd", g, 2.5)):
-            f()
-            ms = timed_ms(torch, fn, iters)
-            tf = mult * fwd_flops(B, H, N, d) / (ms * 1e-3) / 1e12
-            res[name] = {"ms": round(ms, 4), "tflops": round(tf, 1),
-                         "frac_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+            res[name] = rate_entry(timed_stats(torch, fn), mult * fwd_flops(B, H, N, d), "TFLOP/s",
+                                   PEAK_BF16_TFLOPS, wl)
         log(f"sweep N={N}: fwd {res['fwd']['tflops']} TFLOP/s, bwd {res['bwd']['tflops']} TFLOP/s")
         out.append(res)
-        del q, k, v, do, o, lse, dq, dk, dv, ws
+        del q, k, v, do, f, g
         torch.cuda.empty_cache()
     return out
 
 
-def gqa_measure(torch, fa, W, dev, iters=20):
+def configs_measure(torch, fa, W, dev):
+    """The workloads at their own shapes: the fp32 128-token forward (latency),
+    the 16K-token forward (target <= 1.75 ms, >= 50% of the bf16 MFMA peak) and
+    the 4K-token backward (O and LSE from fa_fwd).  The 2K forward/backward and
+    the 8K-cache decode are the step's own legs."""
+    stream = torch.cuda.current_stream().cuda_stream
+    out = {}
+    w = W.WORKLOADS["fwd_fp32_b1h1n128d64"]
+    q, k, v = W.make_inputs(w, dev)
+    o, lse = torch.empty_like(q), torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    st = timed_stats(torch, lambda: _ok(fa, fa.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                                      fa.FA_FP32, lse.data_ptr(), w.B, w.H, w.H, w.N, w.d,
+                                                      fa.FA_FP32, 0, w.scale, stream)), max_calls=2000)
+    fl = fwd_flops(w.B, w.H, w.N, w.d, causal=False)
+    out["C1"] = {"workload": "fwd fp32 B1 H1 N128 d64 non-causal", "us": round(st["median_ms"] * 1e3, 2),
+                 "us_min": round(st["min_ms"] * 1e3, 2), "calls": st["calls"],
+                 "tflops": round(fl / (st["median_ms"] * 1e-3) / 1e12, 3),
+                 "note": "launch-latency bound (4.19 MFLOP); the fp32 matrix peak is "
+                         f"{PEAK_FP32_MATRIX_TFLOPS} TFLOP/s, for information only"}
+    log(f"C1 {out['C1']['workload']}: {out['C1']['us']} us")
+
+    w = W.WORKLOADS["fwd_causal_bf16_b1h32n16384d128"]
+    q, k, v = W.make_inputs(w, dev)
+    f, _ = _fwd_bwd_calls(torch, fa, q, k, v, q, True, w.scale, stream)
+    e = rate_entry(timed_stats(torch, f), fwd_flops(w.B, w.H, w.N, w.d), "TFLOP/s", PEAK_BF16_TFLOPS,
+                   "fwd causal bf16 B1 H32 N16384 d128 (inputs N(0,1)*0.5)")
+    e["target_ms"] = 1.75
+    e["target_met"] = e["ms"] <= 1.75
+    out["C3"] = e
+    log(f"C3 {e['workload']}: {e['ms']} ms (min {e['ms_min']}), {e['tflops']} TFLOP/s")
+    del q, k, v, f
+
+    w = W.WORKLOADS["bwd_causal_bf16_b2h16n4096d128"]
+    q, k, v, do = W.make_inputs(w, dev)
+    f, g = _fwd_bwd_calls(torch, fa, q, k, v, do, True, w.scale, stream)
+    f()
+    out["C4"] = rate_entry(timed_stats(torch, g), 2.5 * fwd_flops(w.B, w.H, w.N, w.d), "TFLOP/s",
+                           PEAK_BF16_TFLOPS, "bwd causal bf16 B2 H16 N4096 d128 (O, LSE from fa_fwd)")
+    out["C4_fwd"] = rate_entry(timed_stats(torch, f), fwd_flops(w.B, w.H, w.N, w.d), "TFLOP/s",
+                               PEAK_BF16_TFLOPS, "fwd causal bf16 B2 H16 N4096 d128")
+    log(f"C4 {out['C4']['workload']}: {out['C4']['ms']} ms, {out['C4']['tflops']} TFLOP/s")
+    del q, k, v, do, f, g
+    torch.cuda.empty_cache()
+    return out
+
+
+def gqa_measure(torch, fa, W, dev):
     """Grouped-query attention (K/V heads shared by groups of query heads).
 
     decode: B64 H32 Hkv8 L8192 d128 (groups of 4); each cache head is read
@@ -189,56 +297,27 @@ def gqa_measure(torch, fa, W, dev, iters=20):
     """
     stream = torch.cuda.current_stream().cuda_stream
     out = {}
-
-    def timed(fn):
-        return timed_ms(torch, fn, iters)
-
     B, H, Hkv, L, d = 64, 32, 8, 8192, 128
-    q, kc, vc = W.make_gqa(B, H, Hkv, 1, d, "bf16", seed=20, device=dev, Nk=L)
-    o = torch.empty_like(q)
-    lse = torch.empty((B, H), dtype=torch.float32, device=dev)
-    nb = fa.fa_decode_workspace_bytes(B, H, Hkv, L, d, 0)
-    ws = torch.empty((nb,), dtype=torch.uint8, device=dev)
     scale = 1.0 / math.sqrt(d)
-    ms = timed(lambda: fa.fa_decode(q.data_ptr(), kc.data_ptr(), vc.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                                    ws.data_ptr(), nb, B, H, Hkv, L, d, fa.FA_BF16, 0, scale, stream))
-    byt = 2.0 * B * Hkv * L * d * 2
-    gbs = byt / (ms * 1e-3) / 1e9
-    out["decode"] = {"workload": f"B{B} H{H} Hkv{Hkv} L{L} d{d}", "ms": round(ms, 4), "GBps": round(gbs, 1),
-                     "bound": "hbm", "frac": round(gbs / PEAK_HBM_GBPS, 4), "algorithmic_bytes": byt,
-                     "splits": fa.fa_decode_num_splits(B, H, Hkv, L, d)}
-    log(f"gqa decode {out['decode']['workload']}: {ms:.4f} ms, {gbs:.1f} GB/s")
-    del q, kc, vc, o, ws
+    q, kc, vc = W.make_gqa(B, H, Hkv, 1, d, "bf16", seed=20, device=dev, Nk=L)
+    out["decode"] = rate_entry(timed_stats(torch, _decode_call(torch, fa, q, kc, vc, scale, stream)),
+                               2.0 * B * Hkv * L * d * 2, "GB/s", PEAK_HBM_GBPS, f"B{B} H{H} Hkv{Hkv} L{L} d{d}",
+                               bound="hbm", splits=fa.fa_decode_num_splits(B, H, Hkv, L, d))
+    log(f"gqa decode {out['decode']['workload']}: {out['decode']['ms']} ms, {out['decode']['GBps']} GB/s")
+    del q, kc, vc
 
     B, H, Hkv, N = 4, 16, 4, 2048
     q, k, v, do = W.make_gqa(B, H, Hkv, N, d, "bf16", seed=21, with_dout=True, device=dev)
-    o = torch.empty_like(q)
-    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    nb = fa.fa_bwd_workspace_bytes(B, H, Hkv, N, d)
-    ws = torch.empty((nb,), dtype=torch.uint8, device=dev)
-
-    def f():
-        fa.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), fa.FA_BF16, lse.data_ptr(),
-                  B, H, Hkv, N, d, fa.FA_BF16, 1, scale, stream)
-
-    def g():
-        fa.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), fa.FA_BF16, lse.data_ptr(),
-                  do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr(), nb,
-                  B, H, Hkv, N, d, fa.FA_BF16, 1, scale, stream)
-
-    ff = fwd_flops(B, H, N, d)
+    f, g = _fwd_bwd_calls(torch, fa, q, k, v, do, True, scale, stream)
+    f()
     for name, fn, mult in (("fwd", f, 1.0), ("bwd", g, 2.5)):
-        f()
-        ms = timed(fn)
-        tf = mult * ff / (ms * 1e-3) / 1e12
-        out[name] = {"workload": f"B{B} H{H} Hkv{Hkv} N{N} d{d} causal", "ms": round(ms, 4),
-                     "tflops": round(tf, 1), "bound": "mfma", "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
-        log(f"gqa {name} {out[name]['workload']}: {ms:.4f} ms, {tf:.1f} TFLOP/s")
+        out[name] = rate_entry(timed_stats(torch, fn), mult * fwd_flops(B, H, N, d), "TFLOP/s", PEAK_BF16_TFLOPS,
+                               f"B{B} H{H} Hkv{Hkv} N{N} d{d} causal", bound="mfma")
+        log(f"gqa {name} {out[name]['workload']}: {out[name]['ms']} ms, {out[name]['tflops']} TFLOP/s")
     return out
 
 
-def paged_measure(torch, fa, dev, iters=20):
+def paged_measure(torch, fa, dev):
     """Decode against a paged cache: B64 H32 L8192 d128, 64-token pages of one
     pool in shuffled order, every sequence full length; multi-head (32 cache
     heads, per-head kernel) and grouped (8 cache heads, grouped kernel).
@@ -262,24 +341,18 @@ def paged_measure(torch, fa, dev, iters=20):
         ws = torch.empty((nb,), dtype=torch.uint8, device=dev)
 
         def fn():
-            st = fa.fa_decode_paged(q.data_ptr(), kp.data_ptr(), vp.data_ptr(), table.data_ptr(), lens.data_ptr(),
-                                    o.data_ptr(), lse.data_ptr(), ws.data_ptr(), nb, B, H, Hkv, pages, ps,
-                                    L // ps, d, fa.FA_BF16, 0, scale, stream)
-            if st != fa.FA_OK:
-                raise RuntimeError(fa.fa_status_string(st))
-        ms = timed_ms(torch, fn, iters)
-        byt = 2.0 * B * Hkv * L * d * 2
-        gbs = byt / (ms * 1e-3) / 1e9
-        out[name] = {"workload": f"B{B} H{H} Hkv{Hkv} L{L} d{d} page{ps}", "ms": round(ms, 4),
-                     "GBps": round(gbs, 1), "bound": "hbm", "frac": round(gbs / PEAK_HBM_GBPS, 4),
-                     "algorithmic_bytes": byt}
-        log(f"paged decode {out[name]['workload']}: {ms:.4f} ms, {gbs:.1f} GB/s")
+            _ok(fa, fa.fa_decode_paged(q.data_ptr(), kp.data_ptr(), vp.data_ptr(), table.data_ptr(),
+                                       lens.data_ptr(), o.data_ptr(), lse.data_ptr(), ws.data_ptr(), nb, B, H, Hkv,
+                                       pages, ps, L // ps, d, fa.FA_BF16, 0, scale, stream))
+        out[name] = rate_entry(timed_stats(torch, fn), 2.0 * B * Hkv * L * d * 2, "GB/s", PEAK_HBM_GBPS,
+                               f"B{B} H{H} Hkv{Hkv} L{L} d{d} page{ps}", bound="hbm")
+        log(f"paged decode {out[name]['workload']}: {out[name]['ms']} ms, {out[name]['GBps']} GB/s")
         del q, kp, vp, table, lens, o, lse, ws
         torch.cuda.empty_cache()
     return out
 
 
-def fp8_measure(torch, fa, W, dev, iters=30):
+def fp8_measure(torch, fa, W, dev):
     """FP8 (e4m3) forward, causal, d = 128, at the 2K workload (B4 H16 N2048) and
     the long-context one (B1 H32 N16384); same flop formula, against the fp8
     MFMA peak."""
@@ -293,19 +366,16 @@ def fp8_measure(torch, fa, W, dev, iters=30):
         lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
 
         def f():
-            st = fa.fa_fwd_fp8(q8.data_ptr(), k8.data_ptr(), vt8.data_ptr(), qs, ks, vs, o.data_ptr(), fa.FA_BF16,
-                               lse.data_ptr(), B, H, H, N, d, 1, scale, stream)
-            assert st == fa.FA_OK, fa.fa_status_string(st)
-        ms = timed_ms(torch, f, iters)
-        tf = fwd_flops(B, H, N, d) / (ms * 1e-3) / 1e12
-        out[key] = {"workload": f"B{B} H{H} N{N} d{d} causal, e4m3 in, bf16 out", "ms": round(ms, 4),
-                    "tflops": round(tf, 1), "bound": "mfma", "frac": round(tf / PEAK_FP8_TFLOPS, 4)}
-        log(f"fp8 fwd {out[key]['workload']}: {ms:.4f} ms, {tf:.1f} TFLOP/s")
+            _ok(fa, fa.fa_fwd_fp8(q8.data_ptr(), k8.data_ptr(), vt8.data_ptr(), qs, ks, vs, o.data_ptr(),
+                                  fa.FA_BF16, lse.data_ptr(), B, H, H, N, d, 1, scale, stream))
+        out[key] = rate_entry(timed_stats(torch, f), fwd_flops(B, H, N, d), "TFLOP/s", PEAK_FP8_TFLOPS,
+                              f"B{B} H{H} N{N} d{d} causal, e4m3 in, bf16 out", bound="mfma")
+        log(f"fp8 fwd {out[key]['workload']}: {out[key]['ms']} ms, {out[key]['tflops']} TFLOP/s")
         del q8, k8, vt8, o, lse
     return out
 
 
-def small_batch_decode_measure(torch, fa, W, dev, iters=200):
+def small_batch_decode_measure(torch, fa, W, dev):
     """Decode steps at batch 1 (latency-bound: a few MB of cache), with 8
     cache heads (grouped kernel) and 32 (per-head kernel), L = 4K and 16K."""
     stream = torch.cuda.current_stream().cuda_stream
@@ -313,101 +383,246 @@ def small_batch_decode_measure(torch, fa, W, dev, iters=200):
     for key, (Hkv, L) in (("gqa_l4096", (8, 4096)), ("gqa_l16384", (8, 16384)), ("mha_l16384", (32, 16384))):
         B, H, d = 1, 32, 128
         q, kc, vc = W.make_gqa(B, H, Hkv, 1, d, "bf16", seed=61 + L // 4096 + Hkv, device=dev, Nk=L)
-        o = torch.empty_like(q)
-        lse = torch.empty((B, H), dtype=torch.float32, device=dev)
-        nb = fa.fa_decode_workspace_bytes(B, H, Hkv, L, d, 0)
-        ws = torch.empty((nb,), dtype=torch.uint8, device=dev)
-        scale = 1.0 / math.sqrt(d)
-        ms = timed_ms(torch, lambda: fa.fa_decode(q.data_ptr(), kc.data_ptr(), vc.data_ptr(), o.data_ptr(),
-                                                  lse.data_ptr(), ws.data_ptr(), nb, B, H, Hkv, L, d, fa.FA_BF16,
-                                                  0, scale, stream), iters)
+        st = timed_stats(torch, _decode_call(torch, fa, q, kc, vc, 1.0 / math.sqrt(d), stream), max_calls=2000)
         byt = 2.0 * B * Hkv * L * d * 2
-        out[key] = {"workload": f"B{B} H{H} Hkv{Hkv} L{L} d{d}", "us": round(ms * 1e3, 2),
-                    "GBps": round(byt / (ms * 1e-3) / 1e9, 1),
+        out[key] = {"workload": f"B{B} H{H} Hkv{Hkv} L{L} d{d}", "us": round(st["median_ms"] * 1e3, 2),
+                    "us_min": round(st["min_ms"] * 1e3, 2), "calls": st["calls"],
+                    "GBps": round(byt / (st["median_ms"] * 1e-3) / 1e9, 1),
                     "splits": fa.fa_decode_num_splits(B, H, Hkv, L, d)}
         log(f"small-batch decode {out[key]['workload']}: {out[key]['us']} us, {out[key]['GBps']} GB/s")
     return out
 
 
-def d256_measure(torch, fa, W, dev, iters=10):
-    """Head dim 256: causal bf16 forward at B4 H16 N4096 and decode at
-    B64 H16 L4096 (multi-head) -- same flop formula / bytes as at d = 128."""
+def d256_measure(torch, fa, W, dev):
+    """Head dim 256: causal bf16 forward and backward at B4 H16 N4096, and
+    decode at B64 H16 L4096 (multi-head) -- same flop formula / bytes as at
+    d = 128."""
     stream = torch.cuda.current_stream().cuda_stream
     out = {}
-
-    def timed(fn):
-        return timed_ms(torch, fn, iters)
-
     B, H, N, d = 4, 16, 4096, 256
     scale = 1.0 / math.sqrt(d)
-    q, k, v = W.make_custom(B, H, N, d, "bf16", seed=40, device=dev)
-    o = torch.empty_like(q)
-    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
-    ms = timed(lambda: fa.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), fa.FA_BF16,
-                                 lse.data_ptr(), B, H, H, N, d, fa.FA_BF16, 1, scale, stream))
-    tf = fwd_flops(B, H, N, d) / (ms * 1e-3) / 1e12
-    out["fwd"] = {"workload": f"B{B} H{H} N{N} d{d} causal", "ms": round(ms, 4), "tflops": round(tf, 1),
-                  "bound": "mfma", "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
-    log(f"d256 fwd {out['fwd']['workload']}: {ms:.4f} ms, {tf:.1f} TFLOP/s")
-    del q, k, v, o, lse
+    q, k, v, do = W.make_custom(B, H, N, d, "bf16", seed=40, n_tensors=4, device=dev)
+    f, g = _fwd_bwd_calls(torch, fa, q, k, v, do, True, scale, stream)
+    f()
+    for name, fn, mult in (("fwd", f, 1.0), ("bwd", g, 2.5)):
+        out[name] = rate_entry(timed_stats(torch, fn), mult * fwd_flops(B, H, N, d), "TFLOP/s", PEAK_BF16_TFLOPS,
+                               f"B{B} H{H} N{N} d{d} causal", bound="mfma")
+        log(f"d256 {name} {out[name]['workload']}: {out[name]['ms']} ms, {out[name]['tflops']} TFLOP/s")
+    del q, k, v, do, f, g
 
     B, H, L = 64, 16, 4096
     q, kc, vc = W.make_custom(B, H, 1, d, "bf16", seed=41, device=dev, Nk=L)
-    o = torch.empty_like(q)
-    lse = torch.empty((B, H), dtype=torch.float32, device=dev)
-    nb = fa.fa_decode_workspace_bytes(B, H, H, L, d, 0)
-    ws = torch.empty((nb,), dtype=torch.uint8, device=dev)
-    ms = timed(lambda: fa.fa_decode(q.data_ptr(), kc.data_ptr(), vc.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                                    ws.data_ptr(), nb, B, H, H, L, d, fa.FA_BF16, 0, scale, stream))
-    byt = 2.0 * B * H * L * d * 2
-    gbs = byt / (ms * 1e-3) / 1e9
-    out["decode"] = {"workload": f"B{B} H{H} L{L} d{d}", "ms": round(ms, 4), "GBps": round(gbs, 1),
-                     "bound": "hbm", "frac": round(gbs / PEAK_HBM_GBPS, 4), "algorithmic_bytes": byt}
-    log(f"d256 decode {out['decode']['workload']}: {ms:.4f} ms, {gbs:.1f} GB/s")
+    out["decode"] = rate_entry(timed_stats(torch, _decode_call(torch, fa, q, kc, vc, scale, stream)),
+                               2.0 * B * H * L * d * 2, "GB/s", PEAK_HBM_GBPS, f"B{B} H{H} L{L} d{d}", bound="hbm")
+    log(f"d256 decode {out['decode']['workload']}: {out['decode']['ms']} ms, {out['decode']['GBps']} GB/s")
     return out
 
 
-def cpu_baseline(W, min_seconds=10.0, max_passes=8):
-    """The fp64 oracle, as it stands, on the 2K training workload.
+def ceilings(torch, dev, fwd_q=None):
+    """Calibration with the probe library (outside every timed step).
 
-    One pass is ref_fwd + ref_bwd over all B*H = 64 heads of B4 H16 N2048 d128
-    (causal); passes repeat until ``min_seconds`` have elapsed, and the rate is
-    the mean over them.
+    MFMA: a register-only v_mfma_f32_32x32x16_bf16 loop at two waves per SIMD
+    on every CU, on random bf16 operands, on the same with one v_exp_f32 per
+    product, and on constant operands; each with the shader clock the chip ran
+    at (s_memtime cycles over the 100 MHz s_memrealtime, per workgroup).  HBM:
+    a streaming read of 4 GiB.  Clock of the library's own forward kernel at
+    B1 H32 N16384 d128 causal (its per-workgroup clock record on), and its
+    MFMA utilisation at that clock.
+    """
+    import ctypes
+    import statistics
+    path = os.path.join(ROOT, "exact_io_aware_11_amd", "libfa_probe.so")
+    if not os.path.exists(path):
+        log(f"no {path}: ceilings skipped (build with exact_io_aware_11_amd/build.py)")
+        return None
+    lib = ctypes.CDLL(path)
+    P, I, F, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.fa_probe_mfma.argtypes = [I, P, I, I, P, P, P]
+    lib.fa_probe_stream_read.argtypes = [P, Z, I, P, P]
+    lib.fa_probe_fwd_clock.argtypes = [P, P, P, P, P, I, I, I, F, P, P]
+    stream = torch.cuda.current_stream().cuda_stream
+    out = {}
+    grid = 512                                   # two workgroups of 4 waves per CU
+    nops = grid * 256 * 8 * 8                    # 8 operand vectors of 8 bf16 per lane
+    g = torch.Generator(device=dev)
+    g.manual_seed(77)
+    ops_rand = torch.randn((nops,), generator=g, device=dev).to(torch.bfloat16)
+    ops_const = torch.full((nops,), 1.0, dtype=torch.bfloat16, device=dev)
+    sink = torch.empty((grid * 256,), dtype=torch.float32, device=dev)
+    clk = torch.zeros((2 * grid,), dtype=torch.int64, device=dev)
+
+    def clock_ghz(c):
+        c = c.view(-1, 2).double()
+        return float(c[:, 0].sum() / c[:, 1].sum()) * 0.1
+
+    for mode, name, ops in ((0, "mfma_bf16_random", ops_rand), (1, "mfma_bf16_random_exp", ops_rand),
+                            (2, "mfma_bf16_constant", ops_const)):
+        iters = 60000
+        run = lambda: lib.fa_probe_mfma(mode, ops.data_ptr(), iters, grid, sink.data_ptr(), clk.data_ptr(), stream)
+        st = timed_stats(torch, run, min_calls=5, min_ms=100.0, max_calls=50, warm_ms=100.0)
+        flops = grid * 4.0 * iters * 4 * 2 * 32 * 32 * 16
+        tf = flops / (st["median_ms"] * 1e-3) / 1e12
+        ghz = clock_ghz(clk)
+        out[name] = {"tflops": round(tf, 1), "frac_spec": round(tf / PEAK_BF16_TFLOPS, 4), "clock_ghz": round(ghz, 3),
+                     "ms": round(st["median_ms"], 3)}
+        log(f"ceiling {name}: {tf:.1f} TFLOP/s at {ghz:.3f} GHz")
+
+    nbytes = 4 << 30
+    buf = torch.empty((nbytes,), dtype=torch.uint8, device=dev)
+    rsink = torch.empty((2048 * 256,), dtype=torch.int32, device=dev)
+    st = timed_stats(torch, lambda: lib.fa_probe_stream_read(buf.data_ptr(), nbytes, 2048, rsink.data_ptr(), stream),
+                     min_calls=20, min_ms=100.0)
+    gbs = nbytes / (st["median_ms"] * 1e-3) / 1e9
+    out["stream_read"] = {"GBps": round(gbs, 1), "frac_spec": round(gbs / PEAK_HBM_GBPS, 4),
+                          "bytes": nbytes, "ms": round(st["median_ms"], 3)}
+    log(f"ceiling stream read: {gbs:.1f} GB/s")
+    del buf, ops_rand, ops_const
+
+    if fwd_q is not None:
+        q, k, v = fwd_q
+        B, H, N, d = q.shape
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+        fclk = torch.zeros((2 * ((N + 127) // 128) * B * H,), dtype=torch.int64, device=dev)
+        scale = 1.0 / math.sqrt(d)
+        run = lambda: lib.fa_probe_fwd_clock(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                             lse.data_ptr(), B, H, N, scale, fclk.data_ptr(), stream)
+        st = timed_stats(torch, run)
+        ghz = clock_ghz(fclk)
+        tf = fwd_flops(B, H, N, d) / (st["median_ms"] * 1e-3) / 1e12
+        at_clock = PEAK_BF16_TFLOPS * ghz / SPEC_CLOCK_GHZ
+        out["fwd_clock"] = {"workload": f"fwd causal bf16 B{B} H{H} N{N} d{d}", "tflops": round(tf, 1),
+                            "clock_ghz": round(ghz, 3), "peak_at_clock": round(at_clock, 1),
+                            "mfma_util_at_clock": round(tf / at_clock, 4)}
+        log(f"forward clock: {ghz:.3f} GHz, {tf:.1f} TFLOP/s, {100 * tf / at_clock:.1f}% of the peak at that clock")
+    return out
+
+
+def host_info():
+    """CPU model, core counts and the BLAS thread count the oracle runs with."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=None)
+    except Exception:
+        pass
+    return {"cpu_model": model, "os_cpu_count": os.cpu_count(), "affinity_cores": len(os.sched_getaffinity(0)),
+            "blas_threads": threads}
+
+
+def cpu_baseline(W, c3_inputs=None, c5_inputs=None, c5_slices=8):
+    """The fp64 oracle, as it stands, on the host cores (about 20-30 s in all).
+
+    Every call materialises the full N x N scores (the oracle's definition), so
+    rates use the same causal flop count as the GPU.
+      C1: ref_fwd on the fp32 128-token head, on all cores and on one.
+      C2: ref_fwd and ref_bwd over the whole 2K workload (64 heads); the
+          headline ``value`` is its fwd+bwd TFLOP/s.
+      C4: ref_fwd and ref_bwd over the whole 4K backward workload (32 heads).
+      C3: the parity check's 64 sampled rows for all 32 heads (ref_fwd_rows),
+          and one whole head, reported times 32 as *extrapolated*.
+      C5: ref_decode on ``c5_slices`` batch slices of the 8K cache (read back
+          from the device), reported times 64 / c5_slices as *extrapolated*.
     """
     import numpy as np
     import torch
 
-    from oracle import ref_bwd, ref_fwd
-    t = W.WORKLOADS["fwd_causal_bf16_b4h16n2048d128"]
-    q, k, v, do = W.draw([(t.B, t.H, t.N, t.d)] * 4, t.seed, torch.bfloat16, device="cpu")
-    q, k, v, do = (x.float().numpy().astype(np.float64) for x in (q, k, v, do))
-    threads = None
+    from oracle import ref_bwd, ref_decode, ref_fwd, ref_fwd_rows
+
+    def to64(x):
+        return x.float().cpu().numpy().astype(np.float64)
+
+    def secs(fn):
+        t0 = time.perf_counter()
+        fn()
+        return time.perf_counter() - t0
+
+    def per_call(fn, min_s=0.3):
+        n, t0 = 0, time.perf_counter()
+        while True:
+            fn()
+            n += 1
+            if time.perf_counter() - t0 >= min_s:
+                return (time.perf_counter() - t0) / n
+
+    info = host_info()
+    res = {}
+    t_all = time.perf_counter()
+
+    w = W.WORKLOADS["fwd_fp32_b1h1n128d64"]
+    q, k, v = (to64(x) for x in W.make_inputs(w, "cpu"))
+    c1 = {"all_cores_us": round(1e6 * per_call(lambda: ref_fwd(q, k, v, False, w.scale)), 1)}
     try:
-        from threadpoolctl import threadpool_info
-        info = threadpool_info()
-        threads = max((i.get("num_threads", 1) for i in info), default=None)
-    except Exception:
-        pass
-    passes = 0
-    t0 = time.perf_counter()
-    while passes < max_passes:
-        ref_fwd(q, k, v, True, t.scale)
-        ref_bwd(q, k, v, do, True, t.scale)
-        passes += 1
-        if time.perf_counter() - t0 >= min_seconds:
-            break
-    secs = time.perf_counter() - t0
-    flops = passes * 3.5 * fwd_flops(t.B, t.H, t.N, t.d)
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(1):
+            c1["one_core_us"] = round(1e6 * per_call(lambda: ref_fwd(q, k, v, False, w.scale)), 1)
+    except ImportError:
+        c1["one_core_us"] = None
+    res["C1"] = c1
+    log(f"cpu oracle C1: {c1}")
+
+    for key, name in (("C2", "fwd_causal_bf16_b4h16n2048d128"), ("C4", "bwd_causal_bf16_b2h16n4096d128")):
+        w = W.WORKLOADS[name]
+        q, k, v, do = (to64(x) for x in W.make_inputs(w, "cpu", with_dout=True))
+        tf = secs(lambda: ref_fwd(q, k, v, True, w.scale))
+        tb = secs(lambda: ref_bwd(q, k, v, do, True, w.scale))
+        fl = fwd_flops(w.B, w.H, w.N, w.d)
+        res[key] = {"workload": f"B{w.B} H{w.H} N{w.N} d{w.d} causal", "fwd_s": round(tf, 3), "bwd_s": round(tb, 3),
+                    "fwd_tflops": round(fl / tf / 1e12, 5), "fwd_bwd_tflops": round(3.5 * fl / (tf + tb) / 1e12, 5)}
+        log(f"cpu oracle {key}: {res[key]}")
+        del q, k, v, do
+
+    if c3_inputs is not None:
+        w = W.WORKLOADS["fwd_causal_bf16_b1h32n16384d128"]
+        q, k, v = (to64(x) for x in c3_inputs)
+        rows = W.sample_rows(w.N, w.extra["sample_rows"], w.extra["row_seed"])
+        tr = secs(lambda: ref_fwd_rows(q, k, v, True, w.scale, rows))
+        th = secs(lambda: ref_fwd(q[:, :1], k[:, :1], v[:, :1], True, w.scale))
+        fl = fwd_flops(w.B, w.H, w.N, w.d)
+        res["C3"] = {"workload": f"B{w.B} H{w.H} N{w.N} d{w.d} causal", "rows_check_s": round(tr, 3),
+                     "rows": len(rows), "one_head_s": round(th, 3), "whole_s_extrapolated": round(32 * th, 2),
+                     "fwd_tflops_extrapolated": round(fl / (32 * th) / 1e12, 5),
+                     "note": "whole-workload time extrapolated from one head x 32"}
+        log(f"cpu oracle C3: {res['C3']}")
+        del q, k, v
+
+    if c5_inputs is not None:
+        w = W.WORKLOADS["decode_bf16_b64h32l8192d128"]
+        qd, kc, vc = c5_inputs
+        n = min(c5_slices, w.B)
+        t = 0.0
+        for bi in range(n):
+            t += secs(lambda: ref_decode(to64(qd[bi:bi + 1]), to64(kc[bi:bi + 1]), to64(vc[bi:bi + 1]), w.scale))
+        whole = t * w.B / n
+        byt = 2.0 * w.B * w.H * w.N * w.d * 2
+        res["C5"] = {"workload": f"B{w.B} H{w.H} L{w.N} d{w.d}", "slices_timed": n, "slices_s": round(t, 3),
+                     "whole_s_extrapolated": round(whole, 2), "GBps_extrapolated": round(byt / whole / 1e9, 3),
+                     "note": f"per batch slice (device read-back, fp64 widening, ref_decode), "
+                             f"{n} of {w.B} slices timed and scaled"}
+        log(f"cpu oracle C5: {res['C5']}")
+
+    total = time.perf_counter() - t_all
+    c2 = res["C2"]
     return {
-        "value": round(flops / secs / 1e12, 5),
+        "value": c2["fwd_bwd_tflops"],
         "unit": "TFLOP/s",
-        "cores": threads or os.cpu_count(),
+        "cores": info["blas_threads"] or info["affinity_cores"],
         "kind": "oracle",
-        "sample": f"oracle ref_fwd + ref_bwd (fp64, full N x N scores) on the whole B4 H16 N2048 d128 "
-                  f"causal workload, {passes} pass(es) in {secs:.2f} s; rate uses the same causal flop "
-                  "count as the GPU",
-        "seconds": round(secs, 3),
-        "affinity_cores": len(os.sched_getaffinity(0)),
+        "sample": "fp64 oracle (full N x N scores): ref_fwd + ref_bwd once over the whole B4 H16 N2048 d128 causal "
+                  "workload (the headline value, counted with the GPU's causal flops); per-workload figures in "
+                  "configs (C3 and C5 partly extrapolated, as labelled)",
+        "seconds": round(total, 2),
+        **info,
+        "configs": res,
     }
 
 
@@ -436,15 +651,17 @@ def _step_kernels():
 
 
 def kernel_digest(src, csrc=None):
-    """SHA-256 of what a kernel is compiled from: its .hip file and the two
-    shared headers, with comments and whitespace removed (so a comment edit
+    """SHA-256 of what a kernel is compiled from: its .hip file (with the
+    forward's kernel header) and the two shared headers, with comments and
+    whitespace removed (so a comment edit
     keeps a traffic record valid, while any code change in the file or the
     headers invalidates it)."""
     import hashlib
     import re
     csrc = csrc or os.path.join(ROOT, "exact_io_aware_11_amd", "csrc")
     h = hashlib.sha256()
-    for name in (src, "fa_common.hpp", "fa_internal.hpp"):
+    extra = ("fa_fwd_kernel.hpp",) if src == "fa_fwd.hip" else ()
+    for name in (src,) + extra + ("fa_common.hpp", "fa_internal.hpp"):
         with open(os.path.join(csrc, name)) as fh:
             text = fh.read()
         text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
@@ -617,7 +834,11 @@ def main():
             ev[name].append((e0, e1))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms = {n: sum(a.elapsed_time(c) for a, c in ev[n]) / args.steps for n in active}
+    import statistics
+    per = {n: [a.elapsed_time(c) for a, c in ev[n]] for n in active}
+    ms = {n: sum(per[n]) / args.steps for n in active}
+    med = {n: statistics.median(per[n]) for n in active}
+    mins = {n: min(per[n]) for n in active}
     log("per-call ms: " + ", ".join(f"{n} {ms[n]:.4f}" for n in active))
 
     t, dc = b.w_tr, b.w_dec
@@ -628,14 +849,16 @@ def main():
     roofs = []
     if "fwd" in ms:
         tf = f_fwd / (ms["fwd"] * 1e-3) / 1e12
-        parts["fwd"] = {"ms": round(ms["fwd"], 4), "tflops": round(tf, 1)}
+        parts["fwd"] = {"ms": round(ms["fwd"], 4), "ms_median": round(med["fwd"], 4), "ms_min": round(mins["fwd"], 4),
+                        "tflops": round(tf, 1)}
         roofs.append({"kernel": "fwd_bf16_kernel<128,causal>", "bound": "mfma", "achieved": round(tf, 1),
                       "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
                       "traffic": traffic_record("fwd"), "ms": ms["fwd"],
                       "per_launch": f"{f_fwd:.4g} flop (4*B*H*N^2*d/2 at B4 H16 N2048 d128)"})
     if "bwd" in ms:
         tf = f_bwd / (ms["bwd"] * 1e-3) / 1e12
-        parts["bwd"] = {"ms": round(ms["bwd"], 4), "tflops": round(tf, 1)}
+        parts["bwd"] = {"ms": round(ms["bwd"], 4), "ms_median": round(med["bwd"], 4), "ms_min": round(mins["bwd"], 4),
+                        "tflops": round(tf, 1)}
         tr = [traffic_record("bwd_dkdv"), traffic_record("bwd_dq")]
         roofs.append({"kernel": "fa_bwd (bwd_prep + bwd_dkdv_kernel<128,causal> + bwd_dq_kernel<128,causal>)",
                       "bound": "mfma", "achieved": round(tf, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
@@ -644,7 +867,8 @@ def main():
                       "ms": ms["bwd"], "per_launch": f"{f_bwd:.4g} flop (2.5x forward)"})
     if "decode" in ms:
         gbs = dec_bytes / (ms["decode"] * 1e-3) / 1e9
-        parts["decode"] = {"ms": round(ms["decode"], 4), "GBps": round(gbs, 1), "splits": b.splits}
+        parts["decode"] = {"ms": round(ms["decode"], 4), "ms_median": round(med["decode"], 4),
+                           "ms_min": round(mins["decode"], 4), "GBps": round(gbs, 1), "splits": b.splits}
         roofs.append({"kernel": "fa_decode (decode_split_kernel<128> + merge)", "bound": "hbm",
                       "achieved": round(gbs, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                       "frac": round(gbs / PEAK_HBM_GBPS, 4), "traffic": traffic_record("decode"),
@@ -654,6 +878,11 @@ def main():
     tr_ms = ms.get("fwd", 0.0) + ms.get("bwd", 0.0)
     tr_flops = (f_fwd if "fwd" in ms else 0.0) + (f_bwd if "bwd" in ms else 0.0)
     value = tr_flops / (tr_ms * 1e-3) / 1e12 if tr_ms > 0 else 0.0
+
+    configs = None
+    if not args.no_configs:
+        log("workloads at their own shapes")
+        configs = configs_measure(torch, fa, W, dev)
 
     sweep_res = None
     if not args.no_sweep:
@@ -673,10 +902,25 @@ def main():
         log("fp8 forward")
         next_rows["fp8_forward"] = fp8_measure(torch, fa, W, dev)
 
+    c3_inputs = None
+    if not (args.no_ceilings and args.no_cpu_baseline):
+        c3_inputs = W.make_inputs(W.WORKLOADS["fwd_causal_bf16_b1h32n16384d128"], dev)
+    ceil = None
+    if not args.no_ceilings:
+        log("ceilings (probe library)")
+        ceil = ceilings(torch, dev, fwd_q=c3_inputs)
+        if ceil:
+            for r in roofs:
+                ref = ceil.get("stream_read", {}).get("GBps") if r["bound"] == "hbm" else \
+                    ceil.get("mfma_bf16_random_exp" if r["kernel"].startswith("fwd") else "mfma_bf16_random",
+                             {}).get("tflops")
+                if ref:
+                    r["frac_of_measured_ceiling"] = round(r["achieved"] / ref, 4)
+
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
-        cpu = cpu_baseline(W)
+        cpu = cpu_baseline(W, c3_inputs=c3_inputs, c5_inputs=(b.dq_in, b.kc, b.vc))
 
     line = {
         "metric": "attn fwd/bwd TFLOP/s bf16 causal (N=2K–16K) + % MFMA peak; decode HBM GB/s",
@@ -699,10 +943,16 @@ def main():
         "frac_mfma_peak": round(value / PEAK_BF16_TFLOPS, 4),
         "parts": parts,
         "roofline": {k: dominant[k] for k in ("bound", "achieved", "peak", "unit", "frac", "traffic")}
-                    | {"kernel": dominant["kernel"]},
+                    | {"kernel": dominant["kernel"]}
+                    | ({"frac_of_measured_ceiling": dominant["frac_of_measured_ceiling"]}
+                       if "frac_of_measured_ceiling" in dominant else {}),
         "rooflines": roofs,
+        "timing": "step: per-call HIP events over the timed steps (mean; median and min in parts); every other "
+                  "figure: >= 50 ms warm-up, then >= 20 single calls and >= 200 ms, median (min as *_best)",
+        "configs": configs,
         "sweep": sweep_res,
         "next_rows": next_rows,
+        "ceilings": ceil,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

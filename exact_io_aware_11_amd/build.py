@@ -21,6 +21,10 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libfa.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
+# measurement probes of the benchmark (MFMA and HBM ceilings, the forward's
+# clock); a library of their own, never loaded by the package
+PROBE_SOURCES = ["fa_probe.hip"]
+PROBE_LIB_PATH = os.path.join(PKG_DIR, "libfa_probe.so")
 
 SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_fwd_fp8.hip", "fa_bwd.hip", "fa_decode.hip", "fa_noalloc.hip"]
 
@@ -55,20 +59,27 @@ def _compile(src: str, obj: str) -> None:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{proc.stdout}\n{proc.stderr}")
 
 
+def _link(objs, path) -> None:
+    out_tmp = path + ".tmp"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", out_tmp] + objs
+    proc = subprocess.run(cmd, capture_output=True, text=True)
+    if proc.returncode != 0:
+        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{proc.stdout}\n{proc.stderr}")
+    os.replace(out_tmp, path)
+
+
 def build(verbose: bool = False) -> str:
-    """Compile every source and link ``libfa.so`` next to this file; returns its path."""
+    """Compile every source and link ``libfa.so`` (and the benchmark's
+    ``libfa_probe.so``) next to this file; returns the library's path."""
     with tempfile.TemporaryDirectory(prefix="fa_build_") as tmp:
-        objs = [os.path.join(tmp, os.path.splitext(s)[0] + ".o") for s in SOURCES]
-        with ThreadPoolExecutor(max_workers=min(6, len(SOURCES))) as ex:
-            list(ex.map(_compile, SOURCES, objs))
-        out_tmp = LIB_PATH + ".tmp"
-        cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", out_tmp] + objs
-        proc = subprocess.run(cmd, capture_output=True, text=True)
-        if proc.returncode != 0:
-            raise RuntimeError(f"link failed: {' '.join(cmd)}\n{proc.stdout}\n{proc.stderr}")
-        os.replace(out_tmp, LIB_PATH)
+        srcs = SOURCES + PROBE_SOURCES
+        objs = [os.path.join(tmp, os.path.splitext(s)[0] + ".o") for s in srcs]
+        with ThreadPoolExecutor(max_workers=min(7, len(srcs))) as ex:
+            list(ex.map(_compile, srcs, objs))
+        _link(objs[:len(SOURCES)], LIB_PATH)
+        _link(objs[len(SOURCES):], PROBE_LIB_PATH)
     if verbose:
-        print(f"built {LIB_PATH}")
+        print(f"built {LIB_PATH} and {PROBE_LIB_PATH}")
     return LIB_PATH
 
 
