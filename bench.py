@@ -455,15 +455,19 @@ def ceilings(torch, dev, fwd_q=None):
         c = c.view(-1, 2).double()
         return float(c[:, 0].sum() / c[:, 1].sum()) * 0.1
 
-    for mode, name, ops in ((0, "mfma_bf16_random", ops_rand), (1, "mfma_bf16_random_exp", ops_rand),
-                            (2, "mfma_bf16_constant", ops_const)):
-        iters = 60000
+    # random e4m3 codes (no NaN codes: drawn through the format's own cast)
+    ops_fp8 = (torch.randn((nops * 2,), generator=g, device=dev) * 8).to(torch.float8_e4m3fn).view(torch.uint8)
+    for mode, name, ops, iters, kdim, peak in (
+            (0, "mfma_bf16_random", ops_rand, 60000, 16, PEAK_BF16_TFLOPS),
+            (1, "mfma_bf16_random_exp", ops_rand, 60000, 16, PEAK_BF16_TFLOPS),
+            (2, "mfma_bf16_constant", ops_const, 60000, 16, PEAK_BF16_TFLOPS),
+            (3, "mfma_fp8_random", ops_fp8, 30000, 64, PEAK_FP8_TFLOPS)):
         run = lambda: lib.fa_probe_mfma(mode, ops.data_ptr(), iters, grid, sink.data_ptr(), clk.data_ptr(), stream)
         st = timed_stats(torch, run, min_calls=5, min_ms=100.0, max_calls=50, warm_ms=100.0)
-        flops = grid * 4.0 * iters * 4 * 2 * 32 * 32 * 16
+        flops = grid * 4.0 * iters * 4 * 2 * 32 * 32 * kdim
         tf = flops / (st["median_ms"] * 1e-3) / 1e12
         ghz = clock_ghz(clk)
-        out[name] = {"tflops": round(tf, 1), "frac_spec": round(tf / PEAK_BF16_TFLOPS, 4), "clock_ghz": round(ghz, 3),
+        out[name] = {"tflops": round(tf, 1), "frac_spec": round(tf / peak, 4), "clock_ghz": round(ghz, 3),
                      "ms": round(st["median_ms"], 3)}
         log(f"ceiling {name}: {tf:.1f} TFLOP/s at {ghz:.3f} GHz")
 
@@ -476,7 +480,7 @@ def ceilings(torch, dev, fwd_q=None):
     out["stream_read"] = {"GBps": round(gbs, 1), "frac_spec": round(gbs / PEAK_HBM_GBPS, 4),
                           "bytes": nbytes, "ms": round(st["median_ms"], 3)}
     log(f"ceiling stream read: {gbs:.1f} GB/s")
-    del buf, ops_rand, ops_const
+    del buf, ops_rand, ops_const, ops_fp8
 
     if fwd_q is not None:
         q, k, v = fwd_q
@@ -496,6 +500,41 @@ def ceilings(torch, dev, fwd_q=None):
                             "mfma_util_at_clock": round(tf / at_clock, 4)}
         log(f"forward clock: {ghz:.3f} GHz, {tf:.1f} TFLOP/s, {100 * tf / at_clock:.1f}% of the peak at that clock")
     return out
+
+
+def annotate_ceilings(ceil, configs, sweep_res, next_rows):
+    """Add ``frac_of_measured_ceiling`` to every rate record: bf16 forwards
+    against the MFMA + exponential loop, bf16 backwards against the MFMA-only
+    loop, the fp8 forward against the fp8 loop, decodes against the streaming
+    read."""
+    def ref(kind):
+        key = {"fwd": "mfma_bf16_random_exp", "bwd": "mfma_bf16_random", "fp8": "mfma_fp8_random",
+               "hbm": "stream_read"}[kind]
+        e = ceil.get(key) or {}
+        return e.get("GBps") if kind == "hbm" else e.get("tflops")
+
+    def mark(rec, kind):
+        r = ref(kind)
+        val = rec.get("GBps") if kind == "hbm" else rec.get("tflops")
+        if rec is not None and r and val:
+            rec["frac_of_measured_ceiling"] = round(val / r, 4)
+
+    for s_ in sweep_res or []:
+        mark(s_["fwd"], "fwd")
+        mark(s_["bwd"], "bwd")
+    if configs:
+        mark(configs.get("C3", {}), "fwd")
+        mark(configs.get("C4", {}), "bwd")
+        mark(configs.get("C4_fwd", {}), "fwd")
+    if next_rows:
+        for grp, recs in next_rows.items():
+            for name, rec in recs.items():
+                if grp == "fp8_forward":
+                    mark(rec, "fp8")
+                elif "GBps" in rec and "tflops" not in rec:
+                    mark(rec, "hbm")
+                elif name in ("fwd", "bwd"):
+                    mark(rec, name)
 
 
 def host_info():
@@ -916,6 +955,9 @@ def main():
                              {}).get("tflops")
                 if ref:
                     r["frac_of_measured_ceiling"] = round(r["achieved"] / ref, 4)
+
+    if ceil:
+        annotate_ceilings(ceil, configs, sweep_res, next_rows)
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -11,6 +11,8 @@
 
 namespace fa {
 
+// Internal linkage on purpose: the library and the probe library each
+// compile their own instantiations, and neither exports them.
 namespace {
 
 constexpr int FWD_BR = 128;     // query rows per workgroup (4 waves x 32)

@@ -6,7 +6,8 @@
 //   * fa_probe_mfma: a register-only loop of v_mfma_f32_32x32x16_bf16 on four
 //     independent accumulators at two waves per SIMD, on random operands or on
 //     constant ones, optionally with one v_exp_f32 per product (the forward's
-//     ratio of exponentials to products).  Each workgroup records the
+//     ratio of exponentials to products); or of the e4m3 product
+//     v_mfma_scale_f32_32x32x64_f8f6f4 on random codes.  Each workgroup records the
 //     shader-clock cycles (s_memtime) and the constant 100 MHz reference
 //     (s_memrealtime) it took, which gives the clock the chip ran at.
 //   * fa_probe_stream_read: a streaming read of a large buffer (16-byte
@@ -24,8 +25,12 @@ namespace {
 
 constexpr int PROBE_THREADS = 256;
 
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
 // MODE 0: random operands; 1: random operands and one exp per product;
-// 2: constant operands.  ops holds 8 operand vectors per lane (a0..a3, b0..b3).
+// 2: constant operands (all bf16); 3: random e4m3 codes on the fp8 product
+// (unit block scales).  ops holds 8 16-byte operand vectors per lane
+// (a0..a3, b0..b3; an fp8 operand takes two of them).
 template <int MODE>
 __global__ void __launch_bounds__(PROBE_THREADS) __attribute__((amdgpu_waves_per_eu(2)))
 mfma_probe_kernel(const uint4* __restrict__ ops, int iters, float* __restrict__ sink,
@@ -46,11 +51,28 @@ mfma_probe_kernel(const uint4* __restrict__ ops, int iters, float* __restrict__ 
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[j] = zero16();
     float x[4] = {0.1f, 0.2f, 0.3f, 0.4f};
-    for (int it = 0; it < iters; ++it) {
+    if constexpr (MODE == 3) {
+        i32x8 fa8[2], fb8[2];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            acc[j] = mfma_bf16(a[j], b[j], acc[j]);
-            if constexpr (MODE == 1) x[j] = exp2_fast(fmaf(x[j], -0.37f, 0.6f));
+        for (int j = 0; j < 2; ++j) {
+            const uint4 lo = ops[base + 2 * j], hi = ops[base + 2 * j + 1];
+            const uint4 blo = ops[base + 4 + 2 * j], bhi = ops[base + 5 + 2 * j];
+            fa8[j] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+            fb8[j] = i32x8{(int)blo.x, (int)blo.y, (int)blo.z, (int)blo.w, (int)bhi.x, (int)bhi.y, (int)bhi.z, (int)bhi.w};
+        }
+        for (int it = 0; it < iters; ++it) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                acc[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa8[j & 1], fb8[(j >> 1) & 1], acc[j],
+                                                                         0, 0, 0, 127, 0, 127);
+        }
+    } else {
+        for (int it = 0; it < iters; ++it) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                acc[j] = mfma_bf16(a[j], b[j], acc[j]);
+                if constexpr (MODE == 1) x[j] = exp2_fast(fmaf(x[j], -0.37f, 0.6f));
+            }
         }
     }
     float s = x[0] + x[1] + x[2] + x[3];
@@ -82,18 +104,19 @@ stream_read_kernel(const uint4* __restrict__ p, size_t n16, uint32_t* __restrict
 
 extern "C" {
 
-// mode 0, 1 or 2 (see mfma_probe_kernel); ops: grid * 256 * 8 16-byte operand
+// mode 0..3 (see mfma_probe_kernel); ops: grid * 256 * 8 16-byte operand
 // vectors; sink: grid * 256 floats; clk: 2 * grid values.  Returns a
 // hipError_t code.
 int fa_probe_mfma(int mode, const void* ops, int iters, int grid, float* sink, unsigned long long* clk,
                   void* stream) {
-    if (!ops || !sink || !clk || iters < 1 || grid < 1 || mode < 0 || mode > 2) return (int)hipErrorInvalidValue;
+    if (!ops || !sink || !clk || iters < 1 || grid < 1 || mode < 0 || mode > 3) return (int)hipErrorInvalidValue;
     const dim3 g((unsigned)grid), b(fa::PROBE_THREADS);
     hipStream_t st = (hipStream_t)stream;
     const uint4* o = (const uint4*)ops;
     if (mode == 0) hipLaunchKernelGGL((fa::mfma_probe_kernel<0>), g, b, 0, st, o, iters, sink, clk);
     else if (mode == 1) hipLaunchKernelGGL((fa::mfma_probe_kernel<1>), g, b, 0, st, o, iters, sink, clk);
-    else hipLaunchKernelGGL((fa::mfma_probe_kernel<2>), g, b, 0, st, o, iters, sink, clk);
+    else if (mode == 2) hipLaunchKernelGGL((fa::mfma_probe_kernel<2>), g, b, 0, st, o, iters, sink, clk);
+    else hipLaunchKernelGGL((fa::mfma_probe_kernel<3>), g, b, 0, st, o, iters, sink, clk);
     return (int)hipGetLastError();
 }
 
