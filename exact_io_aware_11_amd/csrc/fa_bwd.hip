@@ -340,9 +340,9 @@ bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, cons
             };
             // P = 2^(c S - LSE log2 e), masked; dS = P (dP - D); both packed to
             // bf16 as the B operands of the two K-steps of this half
-            auto pds = [&](int qb, auto masked) __attribute__((always_inline)) {
+            auto pds = [&](int qb, auto masked, int h0 = 0, int h1 = 2) __attribute__((always_inline)) {
 #pragma unroll
-                for (int h = 0; h < 2; ++h) {
+                for (int h = h0; h < h1; ++h) {
                     uint32_t pk[4], sk[4];
 #pragma unroll
                     for (int j = 0; j < 8; j += 2) {
@@ -401,10 +401,16 @@ bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, cons
                     dvdk(2);
                     dvdk(3);
                 } else {
-                    // one 32-row block: S, dP | P, dS | dV, dK
+                    // one 32-row block: S, dP | P, dS of rows 0..15 | dV, dK
+                    // of K-step 0 beside P, dS of rows 16..31 | dV, dK of
+                    // K-step 1
                     sdp(0);
-                    pds(0, masked);
+                    pds(0, masked, 0, 1);
+                    __builtin_amdgcn_sched_barrier(0);
                     dvdk(0);
+                    pds(0, masked, 1, 2);
+                    FA_INTERLEAVE(2 * D / 32, 4, 4);
+                    __builtin_amdgcn_sched_barrier(0);
                     dvdk(1);
                 }
             };
