@@ -676,8 +676,8 @@ def _step_kernels():
     return {
         "fwd": ("fwd_bf16_kernel", "fa_fwd.hip", "B4 H16 N2048 d128 causal", 4 * t + r,
                 "read Q, K, V; write O, LSE"),
-        "bwd_prep": ("bwd_prep_kernel", "fa_bwd.hip", "B4 H16 N2048 d128 causal", 2 * t + r,
-                     "read O, dO; write D"),
+        "bwd_prep": ("bwd_prep_kernel", "fa_bwd.hip", "B4 H16 N2048 d128 causal", 2 * t + 3 * r,
+                     "read O, dO, LSE; write D, LSE log2 e"),
         "bwd_dkdv": ("bwd_dkdv_kernel", "fa_bwd.hip", "B4 H16 N2048 d128 causal", 6 * t + 2 * r,
                      "read Q, K, V, dO, LSE, D; write dK, dV"),
         "bwd_dq": ("bwd_dq_kernel", "fa_bwd.hip", "B4 H16 N2048 d128 causal", 5 * t + 2 * r,

@@ -9,13 +9,14 @@
 //     dS = P * (dP - D),  dK = scale dS^T Q,  dQ = scale dS K.
 //
 // Three launches on the caller's stream:
-//   1. bwd_prep:  D = rowsum(dO * O) in fp32.
+//   1. bwd_prep:  D = rowsum(dO * O) in fp32, and the LSE in base-2 units
+//                 (LSE log2 e), the form both later kernels exponentiate.
 //   2. bwd_dkdv:  one workgroup per tile of BC = 128 keys of one K/V head (4
 //                 waves, 32 keys each), walking the query tiles (BR = 64 rows)
 //                 that can see its keys -- for each of the H/Hkv query heads
 //                 sharing that K/V head, so a shared head's gradient is summed
 //                 in registers.  K and V of the tile stay in registers; Q, dO,
-//                 LSE and D of the next query tile are copied global -> LDS by
+//                 the base-2 LSE and D of the next query tile are copied global -> LDS by
 //                 buffer DMA while the current one is computed.  dK^T and dV^T
 //                 accumulate in registers and are stored once, staged through
 //                 the free tile buffers so that each store writes whole rows.
@@ -63,8 +64,8 @@ constexpr int BWD_THREADS = 256;
 // ---------------------------------------------------------------------------
 template <int D, bool O_BF16>
 __global__ void __launch_bounds__(256)
-bwd_prep_kernel(const void* __restrict__ O, const __bf16* __restrict__ dO, float* __restrict__ delta,
-                long long rows) {
+bwd_prep_kernel(const void* __restrict__ O, const __bf16* __restrict__ dO, const float* __restrict__ lse,
+                float* __restrict__ delta, float* __restrict__ lse2, long long rows) {
     constexpr int LPR = D / 8;
     const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
     const long long row = gid / LPR;
@@ -102,7 +103,11 @@ bwd_prep_kernel(const void* __restrict__ O, const __bf16* __restrict__ dO, float
         acc = dpp_sum16(acc);
         if constexpr (LPR == 32) acc += __shfl_xor(acc, 16);   // d = 256: two 16-lane rows per row
     }
-    if (live && part == 0) delta[row] = acc;
+    if (live && part == 0) {
+        delta[row] = acc;
+        // one rounding, the same as forming LSE log2 e where it is used
+        lse2[row] = lse[row] * kLog2e;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -136,7 +141,7 @@ bwd_prep_kernel(const void* __restrict__ O, const __bf16* __restrict__ dO, float
 template <int D, bool CAUSAL, bool SPLIT>
 __global__ void __launch_bounds__(BWD_THREADS)
 bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
-                const __bf16* __restrict__ dO, const float* __restrict__ LSE,
+                const __bf16* __restrict__ dO, const float* __restrict__ LSE2 /* LSE log2 e */,
                 const float* __restrict__ delta, __bf16* __restrict__ dK,
                 __bf16* __restrict__ dV, float* __restrict__ pdk, float* __restrict__ pdv,
                 int BHkv, int G, int N, float c /* scale*log2e */, float scale) {
@@ -268,7 +273,7 @@ bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, cons
         issue(dO + qh * N * D, r0, b + QTB);
         const uint32_t nb = (uint32_t)(N - r0) * 4;
         if (w == 0 && lane < BR)
-            b2lds4(make_rsrc(LSE + qh * N + r0, nb), 4 * lane, reinterpret_cast<float*>(b + 2 * QTB));
+            b2lds4(make_rsrc(LSE2 + qh * N + r0, nb), 4 * lane, reinterpret_cast<float*>(b + 2 * QTB));
         if (w == 1 && lane < BR)
             b2lds4(make_rsrc(delta + qh * N + r0, nb), 4 * lane, reinterpret_cast<float*>(b + 2 * QTB + 4 * BR));
     };
@@ -356,7 +361,7 @@ bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, cons
                                                        : dd4[qb][rb];
                             const float lv = t == 0 ? l4.x : t == 1 ? l4.y : t == 2 ? l4.z : l4.w;
                             const float dv = t == 0 ? d4.x : t == 1 ? d4.y : t == 2 ? d4.z : d4.w;
-                            float p = exp2_fast(fmaf(sP[qb][r], c, -lv * kLog2e));
+                            float p = exp2_fast(fmaf(sP[qb][r], c, -lv));
                             if (decltype(masked)::value) {
                                 const int qrow = q0 + 32 * qb + 8 * rb + 4 * g + t;
                                 if (!key_live || qrow >= N || (CAUSAL && key > qrow)) p = 0.f;
@@ -590,8 +595,8 @@ constexpr int DQ_VALU_EACH = 8;     // and between the following ones
 template <int D, bool CAUSAL>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 256 ? 1 : 2)))
 bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
-              const __bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ delta,
-              __bf16* __restrict__ dQ, int BH, int G, int N, int nqt, float c /* scale*log2e */, float scale) {
+              const __bf16* __restrict__ dO, const float* __restrict__ LSE2 /* LSE log2 e */,
+              const float* __restrict__ delta, __bf16* __restrict__ dQ, int BH, int G, int N, int nqt, float c /* scale*log2e */, float scale) {
     constexpr int BR = DQ_BR, BC = dq_bc<D>();
     constexpr int ROWB = 2 * D;
     constexpr int CPR = D / 8;
@@ -641,7 +646,7 @@ bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const 
         df[ks] = as_bf16x8(ud);
     }
     // rows past the end get LSE = +inf (P = 0)
-    const float lse2 = row_live ? LSE[(size_t)bh * N + qrow] * kLog2e : INFINITY;
+    const float lse2 = row_live ? LSE2[(size_t)bh * N + qrow] : INFINITY;
     const float dd = row_live ? delta[(size_t)bh * N + qrow] : 0.f;
 
     const int kv_end = CAUSAL ? min(N, q0 + BR) : N;
@@ -794,10 +799,10 @@ hipError_t launch_kernels(const BwdArgs& a) {
     const unsigned prep_blocks = (unsigned)((rows * (D / 8) + 255) / 256);
     if (a.o_bf16)
         hipLaunchKernelGGL((bwd_prep_kernel<D, true>), dim3(prep_blocks), dim3(256), 0, st, a.o,
-                           (const __bf16*)a.dout, a.delta, rows);
+                           (const __bf16*)a.dout, a.lse, a.delta, a.lse2, rows);
     else
         hipLaunchKernelGGL((bwd_prep_kernel<D, false>), dim3(prep_blocks), dim3(256), 0, st, a.o,
-                           (const __bf16*)a.dout, a.delta, rows);
+                           (const __bf16*)a.dout, a.lse, a.delta, a.lse2, rows);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int nkt = (a.N + BWD_BC - 1) / BWD_BC;
@@ -805,7 +810,7 @@ hipError_t launch_kernels(const BwdArgs& a) {
     if (a.split) {
         hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, true>), dim3((unsigned)(nkt * BH)), dim3(BWD_THREADS), 0,
                            st, (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (const __bf16*)a.dout,
-                           a.lse, a.delta, (__bf16*)a.dk, (__bf16*)a.dv, a.pdk, a.pdv, BHkv, G, a.N,
+                           a.lse2, a.delta, (__bf16*)a.dk, (__bf16*)a.dv, a.pdk, a.pdv, BHkv, G, a.N,
                            a.scale * kLog2e, a.scale);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -815,14 +820,14 @@ hipError_t launch_kernels(const BwdArgs& a) {
     } else {
         hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, false>), dim3((unsigned)(nkt * BHkv)), dim3(BWD_THREADS), 0,
                            st, (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (const __bf16*)a.dout,
-                           a.lse, a.delta, (__bf16*)a.dk, (__bf16*)a.dv, nullptr, nullptr, BHkv, G, a.N,
+                           a.lse2, a.delta, (__bf16*)a.dk, (__bf16*)a.dv, nullptr, nullptr, BHkv, G, a.N,
                            a.scale * kLog2e, a.scale);
     }
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int nqt = (a.N + DQ_BR - 1) / DQ_BR;
     hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)(nqt * BH)), dim3(256), 0, st,
-                       (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (const __bf16*)a.dout, a.lse,
+                       (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (const __bf16*)a.dout, a.lse2,
                        a.delta, (__bf16*)a.dq, BH, G, a.N, nqt, a.scale * kLog2e, a.scale);
     return hipGetLastError();
 }

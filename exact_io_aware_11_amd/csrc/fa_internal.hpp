@@ -48,6 +48,7 @@ struct BwdArgs {
     void* dk;
     void* dv;
     float* delta;    // workspace: [B,H,N] fp32, rowsum(dO * O)
+    float* lse2;     // workspace: [B,H,N] fp32, LSE log2 e (written by the prep kernel)
     float* pdk;      // workspace when split: [B,H,N,d] fp32 partial dK^T rows per query head
     float* pdv;      // workspace when split: [B,H,N,d] fp32 partial dV^T rows per query head
     bool split;      // bwd_split_heads(B, H, Hkv, N)

@@ -141,7 +141,8 @@ fa_status_t fa_fwd_fp8(const void* q, const void* k, const void* vt,
 
 /*
  * fa_bwd_workspace_bytes -- bytes of workspace fa_bwd needs for this shape:
- * the fp32 row statistic D = rowsum(dO * O), [B,H,N], padded to 256 bytes.
+ * the fp32 row statistic D = rowsum(dO * O), [B,H,N], and the LSE in base-2
+ * units (LSE log2 e), [B,H,N] fp32, each padded to 256 bytes.
  * With grouped heads (Hkv < H) and fewer than 512 (K/V head, 128-key tile)
  * pairs, fa_bwd gives every query head its own dK/dV workgroups and the
  * workspace also holds their fp32 partial dK and dV, [B,H,N,d] each, summed

@@ -177,10 +177,11 @@ def test_bwd_rejects_small_workspace():
 
 
 def test_bwd_workspace_size():
-    # one fp32 row statistic D = rowsum(dO * O) per query row: O(N), no N^2 term
+    # two fp32 row statistics per query row, D = rowsum(dO * O) and LSE log2 e:
+    # O(N), no N^2 term
     B, H, N, d = 2, 16, 4096, 128
-    assert fa.fa_bwd_workspace_bytes(B, H, H, N, d) == B * H * N * 4
-    assert fa.fa_bwd_workspace_bytes(1, 3, 3, 5, 64) == 256          # padded to 256 bytes
+    assert fa.fa_bwd_workspace_bytes(B, H, H, N, d) == 2 * B * H * N * 4
+    assert fa.fa_bwd_workspace_bytes(1, 3, 3, 5, 64) == 2 * 256      # each padded to 256 bytes
     assert fa.fa_bwd_workspace_bytes(0, 1, 1, 1, 64) == 0
     assert fa.fa_bwd_workspace_bytes(1, 4, 3, 16, 64) == 0           # Hkv must divide H
 
@@ -198,8 +199,8 @@ def test_bwd_workspace_size():
 def test_bwd_workspace_grouped_split(B, H, Hkv, N, split):
     # the grouped-head split adds fp32 partial dK and dV, [B,H,N,d] each
     d = 64
-    delta = (B * H * N * 4 + 255) // 256 * 256
-    want = delta + (2 * B * H * N * d * 4 if split else 0)
+    rows = 2 * ((B * H * N * 4 + 255) // 256 * 256)
+    want = rows + (2 * B * H * N * d * 4 if split else 0)
     assert fa.fa_bwd_workspace_bytes(B, H, Hkv, N, d) == want
 
 

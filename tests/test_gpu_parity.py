@@ -444,7 +444,7 @@ def test_bwd_gqa_large_grid_sums_in_registers():
     fa = _fa()
     B, H, Hkv, N, d = 64, 16, 8, 256, 64
     G = H // Hkv
-    assert fa.fa_bwd_workspace_bytes(B, H, Hkv, N, d) == B * H * N * 4
+    assert fa.fa_bwd_workspace_bytes(B, H, Hkv, N, d) == 2 * B * H * N * 4
     q, k, v, do = W.make_gqa(B, H, Hkv, N, d, "bf16", seed=4300, with_dout=True, device=DEV)
     scale = 1.0 / math.sqrt(d)
     say(f"fa_bwd gqa large grid B{B} H{H} Hkv{Hkv} N{N} d{d} causal")
@@ -466,7 +466,7 @@ def test_bwd_d256_grouped_without_split_sampled_heads():
     fa = _fa()
     B, H, Hkv, N, d = 16, 8, 4, 1000, 256
     G = H // Hkv
-    assert fa.fa_bwd_workspace_bytes(B, H, Hkv, N, d) == (B * H * N * 4 + 255) // 256 * 256
+    assert fa.fa_bwd_workspace_bytes(B, H, Hkv, N, d) == 2 * ((B * H * N * 4 + 255) // 256 * 256)
     q, k, v, do = W.make_gqa(B, H, Hkv, N, d, "bf16", seed=4400, with_dout=True, device=DEV)
     scale = 1.0 / math.sqrt(d)
     say(f"fa_bwd d256 gqa B{B} H{H} Hkv{Hkv} N{N} causal")
