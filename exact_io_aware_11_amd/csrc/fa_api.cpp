@@ -150,8 +150,8 @@ fa_status_t fa_fwd_fp8(const void* q, const void* k, const void* vt, float q_sca
 }
 
 // workspace layout: D [B,H,N] fp32 and LSE log2 e [B,H,N] fp32, each padded
-// to 256 bytes; then, when the grouped-head split is taken, partial dK^T and
-// dV^T rows [B,H,N,d] fp32 each
+// to 256 bytes; then, when the grouped-head split is taken (s query heads per
+// workgroup), partial dK^T and dV^T rows [B*H/s, N, d] fp32 each
 static size_t bwd_row_bytes(int B, int H, int N) {
     return ((size_t)B * H * N * sizeof(float) + 255) & ~(size_t)255;
 }
@@ -160,7 +160,8 @@ static size_t bwd_delta_bytes(int B, int H, int N) { return 2 * bwd_row_bytes(B,
 size_t fa_bwd_workspace_bytes(int B, int H, int Hkv, int N, int d) {
     if (!dims_ok(B, H, N) || !kv_ok(H, Hkv) || d < 1 || !total_ok(B, H, N, d)) return 0;
     size_t n = bwd_delta_bytes(B, H, N);
-    if (fa::bwd_split_heads(B, H, Hkv, N)) n += 2 * (size_t)B * H * N * d * sizeof(float);
+    const int s = fa::bwd_split_heads(B, H, Hkv, N);     // query heads per split workgroup, 0: none
+    if (s > 0) n += 2 * ((size_t)B * H / s) * N * d * sizeof(float);
     return n;
 }
 
@@ -181,9 +182,9 @@ fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, f
     if (!aligned16(workspace)) return FA_ERR_ALIGN;
     float* delta = static_cast<float*>(workspace);
     float* lse2 = reinterpret_cast<float*>(static_cast<char*>(workspace) + bwd_row_bytes(B, H, N));
-    const bool split = fa::bwd_split_heads(B, H, Hkv, N);
+    const int split = fa::bwd_split_heads(B, H, Hkv, N);
     float* pdk = split ? reinterpret_cast<float*>(static_cast<char*>(workspace) + bwd_delta_bytes(B, H, N)) : nullptr;
-    float* pdv = split ? pdk + (size_t)B * H * N * d : nullptr;
+    float* pdv = split ? pdk + ((size_t)B * H / split) * N * d : nullptr;
     fa::BwdArgs a{q, k, v, o, lse, dout, dq, dk, dv, delta, lse2, pdk, pdv, split, B, H, Hkv, N, d,
                   o_dtype == FA_BF16, causal != 0, scale, stream};
     return from_hip(fa::launch_bwd(a));

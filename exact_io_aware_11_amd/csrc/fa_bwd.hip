@@ -22,9 +22,10 @@
 //                 the free tile buffers so that each store writes whole rows.
 //                 With grouped heads and a grid of few workgroups the causal
 //                 imbalance between key tiles would decide the run time; then
-//                 each query head gets its own workgroup, which stores fp32
-//                 partial dK^T / dV^T rows, and bwd_kv_reduce sums them over
-//                 the group in head order (a fourth launch).
+//                 each group of s query heads (s dividing H/Hkv, chosen to
+//                 give just enough workgroups) gets workgroups of its own,
+//                 which store fp32 partial dK^T / dV^T rows, and bwd_kv_reduce
+//                 sums them over the groups in order (a fourth launch).
 //   3. bwd_dq:    one workgroup per tile of 128 query rows, streaming the K/V
 //                 tiles of its head like the forward pass: it recomputes S, P
 //                 and dP, forms dS and accumulates dQ^T = K^T dS^T in
@@ -135,16 +136,17 @@ bwd_prep_kernel(const void* __restrict__ O, const __bf16* __restrict__ dO, const
     __builtin_amdgcn_s_waitcnt((((n) & 15) | (((n) >> 4) << 14)) | (7 << 4) | (15 << 8))
 #define FA_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4))
 
-// SPLIT: one workgroup per (query head, key tile) instead of per (K/V head,
-// key tile); the unscaled dK^T / dV^T rows of that query head go to the fp32
-// partial buffers pdk / pdv ([B*H, N, D]) and bwd_kv_reduce_kernel sums them.
+// SPLIT: one workgroup per (group of HPG query heads, key tile) instead of per
+// (K/V head, key tile); the group's unscaled dK^T / dV^T rows go to the fp32
+// partial buffers pdk / pdv ([B*H/HPG, N, D]) and bwd_kv_reduce_kernel sums
+// them.
 template <int D, bool CAUSAL, bool SPLIT>
 __global__ void __launch_bounds__(BWD_THREADS)
 bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
                 const __bf16* __restrict__ dO, const float* __restrict__ LSE2 /* LSE log2 e */,
                 const float* __restrict__ delta, __bf16* __restrict__ dK,
                 __bf16* __restrict__ dV, float* __restrict__ pdk, float* __restrict__ pdv,
-                int BHkv, int G, int N, float c /* scale*log2e */, float scale) {
+                int BHkv, int G, int HPG, int N, float c /* scale*log2e */, float scale) {
     constexpr int BR = bwd_br<D>(), BC = BWD_BC;
     constexpr int ROWB = 2 * D;                  // bytes per row of a Q/dO/K tile
     constexpr int CPR = D / 8;
@@ -169,15 +171,18 @@ bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, cons
     // One workgroup per (K/V head, key tile); heavy tiles first: key tile 0
     // sees every query tile.  The G query heads sharing this K/V head are
     // visited in turn, so dK and dV sum their contributions in registers.
-    // SPLIT: one workgroup per (query head, key tile), in the forward's block
-    // order (the G heads of a K/V head NG = B*Hkv ids apart).
-    const int NHG = SPLIT ? 1 : G;                // query heads this workgroup visits
-    int kvh, kt, head0;                           // K/V head, key tile, first query head
+    // SPLIT: one workgroup per (group of HPG query heads, key tile); the G/HPG
+    // groups of a K/V head are B*Hkv block ids apart.  Its fp32 partial rows go
+    // to partial block `part` = K/V head * (G/HPG) + group.
+    const int NHG = SPLIT ? HPG : G;              // query heads this workgroup visits
+    int kvh, kt, head0, part = 0;                 // K/V head, key tile, first query head
     if constexpr (SPLIT) {
-        const int BH = BHkv * G, j = blockIdx.x % BH;
-        kt = blockIdx.x / BH;
-        head0 = (j % BHkv) * G + j / BHkv;
-        kvh = head0 / G;
+        const int NGR = G / HPG, BG = BHkv * NGR, j = blockIdx.x % BG;
+        kt = blockIdx.x / BG;
+        kvh = j % BHkv;
+        const int grp = j / BHkv;
+        head0 = kvh * G + grp * HPG;
+        part = kvh * NGR + grp;
     } else {
         kvh = blockIdx.x % BHkv;
         kt = blockIdx.x / BHkv;
@@ -459,7 +464,7 @@ bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, cons
                 for (int rb = 0; rb < 4; ++rb) {
                     const int d0 = 32 * mb + 8 * rb + 4 * g;
                     if constexpr (SPLIT) {
-                        const size_t o = ((size_t)head0 * N + key) * D + d0;
+                        const size_t o = ((size_t)part * N + key) * D + d0;
                         *reinterpret_cast<float4*>(pdv + o) =
                             make_float4(dvt[mb][4 * rb], dvt[mb][4 * rb + 1], dvt[mb][4 * rb + 2], dvt[mb][4 * rb + 3]);
                         *reinterpret_cast<float4*>(pdk + o) =
@@ -497,7 +502,7 @@ bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, cons
             for (int p = 0; p < 32 / RPPF; ++p) {
                 const int r = RPPF * p + lane / CHF, ch = lane % CHF;
                 const float4 v = *reinterpret_cast<const float4*>(wb + r * RB + 16 * (ch ^ (r % CHF)));
-                if (wk0 + r < N) *reinterpret_cast<float4*>(dst + ((size_t)head0 * N + wk0 + r) * D + 4 * ch) = v;
+                if (wk0 + r < N) *reinterpret_cast<float4*>(dst + ((size_t)part * N + wk0 + r) * D + 4 * ch) = v;
             }
         };
         stagef(dvt, pdv);
@@ -545,22 +550,22 @@ bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, cons
 }
 
 // ---------------------------------------------------------------------------
-// Sum of the split dK/dV partials over the G query heads of each K/V head,
-// in head order (deterministic); dK is scaled here.  Eight elements per
+// Sum of the split dK/dV partials over the NGR head groups of each K/V head,
+// in group order (deterministic); dK is scaled here.  Eight elements per
 // thread.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ void __launch_bounds__(256)
 bwd_kv_reduce_kernel(const float* __restrict__ pdk, const float* __restrict__ pdv, __bf16* __restrict__ dK,
-                     __bf16* __restrict__ dV, long long n8, int G, int N, float scale) {
+                     __bf16* __restrict__ dV, long long n8, int NGR, int N, float scale) {
     const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
     if (i >= n8) return;
     const long long e = 8 * i;                          // element of [B*Hkv, N, D]
     const long long per_head = (long long)N * D;
     const long long kvh = e / per_head, rem = e - kvh * per_head;
     float sk[8] = {}, sv[8] = {};
-    for (int r = 0; r < G; ++r) {
-        const size_t src = (size_t)((kvh * G + r) * per_head + rem);
+    for (int r = 0; r < NGR; ++r) {
+        const size_t src = (size_t)((kvh * NGR + r) * per_head + rem);
         const float4 k0 = *reinterpret_cast<const float4*>(pdk + src);
         const float4 k1 = *reinterpret_cast<const float4*>(pdk + src + 4);
         const float4 v0 = *reinterpret_cast<const float4*>(pdv + src);
@@ -808,19 +813,21 @@ hipError_t launch_kernels(const BwdArgs& a) {
     const int nkt = (a.N + BWD_BC - 1) / BWD_BC;
     const int G = a.H / a.Hkv, BHkv = a.B * a.Hkv;
     if (a.split) {
-        hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, true>), dim3((unsigned)(nkt * BH)), dim3(BWD_THREADS), 0,
-                           st, (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (const __bf16*)a.dout,
-                           a.lse2, a.delta, (__bf16*)a.dk, (__bf16*)a.dv, a.pdk, a.pdv, BHkv, G, a.N,
+        const int hpg = a.split, ngr = G / hpg;     // query heads per group, groups per K/V head
+        if (hpg < 1 || G % hpg != 0) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, true>), dim3((unsigned)(nkt * BHkv * ngr)), dim3(BWD_THREADS),
+                           0, st, (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (const __bf16*)a.dout,
+                           a.lse2, a.delta, (__bf16*)a.dk, (__bf16*)a.dv, a.pdk, a.pdv, BHkv, G, hpg, a.N,
                            a.scale * kLog2e, a.scale);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
         const long long n8 = (long long)BHkv * a.N * (D / 8);
         hipLaunchKernelGGL((bwd_kv_reduce_kernel<D>), dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st,
-                           a.pdk, a.pdv, (__bf16*)a.dk, (__bf16*)a.dv, n8, G, a.N, a.scale);
+                           a.pdk, a.pdv, (__bf16*)a.dk, (__bf16*)a.dv, n8, ngr, a.N, a.scale);
     } else {
         hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, false>), dim3((unsigned)(nkt * BHkv)), dim3(BWD_THREADS), 0,
                            st, (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (const __bf16*)a.dout,
-                           a.lse2, a.delta, (__bf16*)a.dk, (__bf16*)a.dv, nullptr, nullptr, BHkv, G, a.N,
+                           a.lse2, a.delta, (__bf16*)a.dk, (__bf16*)a.dv, nullptr, nullptr, BHkv, G, G, a.N,
                            a.scale * kLog2e, a.scale);
     }
     e = hipGetLastError();

@@ -49,9 +49,9 @@ struct BwdArgs {
     void* dv;
     float* delta;    // workspace: [B,H,N] fp32, rowsum(dO * O)
     float* lse2;     // workspace: [B,H,N] fp32, LSE log2 e (written by the prep kernel)
-    float* pdk;      // workspace when split: [B,H,N,d] fp32 partial dK^T rows per query head
-    float* pdv;      // workspace when split: [B,H,N,d] fp32 partial dV^T rows per query head
-    bool split;      // bwd_split_heads(B, H, Hkv, N)
+    float* pdk;      // workspace when split: [B*H/s, N, d] fp32 partial dK^T rows per head group
+    float* pdv;      // workspace when split: [B*H/s, N, d] fp32 partial dV^T rows per head group
+    int split;       // bwd_split_heads(B, H, Hkv, N): query heads per split workgroup, 0 = no split
     int B, H, Hkv, N, d;
     bool o_bf16;
     bool causal;
@@ -90,17 +90,28 @@ struct DecodeArgs {
 // Backward with grouped heads: the dK/dV kernel normally sums the G query
 // heads of a K/V head inside one workgroup (one per K/V head and 128-key
 // tile).  When that grid is small -- below two workgroups per CU -- the
-// uneven causal work of the key tiles decides the run time, so each query head
-// gets a workgroup of its own, writing fp32 partial dK/dV that a second kernel
-// sums over the group in a fixed order.  (Measured on MI355X with 4 query
-// heads per K/V head: the split gains 13% at 256 workgroups and loses 18-29%
-// at 512, where the partials' extra traffic outweighs the better balance.)
+// uneven causal work of the key tiles decides the run time, so the query heads
+// are split into groups of s, each with workgroups of its own, writing fp32
+// partial dK/dV that a second kernel sums over the groups in a fixed order.
+// s is chosen to give just enough workgroups: measured on MI355X with 4 query
+// heads per K/V head, a split into single heads gains 13% at 256 workgroups
+// and loses 18-29% at 512, where the partials' extra traffic outweighs the
+// better balance.
 constexpr int kBwdKeyTile = 128;
 constexpr long long kBwdSplitBelow = 512;
-inline bool bwd_split_heads(int B, int H, int Hkv, int N) {
-    if (Hkv >= H) return false;
+// Returns s, the query heads one dK/dV workgroup visits on the split path:
+// the largest divisor of G = H/Hkv below G that still gives at least
+// kBwdSplitBelow workgroups (1 if none does); 0 when the (K/V head, key tile)
+// pairs alone are enough and no split is taken.
+inline int bwd_split_heads(int B, int H, int Hkv, int N) {
+    if (Hkv >= H) return 0;
     const long long nkt = (N + kBwdKeyTile - 1) / kBwdKeyTile;
-    return nkt * B * Hkv < kBwdSplitBelow;
+    const long long pairs = nkt * B * Hkv;
+    if (pairs >= kBwdSplitBelow) return 0;
+    const int G = H / Hkv;
+    for (int s = G / 2; s > 1; --s)
+        if (G % s == 0 && pairs * (G / s) >= kBwdSplitBelow) return s;
+    return 1;
 }
 
 // Decode kernels by group size G = H/Hkv:

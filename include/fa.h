@@ -144,9 +144,11 @@ fa_status_t fa_fwd_fp8(const void* q, const void* k, const void* vt,
  * the fp32 row statistic D = rowsum(dO * O), [B,H,N], and the LSE in base-2
  * units (LSE log2 e), [B,H,N] fp32, each padded to 256 bytes.
  * With grouped heads (Hkv < H) and fewer than 512 (K/V head, 128-key tile)
- * pairs, fa_bwd gives every query head its own dK/dV workgroups and the
- * workspace also holds their fp32 partial dK and dV, [B,H,N,d] each, summed
- * over each group by a second kernel.  Returns 0 if a size is < 1, Hkv does
+ * pairs, fa_bwd splits the G = H/Hkv query heads of a K/V head into groups of
+ * s, each with dK/dV workgroups of its own: s is the largest divisor of G
+ * below G that gives at least 512 workgroups (1 if none does).  The workspace
+ * then also holds their fp32 partial dK and dV, [B*H/s, N, d] each, summed
+ * over the groups by a second kernel.  Returns 0 if a size is < 1, Hkv does
  * not divide H or the total overflows.
  */
 size_t fa_bwd_workspace_bytes(int B, int H, int Hkv, int N, int d);

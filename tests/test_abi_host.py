@@ -186,21 +186,31 @@ def test_bwd_workspace_size():
     assert fa.fa_bwd_workspace_bytes(1, 4, 3, 16, 64) == 0           # Hkv must divide H
 
 
-@pytest.mark.parametrize("B,H,Hkv,N,split", [
-    (4, 16, 4, 2048, True),      # 16 key tiles x 16 K/V heads = 256 workgroups
-    (4, 32, 8, 2048, False),     # 512: enough workgroups, sum in registers
-    (64, 16, 8, 256, False),     # 2 key tiles x 512 = 1024
-    (63, 16, 8, 128, True),      # 1 key tile x 504
-    (64, 16, 8, 128, False),     # 1 key tile x 512
-    (21, 16, 8, 384, True),      # 3 key tiles x 168 = 504
-    (21, 16, 8, 385, False),     # ragged: 4 key tiles x 168 = 672
-    (4, 16, 16, 2048, False),    # no grouping: never split
+@pytest.mark.parametrize("B,H,Hkv,N,s", [
+    (4, 16, 4, 2048, 2),         # 16 key tiles x 16 K/V heads = 256 pairs; 2 groups of 2 -> 512
+    (4, 32, 4, 2048, 4),         # 256 pairs, G = 8: 2 groups of 4 -> 512
+    (2, 32, 4, 2048, 2),         # 128 pairs, G = 8: 4 groups of 2 -> 512
+    (1, 32, 1, 2048, 1),         # MQA, 16 pairs: even single heads give only 512
+    (4, 32, 8, 2048, 0),         # 512 pairs: enough workgroups, sum in registers
+    (64, 16, 8, 256, 0),         # 2 key tiles x 512 = 1024
+    (63, 16, 8, 128, 1),         # 1 key tile x 504, G = 2: single heads
+    (64, 16, 8, 128, 0),         # 1 key tile x 512
+    (21, 16, 8, 384, 1),         # 3 key tiles x 168 = 504
+    (21, 16, 8, 385, 0),         # ragged: 4 key tiles x 168 = 672
+    (4, 16, 16, 2048, 0),        # no grouping: never split
 ])
-def test_bwd_workspace_grouped_split(B, H, Hkv, N, split):
-    # the grouped-head split adds fp32 partial dK and dV, [B,H,N,d] each
+def test_bwd_workspace_grouped_split(B, H, Hkv, N, s):
+    # the grouped-head split (s query heads per workgroup) adds fp32 partial
+    # dK and dV, [B*H/s, N, d] each; s is the largest divisor of G below G
+    # that reaches 512 workgroups, else 1
     d = 64
+    G, pairs = H // Hkv, -(-N // 128) * B * Hkv
+    if Hkv == H or pairs >= 512:
+        assert s == 0
+    else:
+        assert s == next((t for t in range(G // 2, 1, -1) if G % t == 0 and pairs * (G // t) >= 512), 1)
     rows = 2 * ((B * H * N * 4 + 255) // 256 * 256)
-    want = rows + (2 * B * H * N * d * 4 if split else 0)
+    want = rows + (2 * (B * H // s) * N * d * 4 if s else 0)
     assert fa.fa_bwd_workspace_bytes(B, H, Hkv, N, d) == want
 
 

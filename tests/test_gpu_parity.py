@@ -440,7 +440,7 @@ def test_bwd_gqa(B, H, Hkv, N, d, causal):
 def test_bwd_gqa_large_grid_sums_in_registers():
     # 2 key tiles x 512 K/V heads = 1024 dK/dV workgroups: enough work for the
     # kernel to sum each group in registers (the workspace has no partials).
-    # The small grouped shapes above take the per-query-head split instead.
+    # The small grouped shapes above split the query heads instead.
     fa = _fa()
     B, H, Hkv, N, d = 64, 16, 8, 256, 64
     G = H // Hkv
@@ -509,6 +509,43 @@ def test_bwd_d256_deterministic():
     b = fa.attention_backward(q, k, v, o, lse, do, is_causal=True)
     torch.cuda.synchronize()
     for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("B,H,Hkv,N,d,causal", [
+    (4, 16, 4, 2048, 128, True),     # 256 (K/V head, key tile) pairs: groups of 2 query heads
+    (4, 32, 4, 2048, 128, True),     # G = 8: groups of 4
+    (4, 16, 4, 2000, 64, False),     # groups of 2, ragged, no mask
+    (4, 16, 4, 2048, 256, True),     # groups of 2 at d = 256
+])
+def test_bwd_gqa_head_groups_sampled(B, H, Hkv, N, d, causal):
+    # Few (K/V head, key tile) pairs: the dK/dV kernel splits each K/V head's
+    # query heads into groups and sums the groups' fp32 partials afterwards.
+    # The workspace size shows the group size; sampled (batch, K/V head)
+    # pairs are checked against the oracle.
+    fa = _fa()
+    G, pairs = H // Hkv, -(-N // 128) * B * Hkv
+    s = next((t for t in range(G // 2, 1, -1) if G % t == 0 and pairs * (G // t) >= 512), 1)
+    assert s > 1
+    rows = 2 * ((B * H * N * 4 + 255) // 256 * 256)
+    assert fa.fa_bwd_workspace_bytes(B, H, Hkv, N, d) == rows + 2 * (B * H // s) * N * d * 4
+    q, k, v, do = W.make_gqa(B, H, Hkv, N, d, "bf16", seed=4500 + G + d, with_dout=True, device=DEV)
+    scale = 1.0 / math.sqrt(d)
+    say(f"fa_bwd gqa head groups of {s} B{B} H{H} Hkv{Hkv} N{N} d{d} causal={causal}")
+    o, lse = fa.attention(q, k, v, is_causal=causal, scale=scale)
+    dq, dk, dv = fa.attention_backward(q, k, v, o, lse, do, is_causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    for b, hk in [(0, 0), (B - 1, Hkv - 1)]:
+        qs = (slice(b, b + 1), slice(hk * G, hk * G + G))
+        ks = (slice(b, b + 1), slice(hk, hk + 1))
+        rq, rk, rv = ref_bwd(to64(q[qs]), to64(k[ks]), to64(v[ks]), to64(do[qs]), causal, scale)
+        assert_grad_close(to64(dq[qs]), rq, f"dQ {(b, hk)}")
+        assert_grad_close(to64(dk[ks]), rk, f"dK {(b, hk)}")
+        assert_grad_close(to64(dv[ks]), rv, f"dV {(b, hk)}")
+    # deterministic: the groups are summed in a fixed order
+    again = fa.attention_backward(q, k, v, o, lse, do, is_causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    for x, y in zip((dq, dk, dv), again):
         assert torch.equal(x, y)
 
 
