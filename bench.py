@@ -676,12 +676,10 @@ def _step_kernels():
     return {
         "fwd": ("fwd_bf16_kernel", "fa_fwd.hip", "B4 H16 N2048 d128 causal", 4 * t + r,
                 "read Q, K, V; write O, LSE"),
-        "bwd_prep": ("bwd_prep_kernel", "fa_bwd.hip", "B4 H16 N2048 d128 causal", 2 * t + 3 * r,
-                     "read O, dO, LSE; write D, LSE log2 e"),
         "bwd_dkdv": ("bwd_dkdv_kernel", "fa_bwd.hip", "B4 H16 N2048 d128 causal", 6 * t + 2 * r,
                      "read Q, K, V, dO, LSE, D; write dK, dV"),
-        "bwd_dq": ("bwd_dq_kernel", "fa_bwd.hip", "B4 H16 N2048 d128 causal", 5 * t + 2 * r,
-                   "read Q, K, V, dO, LSE, D; write dQ"),
+        "bwd_dq": ("bwd_dq_kernel", "fa_bwd.hip", "B4 H16 N2048 d128 causal", 6 * t + 3 * r,
+                   "read Q, K, V, dO, O, LSE; write dQ, D, LSE log2 e"),
         "decode": ("decode_split_kernel", "fa_decode.hip", "B64 H32 L8192 d128",
                    2 * Bd * Hd * L * d * 2, "read the K and V caches"),
         "decode_merge": ("decode_merge_kernel", "fa_decode.hip", "B64 H32 L8192 d128", None,
@@ -899,7 +897,7 @@ def main():
         parts["bwd"] = {"ms": round(ms["bwd"], 4), "ms_median": round(med["bwd"], 4), "ms_min": round(mins["bwd"], 4),
                         "tflops": round(tf, 1)}
         tr = [traffic_record("bwd_dkdv"), traffic_record("bwd_dq")]
-        roofs.append({"kernel": "fa_bwd (bwd_prep + bwd_dkdv_kernel<128,causal> + bwd_dq_kernel<128,causal>)",
+        roofs.append({"kernel": "fa_bwd (bwd_dq_kernel<128,causal> + bwd_dkdv_kernel<128,causal>)",
                       "bound": "mfma", "achieved": round(tf, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                       "frac": round(tf / PEAK_BF16_TFLOPS, 4),
                       "traffic": None if None in tr else sum(tr),

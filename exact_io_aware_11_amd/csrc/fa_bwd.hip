@@ -8,9 +8,19 @@
 //     dV = P^T dO,  dP = dO V^T,  D_i = sum_k dO_ik O_ik,
 //     dS = P * (dP - D),  dK = scale dS^T Q,  dQ = scale dS K.
 //
-// Three launches on the caller's stream:
-//   1. bwd_prep:  D = rowsum(dO * O) in fp32, and the LSE in base-2 units
-//                 (LSE log2 e), the form both later kernels exponentiate.
+// Two launches on the caller's stream (three with the grouped split):
+//   1. bwd_dq:    one workgroup per tile of 128 query rows, streaming the K/V
+//                 tiles of its head like the forward pass: it recomputes S, P
+//                 and dP, forms dS and accumulates dQ^T = K^T dS^T in
+//                 registers.  Each lane holds half of its query row's dO, so
+//                 it also forms that row's D = rowsum(dO * O) in fp32 (one
+//                 exchange with lane ^ 32) and writes D and the LSE in base-2
+//                 units (LSE log2 e) to the workspace for the next kernel.
+//                 Recomputing S and dP a second time costs three more matrix
+//                 products than accumulating dQ with atomics from the key-tile
+//                 kernel, but those atomics measured slower than the
+//                 products, and this way dQ needs no fp32 accumulator, no
+//                 extra pass and is deterministic.
 //   2. bwd_dkdv:  one workgroup per tile of BC = 128 keys of one K/V head (4
 //                 waves, 32 keys each), walking the query tiles (BR = 64 rows)
 //                 that can see its keys -- for each of the H/Hkv query heads
@@ -25,15 +35,7 @@
 //                 each group of s query heads (s dividing H/Hkv, chosen to
 //                 give just enough workgroups) gets workgroups of its own,
 //                 which store fp32 partial dK^T / dV^T rows, and bwd_kv_reduce
-//                 sums them over the groups in order (a fourth launch).
-//   3. bwd_dq:    one workgroup per tile of 128 query rows, streaming the K/V
-//                 tiles of its head like the forward pass: it recomputes S, P
-//                 and dP, forms dS and accumulates dQ^T = K^T dS^T in
-//                 registers.  Recomputing S and dP a second time costs three
-//                 more matrix products than accumulating dQ with atomics from
-//                 the key-tile kernel, but those atomics measured slower than
-//                 the products, and this way dQ needs no fp32 accumulator, no
-//                 extra pass and is deterministic.
+//                 sums them over the groups in order (a third launch).
 //
 // Layout trick (as in the forward): with queries as MFMA rows and keys as
 // columns, each lane holds one key and 16 queries, and those registers are
@@ -61,58 +63,7 @@ constexpr int BWD_BC = kBwdKeyTile;   // keys per workgroup (4 waves x 32)
 constexpr int BWD_THREADS = 256;
 
 // ---------------------------------------------------------------------------
-// 1. D = rowsum(dO * O).  d/8 lanes per row.
-// ---------------------------------------------------------------------------
-template <int D, bool O_BF16>
-__global__ void __launch_bounds__(256)
-bwd_prep_kernel(const void* __restrict__ O, const __bf16* __restrict__ dO, const float* __restrict__ lse,
-                float* __restrict__ delta, float* __restrict__ lse2, long long rows) {
-    constexpr int LPR = D / 8;
-    const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
-    const long long row = gid / LPR;
-    const int part = (int)(gid % LPR);
-    const bool live = row < rows;
-    float acc = 0.f;
-    if (live) {
-        const size_t base = (size_t)row * D + 8 * part;
-        const uint4 du = *reinterpret_cast<const uint4*>(dO + base);
-        const uint32_t* dp = reinterpret_cast<const uint32_t*>(&du);
-        float ov[8];
-        if (O_BF16) {
-            const uint4 ou = *reinterpret_cast<const uint4*>(static_cast<const __bf16*>(O) + base);
-            const uint32_t* op = reinterpret_cast<const uint32_t*>(&ou);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                ov[2 * j] = bf16_lo(op[j]);
-                ov[2 * j + 1] = bf16_hi(op[j]);
-            }
-        } else {
-            const float4 a = *reinterpret_cast<const float4*>(static_cast<const float*>(O) + base);
-            const float4 b = *reinterpret_cast<const float4*>(static_cast<const float*>(O) + base + 4);
-            ov[0] = a.x; ov[1] = a.y; ov[2] = a.z; ov[3] = a.w;
-            ov[4] = b.x; ov[5] = b.y; ov[6] = b.z; ov[7] = b.w;
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            acc = fmaf(bf16_lo(dp[j]), ov[2 * j], acc);
-            acc = fmaf(bf16_hi(dp[j]), ov[2 * j + 1], acc);
-        }
-    }
-    if constexpr (LPR == 8) {
-        acc = dpp_sum8(acc);
-    } else {
-        acc = dpp_sum16(acc);
-        if constexpr (LPR == 32) acc += __shfl_xor(acc, 16);   // d = 256: two 16-lane rows per row
-    }
-    if (live && part == 0) {
-        delta[row] = acc;
-        // one rounding, the same as forming LSE log2 e where it is used
-        lse2[row] = lse[row] * kLog2e;
-    }
-}
-
-// ---------------------------------------------------------------------------
-// 2. main kernel
+// dK/dV kernel
 // ---------------------------------------------------------------------------
 // Q and dO tiles live in LDS row-major (2*D bytes per row, no padding),
 // filled by direct global -> LDS copies.  Each is read two ways: 16-byte
@@ -583,7 +534,8 @@ bwd_kv_reduce_kernel(const float* __restrict__ pdk, const float* __restrict__ pd
 }
 
 // ---------------------------------------------------------------------------
-// 3. dQ kernel: query-tile outer, K/V tiles streamed through LDS.
+// dQ kernel: query-tile outer, K/V tiles streamed through LDS; also forms D
+// and the base-2 LSE for the dK/dV kernel.
 // ---------------------------------------------------------------------------
 constexpr int DQ_BR = 128;       // query rows per workgroup (4 waves x 32)
 // keys per K/V tile: 64, or 32 at d = 256 (as in the forward), where Q^T and
@@ -600,8 +552,8 @@ constexpr int DQ_VALU_EACH = 8;     // and between the following ones
 template <int D, bool CAUSAL>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 256 ? 1 : 2)))
 bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
-              const __bf16* __restrict__ dO, const float* __restrict__ LSE2 /* LSE log2 e */,
-              const float* __restrict__ delta, __bf16* __restrict__ dQ, int BH, int G, int N, int nqt, float c /* scale*log2e */, float scale) {
+              const __bf16* __restrict__ dO, const void* __restrict__ O, int o_bf16, const float* __restrict__ LSE,
+              float* __restrict__ delta, float* __restrict__ LSE2, __bf16* __restrict__ dQ, int BH, int G, int N, int nqt, float c /* scale*log2e */, float scale) {
     constexpr int BR = DQ_BR, BC = dq_bc<D>();
     constexpr int ROWB = 2 * D;
     constexpr int CPR = D / 8;
@@ -650,9 +602,44 @@ bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const 
         qf[ks] = as_bf16x8(uq);
         df[ks] = as_bf16x8(ud);
     }
-    // rows past the end get LSE = +inf (P = 0)
-    const float lse2 = row_live ? LSE2[(size_t)bh * N + qrow] : INFINITY;
-    const float dd = row_live ? delta[(size_t)bh * N + qrow] : 0.f;
+    // D = rowsum(dO * O) of this lane's row: the lane holds chunks 16*ks + 8*g
+    // of dO, lane ^ 32 the other half.  With the base-2 LSE it goes to the
+    // workspace for the dK/dV kernel.  Rows past the end get LSE = +inf (P = 0).
+    float dpart = 0.f;
+    if (row_live) {
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+            const size_t oe = hoff + (size_t)qrow * D + 16 * ks + 8 * g;
+            float ov[8];
+            if (o_bf16) {
+                const uint4 ou = *reinterpret_cast<const uint4*>(static_cast<const __bf16*>(O) + oe);
+                const uint32_t* op = reinterpret_cast<const uint32_t*>(&ou);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    ov[2 * j] = bf16_lo(op[j]);
+                    ov[2 * j + 1] = bf16_hi(op[j]);
+                }
+            } else {
+                const float4 a = *reinterpret_cast<const float4*>(static_cast<const float*>(O) + oe);
+                const float4 b = *reinterpret_cast<const float4*>(static_cast<const float*>(O) + oe + 4);
+                ov[0] = a.x; ov[1] = a.y; ov[2] = a.z; ov[3] = a.w;
+                ov[4] = b.x; ov[5] = b.y; ov[6] = b.z; ov[7] = b.w;
+            }
+            const uint4 du = __builtin_bit_cast(uint4, df[ks]);
+            const uint32_t* dp = reinterpret_cast<const uint32_t*>(&du);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                dpart = fmaf(bf16_lo(dp[j]), ov[2 * j], dpart);
+                dpart = fmaf(bf16_hi(dp[j]), ov[2 * j + 1], dpart);
+            }
+        }
+    }
+    const float dd = dpart + __shfl_xor(dpart, 32);
+    const float lse2 = row_live ? LSE[(size_t)bh * N + qrow] * kLog2e : INFINITY;
+    if (row_live && g == 0) {
+        delta[(size_t)bh * N + qrow] = dd;
+        LSE2[(size_t)bh * N + qrow] = lse2;
+    }
 
     const int kv_end = CAUSAL ? min(N, q0 + BR) : N;
     const int nkt = (kv_end + BC - 1) / BC;
@@ -800,18 +787,16 @@ template <int D, bool CAUSAL>
 hipError_t launch_kernels(const BwdArgs& a) {
     hipStream_t st = (hipStream_t)a.stream;
     const int BH = a.B * a.H;
-    const long long rows = (long long)BH * a.N;
-    const unsigned prep_blocks = (unsigned)((rows * (D / 8) + 255) / 256);
-    if (a.o_bf16)
-        hipLaunchKernelGGL((bwd_prep_kernel<D, true>), dim3(prep_blocks), dim3(256), 0, st, a.o,
-                           (const __bf16*)a.dout, a.lse, a.delta, a.lse2, rows);
-    else
-        hipLaunchKernelGGL((bwd_prep_kernel<D, false>), dim3(prep_blocks), dim3(256), 0, st, a.o,
-                           (const __bf16*)a.dout, a.lse, a.delta, a.lse2, rows);
+    const int G = a.H / a.Hkv, BHkv = a.B * a.Hkv;
+    // dQ first: it also writes D and the base-2 LSE that the dK/dV kernel reads
+    const int nqt = (a.N + DQ_BR - 1) / DQ_BR;
+    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)(nqt * BH)), dim3(256), 0, st,
+                       (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (const __bf16*)a.dout, a.o,
+                       a.o_bf16 ? 1 : 0, a.lse, a.delta, a.lse2, (__bf16*)a.dq, BH, G, a.N, nqt, a.scale * kLog2e,
+                       a.scale);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int nkt = (a.N + BWD_BC - 1) / BWD_BC;
-    const int G = a.H / a.Hkv, BHkv = a.B * a.Hkv;
     if (a.split) {
         const int hpg = a.split, ngr = G / hpg;     // query heads per group, groups per K/V head
         if (hpg < 1 || G % hpg != 0) return hipErrorInvalidValue;
@@ -830,20 +815,12 @@ hipError_t launch_kernels(const BwdArgs& a) {
                            a.lse2, a.delta, (__bf16*)a.dk, (__bf16*)a.dv, nullptr, nullptr, BHkv, G, G, a.N,
                            a.scale * kLog2e, a.scale);
     }
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const int nqt = (a.N + DQ_BR - 1) / DQ_BR;
-    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)(nqt * BH)), dim3(256), 0, st,
-                       (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (const __bf16*)a.dout, a.lse2,
-                       a.delta, (__bf16*)a.dq, BH, G, a.N, nqt, a.scale * kLog2e, a.scale);
     return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_bwd(const BwdArgs& a) {
-    const long long rows = (long long)a.B * a.H * a.N;
-    if (rows * (a.d / 8) / 256 + 1 > 0x7fffffffLL) return hipErrorInvalidValue;
     if (a.d == 64) return a.causal ? launch_kernels<64, true>(a) : launch_kernels<64, false>(a);
     if (a.d == 256) return a.causal ? launch_kernels<256, true>(a) : launch_kernels<256, false>(a);
     return a.causal ? launch_kernels<128, true>(a) : launch_kernels<128, false>(a);

@@ -47,8 +47,8 @@ struct BwdArgs {
     void* dq;
     void* dk;
     void* dv;
-    float* delta;    // workspace: [B,H,N] fp32, rowsum(dO * O)
-    float* lse2;     // workspace: [B,H,N] fp32, LSE log2 e (written by the prep kernel)
+    float* delta;    // workspace: [B,H,N] fp32, rowsum(dO * O) (written by the dQ kernel)
+    float* lse2;     // workspace: [B,H,N] fp32, LSE log2 e (written by the dQ kernel)
     float* pdk;      // workspace when split: [B*H/s, N, d] fp32 partial dK^T rows per head group
     float* pdv;      // workspace when split: [B*H/s, N, d] fp32 partial dV^T rows per head group
     int split;       // bwd_split_heads(B, H, Hkv, N): query heads per split workgroup, 0 = no split
