@@ -68,6 +68,8 @@ def parse():
                     help="skip the grouped-query, paged-cache, head-dim-256 and fp8 measurements")
     ap.add_argument("--no-configs", action="store_true", help="skip the per-workload measurements")
     ap.add_argument("--no-ceilings", action="store_true", help="skip the probe-library calibration")
+    ap.add_argument("--settle-ms", type=float, default=200.0,
+                    help="untimed whole steps for at least this long before the warm-up steps (0: none)")
     ap.add_argument("--reduce-counters", nargs="+", metavar="DIR",
                     help="host only: summarise rocprofv3 --pmc output of this script and exit")
     ap.add_argument("--write-traffic", action="store_true",
@@ -852,6 +854,19 @@ def main():
     stages = {"fwd": run_fwd, "bwd": run_bwd, "decode": run_decode}
     active = list(stages)
 
+    # The chip reaches the timed loop at a lower clock when only a few steps
+    # precede it: measured on MI355X with 20 timed steps, 5 warm-up steps gave
+    # 650-664 TFLOP/s, 20 gave 683-686 and 50 gave 701.  So before the W warm-up
+    # steps, whole steps run untimed (each synchronised) until --settle-ms of
+    # wall time have passed; the timed region is still exactly K steps.
+    settle_steps, t_s = 0, time.perf_counter()
+    while (time.perf_counter() - t_s) * 1e3 < args.settle_ms:
+        for name in active:
+            stages[name](fa, b, stream)
+        torch.cuda.synchronize()
+        settle_steps += 1
+    settle_ms = (time.perf_counter() - t_s) * 1e3
+    log(f"settle {settle_steps} steps ({settle_ms:.0f} ms)")
     log(f"warmup {args.warmup} steps ({', '.join(active)})")
     for _ in range(args.warmup):
         for name in active:
@@ -987,8 +1002,10 @@ def main():
                     | ({"frac_of_measured_ceiling": dominant["frac_of_measured_ceiling"]}
                        if "frac_of_measured_ceiling" in dominant else {}),
         "rooflines": roofs,
-        "timing": "step: per-call HIP events over the timed steps (mean; median and min in parts); every other "
-                  "figure: >= 50 ms warm-up, then >= 20 single calls and >= 200 ms, median (min as *_best)",
+        "timing": "step: untimed settle steps for >= settle_ms, then the warm-up steps, then per-call HIP events "
+                  "over the timed steps (mean; median and min in parts); every other figure: >= 50 ms warm-up, then "
+                  ">= 20 single calls and >= 200 ms, median (min as *_best)",
+        "settle": {"steps": settle_steps, "ms": round(settle_ms, 1)},
         "configs": configs,
         "sweep": sweep_res,
         "next_rows": next_rows,
