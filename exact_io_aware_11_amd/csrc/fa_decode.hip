@@ -27,6 +27,8 @@
 #include "fa_common.hpp"
 #include "fa_internal.hpp"
 
+#include <type_traits>
+
 namespace fa {
 
 namespace {
@@ -707,34 +709,36 @@ decode_merge_kernel(const float* __restrict__ Opart, const float* __restrict__ L
     tot = wave_sum(tot);
     const float lse = (tot > 0.f) ? Mu + __logf(tot) : -INFINITY;
     constexpr int PER = D / 64;
-    constexpr int U = 8;
+    // partial rows loaded before they are combined: 64 registers' worth
+    // (64, 32, 16 rows at d = 64, 128, 256), then blocks of 8, then single
+    // rows, so that 64 splits take two load rounds at d = 128, not eight
+    constexpr int U = 64 / PER;
     float acc[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) acc[i] = 0.f;
     const float* orow = Opart + (size_t)bh * S * D + lane;
+    // rows s0 + j .. s0 + j + R - 1, in split order
+    auto block = [&](auto R, int s0, int j, float wl) __attribute__((always_inline)) {
+        float v[decltype(R)::value][PER];
+#pragma unroll
+        for (int u = 0; u < decltype(R)::value; ++u)
+#pragma unroll
+            for (int i = 0; i < PER; ++i) v[u][i] = orow[(size_t)(s0 + j + u) * D + 64 * i];
+#pragma unroll
+        for (int u = 0; u < decltype(R)::value; ++u) {
+            const float wu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), j + u));
+#pragma unroll
+            for (int i = 0; i < PER; ++i) acc[i] = fmaf(wu, v[u][i], acc[i]);
+        }
+    };
     for (int s0 = 0; s0 < S; s0 += 64) {
         // weight of split s0 + lane; split s0 + j's weight is read from lane j
         const float wl = (s0 + lane < S && tot > 0.f) ? __expf(lp[s0 + lane] - lse) : 0.f;
         const int n = min(64, S - s0);
         int j = 0;
-        for (; j + U <= n; j += U) {
-            float v[U][PER];
-#pragma unroll
-            for (int u = 0; u < U; ++u)
-#pragma unroll
-                for (int i = 0; i < PER; ++i) v[u][i] = orow[(size_t)(s0 + j + u) * D + 64 * i];
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const float wu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), j + u));
-#pragma unroll
-                for (int i = 0; i < PER; ++i) acc[i] = fmaf(wu, v[u][i], acc[i]);
-            }
-        }
-        for (; j < n; ++j) {
-            const float wu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), j));
-#pragma unroll
-            for (int i = 0; i < PER; ++i) acc[i] = fmaf(wu, orow[(size_t)(s0 + j) * D + 64 * i], acc[i]);
-        }
+        for (; j + U <= n; j += U) block(std::integral_constant<int, U>{}, s0, j, wl);
+        for (; j + 8 <= n; j += 8) block(std::integral_constant<int, 8>{}, s0, j, wl);
+        for (; j < n; ++j) block(std::integral_constant<int, 1>{}, s0, j, wl);
     }
 #pragma unroll
     for (int i = 0; i < PER; ++i) O[(size_t)bh * D + lane + 64 * i] = (__bf16)acc[i];
