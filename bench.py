@@ -261,7 +261,8 @@ def configs_measure(torch, fa, W, dev):
     out["C1"] = {"workload": "fwd fp32 B1 H1 N128 d64 non-causal", "us": round(st["median_ms"] * 1e3, 2),
                  "us_min": round(st["min_ms"] * 1e3, 2), "calls": st["calls"],
                  "tflops": round(fl / (st["median_ms"] * 1e-3) / 1e12, 3),
-                 "note": "launch-latency bound (4.19 MFLOP); the fp32 matrix peak is "
+                 "note": "latency-bound: 4.19 MFLOP on one workgroup of one CU (the kernel itself takes ~16 us, "
+                         "chains of dependent fp32 MFMAs and the loads); the fp32 matrix peak is "
                          f"{PEAK_FP32_MATRIX_TFLOPS} TFLOP/s, for information only"}
     log(f"C1 {out['C1']['workload']}: {out['C1']['us']} us")
 

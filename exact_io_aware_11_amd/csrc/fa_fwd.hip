@@ -84,23 +84,37 @@ fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
     const int nkt = (kv_end + BC - 1) / BC;
     const int wrow0 = q0 + 32 * w;
 
-    for (int kt = 0; kt < nkt; ++kt) {
+    // The next tile's K and V rows are loaded into registers while the
+    // current tile is computed, and stored to LDS after it.
+    float4 kk[CPT], vv[CPT];
+    auto load = [&](int kt) __attribute__((always_inline)) {
         const int kv0 = kt * BC;
-        __syncthreads();
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
             const int ch = tid + FWD_THREADS * i;
             const int row = ch / (D / 4), c4 = ch % (D / 4);
-            float4 kk = make_float4(0.f, 0.f, 0.f, 0.f), vv = kk;
+            kk[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+            vv[i] = kk[i];
             if (kv0 + row < N) {
-                kk = *reinterpret_cast<const float4*>(Kh + (size_t)(kv0 + row) * D + 4 * c4);
-                vv = *reinterpret_cast<const float4*>(Vh + (size_t)(kv0 + row) * D + 4 * c4);
+                kk[i] = *reinterpret_cast<const float4*>(Kh + (size_t)(kv0 + row) * D + 4 * c4);
+                vv[i] = *reinterpret_cast<const float4*>(Vh + (size_t)(kv0 + row) * D + 4 * c4);
             }
+        }
+    };
+    if (nkt > 0) load(0);
+    for (int kt = 0; kt < nkt; ++kt) {
+        const int kv0 = kt * BC;
+        __syncthreads();                           // every wave is done with the previous tile
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            const int ch = tid + FWD_THREADS * i;
+            const int row = ch / (D / 4), c4 = ch % (D / 4);
             float* kd = Ks + row * KS + 4 * c4;
-            kd[0] = kk.x; kd[1] = kk.y; kd[2] = kk.z; kd[3] = kk.w;
-            *reinterpret_cast<float4*>(Vs + row * VS + 4 * c4) = vv;
+            kd[0] = kk[i].x; kd[1] = kk[i].y; kd[2] = kk[i].z; kd[3] = kk[i].w;
+            *reinterpret_cast<float4*>(Vs + row * VS + 4 * c4) = vv[i];
         }
         __syncthreads();
+        if (kt + 1 < nkt) load(kt + 1);
         if (wrow0 >= N) continue;
         if (CAUSAL && kv0 > wrow0 + 31) continue;
 
