@@ -712,9 +712,20 @@ bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const 
                 st[kb] = mfma_bf16(*reinterpret_cast<const bf16x8*>(Ks + 32 * kb * ROWB + ko[ks]), qf[ks], st[kb]);
                 pt[kb] = mfma_bf16(*reinterpret_cast<const bf16x8*>(Vs + 32 * kb * ROWB + vo[ks]), df[ks], pt[kb]);
             }
-        // dS^T = P^T (dP^T - D), P^T = 2^(c S^T - LSE log2 e), masked
+        // Mask, only on tiles that cross the diagonal or the end: masked
+        // scores become -inf, so P = 2^(-inf) = 0 below.  Kept out of the dS
+        // loop, which would otherwise carry a compare and a select per element
+        // on every tile.
         const bool need_mask = (kt * BC + BC > N) || (CAUSAL && kt * BC + BC - 1 > wrow0);
-        const int lim = last_visible - kt * BC - 4 * g;
+        if (need_mask) {
+            const int lim = last_visible - kt * BC - 4 * g;
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    if (32 * kb + 8 * (r >> 2) + (r & 3) > lim) st[kb][r] = -INFINITY;
+        }
+        // dS^T = P^T (dP^T - D), P^T = 2^(c S^T - LSE log2 e)
         bf16x8 sb[BC / 16];
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
@@ -727,8 +738,7 @@ bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const 
 #pragma unroll
                     for (int t = 0; t < 2; ++t) {
                         const int r = 8 * h + j + t;
-                        float p = exp2_fast(fmaf(st[kb][r], c, -lse2));
-                        if (need_mask && 32 * kb + 8 * (r >> 2) + (r & 3) > lim) p = 0.f;
+                        const float p = exp2_fast(fmaf(st[kb][r], c, -lse2));
                         v2[t] = p * (pt[kb][r] - dd);
                     }
                     pk[j / 2] = pack_bf16x2(v2[0], v2[1]);
