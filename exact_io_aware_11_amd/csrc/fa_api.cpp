@@ -247,7 +247,8 @@ fa_status_t decode_launch(const void* q, const void* k_cache, const void* v_cach
     float* o_part = static_cast<float*>(workspace);
     float* lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                                (((parts * (size_t)d * sizeof(float)) + 255) & ~(size_t)255));
-    fa::DecodeArgs a{q, k_cache, v_cache, o, lse, o_part, lse_part, B, H, Hkv, L, d, splits, chunk, scale, stream};
+    fa::DecodeArgs a{q, k_cache, v_cache, o, lse, o_part, lse_part, B, H, Hkv, L, d, splits, chunk, scale, stream,
+                     fa::Paging{}};   // contiguous cache: no block table
     return from_hip(fa::launch_decode(a));
 }
 
