@@ -11,13 +11,14 @@
 // sequences fill the chip ("Flash Attention uitgelegd", FA2 section on
 // parallelism over the sequence length).
 //
-// bf16 path (d = 64, 128 or 256): four waves, 32 query rows each, two
-// workgroups per CU (one at d = 256, whose tiles and accumulators are twice
-// as large).  Per key tile of BC = 64 keys a wave computes
-// S^T = K Q^T (keys x queries) with v_mfma_f32_32x32x16_bf16: K comes from
-// LDS, Q^T stays in registers for the whole kernel.  In the C layout each lane
-// then holds one query row and 16 of the tile's keys, so row max and row sum
-// are in-lane work plus one exchange with lane ^ 32.  The probabilities,
+// bf16 path (d = 64, 128 or 256): four waves, 32 query rows each.  Key tiles
+// of BC = 64 keys at d = 64 (four workgroups per CU), 32 keys at d = 128
+// (three per CU) and at d = 256 (two per CU, whose accumulators are twice as
+// large).  Per key tile a wave computes S^T = K Q^T (keys x queries) with
+// v_mfma_f32_32x32x16_bf16: K comes from LDS, Q^T stays in registers for the
+// whole kernel.  In the C layout each lane then holds one query row and 16
+// of the tile's keys, so row max and row sum are in-lane work plus one
+// exchange with lane ^ 32.  The probabilities,
 // rounded to bf16, are already a valid B operand of O^T += V^T P^T; the V^T A
 // operand is read from the row-major V tile with the transposing LDS read.
 // O^T again gives each lane one query row.  K and V tiles are copied

@@ -16,11 +16,18 @@ namespace fa {
 namespace {
 
 constexpr int FWD_BR = 128;     // query rows per workgroup (4 waves x 32)
-constexpr int FWD_BC = 64;      // keys per K/V tile, bf16 path (d <= 128)
-// d = 256: 32-key tiles, so that S, P and the 256-column O accumulator fit the
-// 256 vector registers of two waves per SIMD
+// Keys per K/V tile of the bf16 path.  d = 64 takes 64-key tiles (four waves
+// per SIMD either way).  d = 128 takes 32-key tiles: the smaller S and P bring
+// the kernel to 166 registers and 32 KB of LDS, so three workgroups -- three
+// waves per SIMD -- are resident per CU instead of two, which overlaps one
+// wave's softmax with the others' products better than the larger tile's
+// fewer barriers do.  d = 256 also takes 32-key tiles, so that S, P and the
+// 256-column O accumulator fit the registers of two waves per SIMD.
 template <int D>
-constexpr int fwd_bc() { return D == 256 ? 32 : FWD_BC; }
+constexpr int fwd_bc() { return D == 64 ? 64 : 32; }
+// waves per SIMD the register budget is sized for
+template <int D>
+constexpr int fwd_waves() { return D == 64 ? 4 : D == 128 ? 3 : 2; }
 constexpr int FWD_BC32 = 32;    // keys per K/V tile, fp32 path
 // instruction schedule of the bf16 tile loop (measured best on MI355X)
 constexpr int QK_AHEAD = 6;        // K-operand LDS reads kept ahead of the S MFMAs
@@ -33,7 +40,7 @@ constexpr int FWD_THREADS = 256;
 // (k_swz for K, read one chunk per lane by 32 consecutive rows; v_swz for V,
 // read with the transposing 8-byte read).
 template <int D, bool CAUSAL, bool OUT_BF16, bool CLOCK = false>
-__global__ void __launch_bounds__(FWD_THREADS) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ void __launch_bounds__(FWD_THREADS) __attribute__((amdgpu_waves_per_eu(fwd_waves<D>())))
 fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                 const __bf16* __restrict__ V, void* __restrict__ O, float* __restrict__ LSE,
                 int BH, int G, int N, int nqt, float c /* scale * log2(e) */,
