@@ -31,8 +31,10 @@
 // minimising non-matmul work).  With grouped-query attention (Hkv < H K/V
 // heads) query head h reads K/V head h / (H / Hkv).
 //
-// fp32 path: same structure on v_mfma_f32_32x32x2_f32 with BC = 32; V needs no
-// transpose because each fp32 K-slot holds a single key.
+// fp32 path: v_mfma_f32_32x32x2_f32 with BC = 32 (V needs no transpose
+// because each fp32 K-slot holds a single key), one workgroup per 32 query
+// rows whose four waves split the key tiles and merge their partial results
+// at the end (see fwd_f32_kernel).
 //
 // The bf16 kernel template lives in fa_fwd_kernel.hpp; this file holds the
 // fp32 kernel and the launchers.
@@ -43,24 +45,38 @@ namespace fa {
 
 namespace {
 
+// fp32 path.  One workgroup per 32 query rows of one (b, h).  Its four waves
+// split the key tiles -- wave w takes tiles w, w + 4, w + 8, ... -- each with
+// the 32 query rows, its own LDS tile and its own online softmax, so the loop
+// has no barrier.  At the end the four partial results (row max m, row sum l
+// and the unnormalised O of each wave) are combined through LDS with the
+// online-softmax merge rule: O = sum_w 2^(m_w - M) O_w / sum_w 2^(m_w - M) l_w
+// with M = max_w m_w.  A 128-token head then runs on four CUs, each wave on
+// one tile, instead of one CU whose waves each walk all four tiles.
+constexpr int F32_BR = 32;      // query rows per workgroup
+constexpr int F32_NW = FWD_THREADS / 64;   // waves splitting the key tiles
+
 template <int D, bool CAUSAL>
 __global__ void __launch_bounds__(FWD_THREADS)
 fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
                const float* __restrict__ V, float* __restrict__ O, float* __restrict__ LSE,
                int BH, int G, int N, int nqt, float c) {
-    constexpr int BR = FWD_BR, BC = FWD_BC32;
+    constexpr int BR = F32_BR, BC = FWD_BC32, NW = F32_NW;
     constexpr int KS = D + 1;      // odd stride: column reads hit distinct banks
     constexpr int VS = D;
-    constexpr int CH = BC * D / 4;                 // 16-byte chunks per tile
-    constexpr int CPT = CH / FWD_THREADS;
-    static_assert(CH % FWD_THREADS == 0, "tile must split evenly");
+    constexpr int WTILE = BC * KS + BC * VS;       // floats of one wave's K and V tiles
+    constexpr int CPL = BC * D / 4 / 64;           // 16-byte chunks per lane per tile
+    constexpr int OS = D + 4;                      // row stride of the partial outputs
+    static_assert(BR == BC, "the causal diagonal is one tile");
+    static_assert(NW * BR * OS + 2 * NW * BR <= NW * WTILE, "the partials fit the tile space");
 
-    __shared__ __attribute__((aligned(16))) float Ks[BC * KS];
-    __shared__ __attribute__((aligned(16))) float Vs[BC * VS];
+    __shared__ __attribute__((aligned(16))) float smem[NW * WTILE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, g = lane >> 5;
+    float* Ks = smem + w * WTILE;                  // this wave's tiles
+    float* Vs = Ks + BC * KS;
 
     int bh, qt;
     fwd_tile_of(blockIdx.x, BH, G, nqt, CAUSAL, bh, qt);
@@ -71,7 +87,7 @@ fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
     const float* Kh = K + kvoff;
     const float* Vh = V + kvoff;
 
-    const int qrow = q0 + 32 * w + l32;
+    const int qrow = q0 + l32;
     float qf[D / 2];
 #pragma unroll
     for (int ks = 0; ks < D / 2; ++ks) qf[ks] = (qrow < N) ? Qh[(size_t)qrow * D + 2 * ks + g] : 0.f;
@@ -83,16 +99,15 @@ fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
 
     const int kv_end = CAUSAL ? min(N, q0 + BR) : N;
     const int nkt = (kv_end + BC - 1) / BC;
-    const int wrow0 = q0 + 32 * w;
 
-    // The next tile's K and V rows are loaded into registers while the
-    // current tile is computed, and stored to LDS after it.
-    float4 kk[CPT], vv[CPT];
+    // The wave's next tile is loaded into registers while the current one is
+    // computed, and stored to its LDS tile after it.
+    float4 kk[CPL], vv[CPL];
     auto load = [&](int kt) __attribute__((always_inline)) {
         const int kv0 = kt * BC;
 #pragma unroll
-        for (int i = 0; i < CPT; ++i) {
-            const int ch = tid + FWD_THREADS * i;
+        for (int i = 0; i < CPL; ++i) {
+            const int ch = lane + 64 * i;
             const int row = ch / (D / 4), c4 = ch % (D / 4);
             kk[i] = make_float4(0.f, 0.f, 0.f, 0.f);
             vv[i] = kk[i];
@@ -102,28 +117,27 @@ fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
             }
         }
     };
-    if (nkt > 0) load(0);
-    for (int kt = 0; kt < nkt; ++kt) {
+    if (w < nkt) load(w);
+    for (int kt = w; kt < nkt; kt += NW) {
         const int kv0 = kt * BC;
-        __syncthreads();                           // every wave is done with the previous tile
+        // Only this wave touches its tiles, and a wave's LDS operations run in
+        // order, so the previous tile's reads are done before these writes
+        // and the writes before the reads below.
 #pragma unroll
-        for (int i = 0; i < CPT; ++i) {
-            const int ch = tid + FWD_THREADS * i;
+        for (int i = 0; i < CPL; ++i) {
+            const int ch = lane + 64 * i;
             const int row = ch / (D / 4), c4 = ch % (D / 4);
             float* kd = Ks + row * KS + 4 * c4;
             kd[0] = kk[i].x; kd[1] = kk[i].y; kd[2] = kk[i].z; kd[3] = kk[i].w;
             *reinterpret_cast<float4*>(Vs + row * VS + 4 * c4) = vv[i];
         }
-        __syncthreads();
-        if (kt + 1 < nkt) load(kt + 1);
-        if (wrow0 >= N) continue;
-        if (CAUSAL && kv0 > wrow0 + 31) continue;
+        if (kt + NW < nkt) load(kt + NW);
 
         f32x16 s = zero16();
 #pragma unroll
         for (int ks = 0; ks < D / 2; ++ks) s = mfma_f32(Ks[l32 * KS + 2 * ks + g], qf[ks], s);
 
-        if ((kv0 + BC > N) || (CAUSAL && kv0 + BC - 1 > wrow0)) {
+        if ((kv0 + BC > N) || (CAUSAL && kv0 + BC - 1 > q0)) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int key = kv0 + 8 * (r >> 2) + 4 * g + (r & 3);
@@ -158,21 +172,58 @@ fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
         }
     }
 
+    // Merge the waves' partial results.  A wave without tiles (or whose keys
+    // are all hidden) has m = -inf, l = 0 and O = 0 and gets weight 0.
     const float l_tot = xor32_sum(l_run);
-    if (qrow < N) {
-        const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
-        float* orow = O + (size_t)bh * N * D + (size_t)qrow * D;
+    __syncthreads();                               // every wave is done with its tiles
+    float* Op = smem;                              // [NW][BR][OS] unnormalised O
+    float* Mp = smem + NW * BR * OS;               // [NW][BR] row max, log2 units
+    float* Lp = Mp + NW * BR;                      // [NW][BR] row sum
 #pragma unroll
-        for (int mb = 0; mb < D / 32; ++mb)
+    for (int mb = 0; mb < D / 32; ++mb)
 #pragma unroll
-            for (int rb = 0; rb < 4; ++rb) {
-                const int d0 = 32 * mb + 8 * rb + 4 * g;
-                *reinterpret_cast<float4*>(orow + d0) =
-                    make_float4(oacc[mb][4 * rb] * inv, oacc[mb][4 * rb + 1] * inv,
-                                oacc[mb][4 * rb + 2] * inv, oacc[mb][4 * rb + 3] * inv);
+        for (int rb = 0; rb < 4; ++rb)
+            *reinterpret_cast<float4*>(Op + (w * BR + l32) * OS + 32 * mb + 8 * rb + 4 * g) =
+                make_float4(oacc[mb][4 * rb], oacc[mb][4 * rb + 1], oacc[mb][4 * rb + 2], oacc[mb][4 * rb + 3]);
+    if (g == 0) {
+        Mp[w * BR + l32] = m_run;
+        Lp[w * BR + l32] = l_tot;
+    }
+    __syncthreads();
+    // 8 threads per row, each 4 columns at a time: a row is written with
+    // 16-byte stores by consecutive lanes.
+    constexpr int TPR = FWD_THREADS / BR;
+    const int r = tid / TPR, part = tid % TPR;
+    const int row = q0 + r;
+    float M = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < NW; ++v) M = fmaxf(M, Mp[v * BR + r]);
+    float a[NW], L = 0.f;
+#pragma unroll
+    for (int v = 0; v < NW; ++v) {
+        const float mv = Mp[v * BR + r];
+        a[v] = (mv == -INFINITY) ? 0.f : exp2_fast(mv - M);
+        L = fmaf(a[v], Lp[v * BR + r], L);
+    }
+    if (row < N) {
+        const float inv = (L > 0.f) ? 1.f / L : 0.f;
+        float* orow = O + (size_t)bh * N * D + (size_t)row * D;
+#pragma unroll
+        for (int j = 0; j < D / (4 * TPR); ++j) {
+            const int col = 4 * (part + TPR * j);
+            float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+            for (int v = 0; v < NW; ++v) {
+                const float4 p = *reinterpret_cast<const float4*>(Op + (v * BR + r) * OS + col);
+                acc.x = fmaf(a[v], p.x, acc.x);
+                acc.y = fmaf(a[v], p.y, acc.y);
+                acc.z = fmaf(a[v], p.z, acc.z);
+                acc.w = fmaf(a[v], p.w, acc.w);
             }
-        if (g == 0)
-            LSE[(size_t)bh * N + qrow] = (l_tot > 0.f) ? m_run * kLn2 + __logf(l_tot) : -INFINITY;
+            *reinterpret_cast<float4*>(orow + col) = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+        }
+        if (part == 0)
+            LSE[(size_t)bh * N + row] = (L > 0.f) ? M * kLn2 + __logf(L) : -INFINITY;
     }
 }
 
@@ -190,7 +241,7 @@ hipError_t launch_bf16(const FwdArgs& a) {
 template <int D, bool CAUSAL>
 hipError_t launch_f32(const FwdArgs& a) {
     const int BH = a.B * a.H;
-    const int nqt = (a.N + FWD_BR - 1) / FWD_BR;
+    const int nqt = (a.N + F32_BR - 1) / F32_BR;
     const dim3 grid((unsigned)(nqt * BH)), block(FWD_THREADS);
     hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL>), grid, block, 0, (hipStream_t)a.stream,
                        (const float*)a.q, (const float*)a.k, (const float*)a.v, (float*)a.o, a.lse, BH,
@@ -210,7 +261,7 @@ hipError_t dispatch_d(const FwdArgs& a) {
 }  // namespace
 
 hipError_t launch_fwd(const FwdArgs& a) {
-    if ((long long)((a.N + FWD_BR - 1) / FWD_BR) * a.B * a.H > 0x7fffffffLL) return hipErrorInvalidValue;
+    if ((long long)((a.N + F32_BR - 1) / F32_BR) * a.B * a.H > 0x7fffffffLL) return hipErrorInvalidValue;
     if (a.d == 256) return dispatch_d<256>(a);
     return a.d == 64 ? dispatch_d<64>(a) : dispatch_d<128>(a);
 }

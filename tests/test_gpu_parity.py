@@ -98,6 +98,11 @@ SMALL = [
     (1, 3, 200, 128, "bf16", False),
     (1, 2, 1000, 128, "bf16", True),
     (1, 1, 1000, 64, "bf16", False),
+    # d = 128 streams 32-key tiles: lengths at and just past tile edges
+    (1, 2, 32, 128, "bf16", True),
+    (1, 1, 33, 128, "bf16", True),
+    (2, 1, 96, 128, "bf16", False),
+    (1, 2, 161, 128, "bf16", True),
     (1, 1, 1, 64, "fp32", False),
     (1, 2, 33, 128, "fp32", True),
     (2, 1, 129, 64, "fp32", True),
