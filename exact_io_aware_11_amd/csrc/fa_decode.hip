@@ -50,6 +50,14 @@ __device__ __forceinline__ void merge_state(float& ma, float& la, float* oa, flo
     ma = mn;
 }
 
+// A value every lane of the wave reads from the same address of memory the
+// kernel never writes (a block-table entry): read through the scalar data
+// cache.  Scalar loads are counted apart from the vector loads, which retire
+// in order, so waiting for the entry never waits for K/V loads in flight.
+__device__ __forceinline__ int load_uniform(const int* p) {
+    return *(const __attribute__((address_space(4))) int*)p;
+}
+
 template <int D, bool PAGED>
 __global__ void __launch_bounds__(DEC_THREADS)
 decode_split_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ Kc,
@@ -93,15 +101,15 @@ decode_split_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ Kc,
             return ((size_t)gkv * L + key) * D;
         }
     };
-    // block-table entries of this lane's keys of the iteration at `base`
-    // (fetched one iteration ahead, so the table lookup is off the path of
-    // the K/V loads that depend on it)
-    auto fetch_pages = [&](int base, int* pgs) __attribute__((always_inline)) {
-#pragma unroll
-        for (int u = 0; u < DEC_UNROLL; ++u) {
-            const int key = base + u * (64 / (D / 8)) + slot;
-            pgs[u] = (key < k_end) ? pg.block_table[(size_t)b * pg.max_pages + (key >> pg.ps_log2)] : -1;
-        }
+    // Block-table entry of the iteration at `base`, read one iteration ahead
+    // so that the lookup is off the path of the K/V loads that depend on it.
+    // An iteration's STEP keys start at a multiple of STEP (chunks are
+    // multiples of 32 keys and STEP divides 32) and a page holds at least 32
+    // keys, so they all lie in one page: one scalar read per wave.
+    static_assert(32 % STEP == 0, "an iteration's keys lie in one page");
+    auto fetch_page = [&](int base) __attribute__((always_inline)) -> int {
+        const int kb = __builtin_amdgcn_readfirstlane(base);
+        return (kb < k_end) ? load_uniform(pg.block_table + (size_t)b * pg.max_pages + (kb >> pg.ps_log2)) : -1;
     };
 
     // q, pre-multiplied by scale*log2(e), 8 dims per lane
@@ -124,14 +132,12 @@ decode_split_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ Kc,
 #pragma unroll
     for (int j = 0; j < 8; ++j) o[j] = 0.f;
 
-    int pg_next[U] = {};
-    if constexpr (PAGED) fetch_pages(k_begin + w * STEP, pg_next);
+    int pg_next = 0;
+    if constexpr (PAGED) pg_next = fetch_page(k_begin + w * STEP);
     for (int base = k_begin + w * STEP; base < k_end; base += DEC_WAVES * STEP) {
         uint4 kr[U], vr[U];
         bool live[U];
-        int pg_cur[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) pg_cur[u] = pg_next[u];
+        const int pg_cur = pg_next;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int key = base + u * KPL + slot;
@@ -139,14 +145,14 @@ decode_split_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ Kc,
             vr[u] = kr[u];
             live[u] = false;
             if (key < k_end) {
-                const size_t r = row_of(key, pg_cur[u], live[u]);
+                const size_t r = row_of(key, pg_cur, live[u]);
                 if (live[u]) {
                     kr[u] = load_stream16(Kl + r);
                     vr[u] = load_stream16(Vl + r);
                 }
             }
         }
-        if constexpr (PAGED) fetch_pages(base + DEC_WAVES * STEP, pg_next);
+        if constexpr (PAGED) pg_next = fetch_page(base + DEC_WAVES * STEP);
         float x[U];
         float mx = -INFINITY;
 #pragma unroll
@@ -279,12 +285,12 @@ decode_small_group_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
             return ((size_t)gkv * L + key) * D;
         }
     };
-    auto fetch_pages = [&](int base, int* pgs) __attribute__((always_inline)) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int key = base + u * KPL + slot;
-            pgs[u] = (key < k_end) ? pg.block_table[(size_t)b * pg.max_pages + (key >> pg.ps_log2)] : -1;
-        }
+    // block-table entry of the iteration at `base`: one page, one scalar read
+    // per wave, one iteration ahead (as in decode_split_kernel)
+    static_assert(32 % STEP == 0, "an iteration's keys lie in one page");
+    auto fetch_page = [&](int base) __attribute__((always_inline)) -> int {
+        const int kb = __builtin_amdgcn_readfirstlane(base);
+        return (kb < k_end) ? load_uniform(pg.block_table + (size_t)b * pg.max_pages + (kb >> pg.ps_log2)) : -1;
     };
 
     // the GH query rows (query head gkv*GH + g), 8 packed bf16 dims per lane
@@ -310,14 +316,12 @@ decode_small_group_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
         for (int j = 0; j < 8; ++j) o[g][j] = 0.f;
     }
 
-    int pg_next[U] = {};
-    if constexpr (PAGED) fetch_pages(k_begin + w * STEP, pg_next);
+    int pg_next = 0;
+    if constexpr (PAGED) pg_next = fetch_page(k_begin + w * STEP);
     for (int base = k_begin + w * STEP; base < k_end; base += DEC_WAVES * STEP) {
         uint4 kr[U], vr[U];
         bool live[U];
-        int pg_cur[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) pg_cur[u] = pg_next[u];
+        const int pg_cur = pg_next;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int key = base + u * KPL + slot;
@@ -325,14 +329,14 @@ decode_small_group_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
             vr[u] = kr[u];
             live[u] = false;
             if (key < k_end) {
-                const size_t r = row_of(key, pg_cur[u], live[u]);
+                const size_t r = row_of(key, pg_cur, live[u]);
                 if (live[u]) {
                     kr[u] = load_stream16(Kl + r);
                     vr[u] = load_stream16(Vl + r);
                 }
             }
         }
-        if constexpr (PAGED) fetch_pages(base + DEC_WAVES * STEP, pg_next);
+        if constexpr (PAGED) pg_next = fetch_page(base + DEC_WAVES * STEP);
         // scores: the dot2 partial sums of every (head, key) first, then the
         // reductions over the key's lanes one step at a time across all of
         // them, so consecutive DPP adds are independent

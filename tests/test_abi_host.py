@@ -314,10 +314,10 @@ def test_decode_split_plan_grouped():
     # small-group kernel (groups of 2 and 3; of 4 from 64 (batch, cache head)
     # pairs): about 512 workgroups, chunks of 256 keys or more, at most 32
     assert fa.fa_decode_num_splits(64, 32, 8, 8192, 128) == 1
-    # the paged call aims at about 1024 workgroups there (2 splits), and the
-    # automatic workspace has room for them
+    # the paged call makes the same choice, and the automatic workspace is
+    # exactly that plan's
     assert fa.fa_decode_workspace_bytes(64, 32, 8, 8192, 128, 0) == \
-        fa.fa_decode_workspace_bytes(64, 32, 8, 8192, 128, 2)
+        fa.fa_decode_workspace_bytes(64, 32, 8, 8192, 128, 1)
     assert fa.fa_decode_num_splits(16, 32, 8, 8192, 128) == 4
     assert fa.fa_decode_num_splits(4, 24, 8, 8192, 128) == 16
     assert fa.fa_decode_num_splits(1, 32, 16, 8192, 128) == 32
