@@ -23,7 +23,8 @@
 //
 // Phase 2 (merge kernel): M = max_s lse_s, lse = M + ln sum_s exp(lse_s - M),
 // O = sum_s exp(lse_s - lse) o_s, the online-softmax rescaling applied to
-// whole chunks.
+// whole chunks.  With one chunk (S = 1) that is the identity, so the phase-1
+// kernels write O and the LSE themselves and the merge is not launched.
 #include "fa_common.hpp"
 #include "fa_internal.hpp"
 
@@ -62,7 +63,8 @@ template <int D, bool PAGED>
 __global__ void __launch_bounds__(DEC_THREADS)
 decode_split_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ Kc,
                     const __bf16* __restrict__ Vc, float* __restrict__ Opart,
-                    float* __restrict__ LSEpart, int G, int L, int S, int chunk, float c, Paging pg) {
+                    float* __restrict__ LSEpart, __bf16* __restrict__ Ofin, float* __restrict__ LSEfin,
+                    int G, int L, int S, int chunk, float c, Paging pg) {
     constexpr int LPK = D / 8;           // lanes per key (8 bf16 each)
     constexpr int KPL = 64 / LPK;        // keys covered by one wave-wide load
     constexpr int U = DEC_UNROLL;
@@ -219,9 +221,16 @@ decode_split_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ Kc,
             const float ob[1] = {sh_o[ww][tid]};
             merge_state<1>(mm, ll, oo, sh_m[ww], sh_l[ww], ob);
         }
-        const size_t pidx = (size_t)bh * S + s;
-        Opart[pidx * D + tid] = (ll > 0.f) ? oo[0] / ll : 0.f;
-        if (tid == 0) LSEpart[pidx] = (ll > 0.f) ? (mm + __log2f(ll)) * kLn2 : -INFINITY;
+        const float ov = (ll > 0.f) ? oo[0] / ll : 0.f;
+        const float lv = (ll > 0.f) ? (mm + __log2f(ll)) * kLn2 : -INFINITY;
+        if (Ofin != nullptr) {          // one split: the final row
+            Ofin[(size_t)bh * D + tid] = (__bf16)ov;
+            if (tid == 0 && LSEfin != nullptr) LSEfin[bh] = lv;
+        } else {
+            const size_t pidx = (size_t)bh * S + s;
+            Opart[pidx * D + tid] = ov;
+            if (tid == 0) LSEpart[pidx] = lv;
+        }
     }
 }
 
@@ -250,7 +259,8 @@ template <int D, int GH, bool PAGED>
 __global__ void __launch_bounds__(DEC_THREADS)
 decode_small_group_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ Kc,
                           const __bf16* __restrict__ Vc, float* __restrict__ Opart,
-                          float* __restrict__ LSEpart, int L, int S, int chunk, float c, Paging pg) {
+                          float* __restrict__ LSEpart, __bf16* __restrict__ Ofin, float* __restrict__ LSEfin,
+                          int L, int S, int chunk, float c, Paging pg) {
     constexpr int LPK = D / 8;
     constexpr int KPL = 64 / LPK;
     constexpr int U = DEC_UNROLL;
@@ -449,9 +459,17 @@ decode_small_group_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
             const float ob[1] = {sh_o[ww][g][dd]};
             merge_state<1>(mm, ll, oo, sh_m[ww][g], sh_l[ww][g], ob);
         }
-        const size_t pidx = ((size_t)gkv * GH + g) * S + s;
-        Opart[pidx * D + dd] = (ll > 0.f) ? oo[0] / ll : 0.f;
-        if (dd == 0) LSEpart[pidx] = (ll > 0.f) ? (mm + __log2f(ll)) * kLn2 : -INFINITY;
+        const size_t hq = (size_t)gkv * GH + g;        // query head (b*H + h)
+        const float ov = (ll > 0.f) ? oo[0] / ll : 0.f;
+        const float lv = (ll > 0.f) ? (mm + __log2f(ll)) * kLn2 : -INFINITY;
+        if (Ofin != nullptr) {          // one split: the final row
+            Ofin[hq * D + dd] = (__bf16)ov;
+            if (dd == 0 && LSEfin != nullptr) LSEfin[hq] = lv;
+        } else {
+            const size_t pidx = hq * S + s;
+            Opart[pidx * D + dd] = ov;
+            if (dd == 0) LSEpart[pidx] = lv;
+        }
     }
 }
 
@@ -483,7 +501,8 @@ template <int D, bool PAGED>
 __global__ void __launch_bounds__(64 * dg_waves<D>())
 decode_group_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ Kc,
                     const __bf16* __restrict__ Vc, float* __restrict__ Opart,
-                    float* __restrict__ LSEpart, int G, int L, int S, int chunk, int units,
+                    float* __restrict__ LSEpart, __bf16* __restrict__ Ofin, float* __restrict__ LSEfin,
+                    int G, int L, int S, int chunk, int units,
                     float c /* scale * log2(e) */, Paging pg) {
     constexpr int ROWB = 2 * D;             // bytes per cached row
     constexpr int CPR = D / 8;              // 16-byte chunks per row
@@ -666,17 +685,31 @@ decode_group_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ Kc,
     // normalised partial of each real head of the group
     const float l_tot = xor32_sum(l_run);
     if (l32 < G) {
-        const size_t pidx = ((size_t)gkv * G + l32) * S + s;
+        const size_t hq = (size_t)gkv * G + l32;     // query head (b*H + h)
         const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
-        float* orow = Opart + pidx * D;
+        const float lv = (l_tot > 0.f) ? m_ref * kLn2 + __logf(l_tot) : -INFINITY;
+        if (Ofin != nullptr) {          // one split: the final row
+            __bf16* orow = Ofin + hq * D;
 #pragma unroll
-        for (int mb = 0; mb < D / 32; ++mb)
+            for (int mb = 0; mb < D / 32; ++mb)
 #pragma unroll
-            for (int rb = 0; rb < 4; ++rb)
-                *reinterpret_cast<float4*>(orow + 32 * mb + 8 * rb + 4 * g) =
-                    make_float4(oacc[mb][4 * rb] * inv, oacc[mb][4 * rb + 1] * inv,
-                                oacc[mb][4 * rb + 2] * inv, oacc[mb][4 * rb + 3] * inv);
-        if (g == 0) LSEpart[pidx] = (l_tot > 0.f) ? m_ref * kLn2 + __logf(l_tot) : -INFINITY;
+                for (int rb = 0; rb < 4; ++rb)
+                    *reinterpret_cast<uint2*>(orow + 32 * mb + 8 * rb + 4 * g) =
+                        make_uint2(pack_bf16x2(oacc[mb][4 * rb] * inv, oacc[mb][4 * rb + 1] * inv),
+                                   pack_bf16x2(oacc[mb][4 * rb + 2] * inv, oacc[mb][4 * rb + 3] * inv));
+            if (g == 0 && LSEfin != nullptr) LSEfin[hq] = lv;
+        } else {
+            const size_t pidx = hq * S + s;
+            float* orow = Opart + pidx * D;
+#pragma unroll
+            for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+                for (int rb = 0; rb < 4; ++rb)
+                    *reinterpret_cast<float4*>(orow + 32 * mb + 8 * rb + 4 * g) =
+                        make_float4(oacc[mb][4 * rb] * inv, oacc[mb][4 * rb + 1] * inv,
+                                    oacc[mb][4 * rb + 2] * inv, oacc[mb][4 * rb + 3] * inv);
+            if (g == 0) LSEpart[pidx] = lv;
+        }
     }
 }
 
@@ -754,34 +787,42 @@ hipError_t launch_d(const DecodeArgs& a) {
     const int BH = a.B * a.H;
     const int G = a.H / a.Hkv;
     hipStream_t st = (hipStream_t)a.stream;
+    // With one split each partial already is the final row: the kernels
+    // write O (bf16) and the LSE themselves -- the same values the merge
+    // would (its weight for the only split is e^0 = 1) -- and the merge
+    // launch is skipped.
+    const bool one = a.splits == 1;
+    __bf16* ofin = one ? (__bf16*)a.o : nullptr;
+    float* lfin = one ? a.lse : nullptr;
     if (decode_small_group(a.B, a.H, a.Hkv) != 0) {
         const dim3 grid((unsigned)(a.B * a.Hkv * a.splits));
         if (G == 2) {
             hipLaunchKernelGGL((decode_small_group_kernel<D, 2, PAGED>), grid, dim3(DEC_THREADS), 0, st,
                                (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, a.o_part,
-                               a.lse_part, a.L, a.splits, a.chunk, a.scale * kLog2e, a.paging);
+                               a.lse_part, ofin, lfin, a.L, a.splits, a.chunk, a.scale * kLog2e, a.paging);
         } else if (G == 3) {
             hipLaunchKernelGGL((decode_small_group_kernel<D, 3, PAGED>), grid, dim3(DEC_THREADS), 0, st,
                                (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, a.o_part,
-                               a.lse_part, a.L, a.splits, a.chunk, a.scale * kLog2e, a.paging);
+                               a.lse_part, ofin, lfin, a.L, a.splits, a.chunk, a.scale * kLog2e, a.paging);
         } else {
             hipLaunchKernelGGL((decode_small_group_kernel<D, 4, PAGED>), grid, dim3(DEC_THREADS), 0, st,
                                (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, a.o_part,
-                               a.lse_part, a.L, a.splits, a.chunk, a.scale * kLog2e, a.paging);
+                               a.lse_part, ofin, lfin, a.L, a.splits, a.chunk, a.scale * kLog2e, a.paging);
         }
     } else if (decode_group_path(a.B, a.H, a.Hkv)) {
         const int units = a.B * a.Hkv * a.splits;
         constexpr int WV = dg_waves<D>();
         hipLaunchKernelGGL((decode_group_kernel<D, PAGED>), dim3((unsigned)((units + WV - 1) / WV)),
                            dim3(64 * WV), 0, st, (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v,
-                           a.o_part, a.lse_part, G, a.L, a.splits, a.chunk, units, a.scale * kLog2e, a.paging);
+                           a.o_part, a.lse_part, ofin, lfin, G, a.L, a.splits, a.chunk, units, a.scale * kLog2e,
+                           a.paging);
     } else {
         hipLaunchKernelGGL((decode_split_kernel<D, PAGED>), dim3((unsigned)(BH * a.splits)), dim3(DEC_THREADS), 0,
                            st, (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, a.o_part, a.lse_part,
-                           G, a.L, a.splits, a.chunk, a.scale * kLog2e, a.paging);
+                           ofin, lfin, G, a.L, a.splits, a.chunk, a.scale * kLog2e, a.paging);
     }
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (e != hipSuccess || one) return e;
     hipLaunchKernelGGL((decode_merge_kernel<D>), dim3((unsigned)((BH + DEC_WAVES - 1) / DEC_WAVES)),
                        dim3(DEC_THREADS), 0, st, a.o_part, a.lse_part, (__bf16*)a.o, a.lse, BH, a.splits);
     return hipGetLastError();
