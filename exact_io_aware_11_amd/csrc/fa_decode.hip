@@ -23,8 +23,9 @@
 //
 // Phase 2 (merge kernel): M = max_s lse_s, lse = M + ln sum_s exp(lse_s - M),
 // O = sum_s exp(lse_s - lse) o_s, the online-softmax rescaling applied to
-// whole chunks.  With one chunk (S = 1) that is the identity, so the phase-1
-// kernels write O and the LSE themselves and the merge is not launched.
+// whole chunks.  With one chunk (S = 1) that is the identity, so the per-head
+// and small-group kernels then write O and the LSE themselves and the merge
+// is not launched.
 #include "fa_common.hpp"
 #include "fa_internal.hpp"
 
@@ -501,8 +502,7 @@ template <int D, bool PAGED>
 __global__ void __launch_bounds__(64 * dg_waves<D>())
 decode_group_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ Kc,
                     const __bf16* __restrict__ Vc, float* __restrict__ Opart,
-                    float* __restrict__ LSEpart, __bf16* __restrict__ Ofin, float* __restrict__ LSEfin,
-                    int G, int L, int S, int chunk, int units,
+                    float* __restrict__ LSEpart, int G, int L, int S, int chunk, int units,
                     float c /* scale * log2(e) */, Paging pg) {
     constexpr int ROWB = 2 * D;             // bytes per cached row
     constexpr int CPR = D / 8;              // 16-byte chunks per row
@@ -685,31 +685,17 @@ decode_group_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ Kc,
     // normalised partial of each real head of the group
     const float l_tot = xor32_sum(l_run);
     if (l32 < G) {
-        const size_t hq = (size_t)gkv * G + l32;     // query head (b*H + h)
+        const size_t pidx = ((size_t)gkv * G + l32) * S + s;
         const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
-        const float lv = (l_tot > 0.f) ? m_ref * kLn2 + __logf(l_tot) : -INFINITY;
-        if (Ofin != nullptr) {          // one split: the final row
-            __bf16* orow = Ofin + hq * D;
+        float* orow = Opart + pidx * D;
 #pragma unroll
-            for (int mb = 0; mb < D / 32; ++mb)
+        for (int mb = 0; mb < D / 32; ++mb)
 #pragma unroll
-                for (int rb = 0; rb < 4; ++rb)
-                    *reinterpret_cast<uint2*>(orow + 32 * mb + 8 * rb + 4 * g) =
-                        make_uint2(pack_bf16x2(oacc[mb][4 * rb] * inv, oacc[mb][4 * rb + 1] * inv),
-                                   pack_bf16x2(oacc[mb][4 * rb + 2] * inv, oacc[mb][4 * rb + 3] * inv));
-            if (g == 0 && LSEfin != nullptr) LSEfin[hq] = lv;
-        } else {
-            const size_t pidx = hq * S + s;
-            float* orow = Opart + pidx * D;
-#pragma unroll
-            for (int mb = 0; mb < D / 32; ++mb)
-#pragma unroll
-                for (int rb = 0; rb < 4; ++rb)
-                    *reinterpret_cast<float4*>(orow + 32 * mb + 8 * rb + 4 * g) =
-                        make_float4(oacc[mb][4 * rb] * inv, oacc[mb][4 * rb + 1] * inv,
-                                    oacc[mb][4 * rb + 2] * inv, oacc[mb][4 * rb + 3] * inv);
-            if (g == 0) LSEpart[pidx] = lv;
-        }
+            for (int rb = 0; rb < 4; ++rb)
+                *reinterpret_cast<float4*>(orow + 32 * mb + 8 * rb + 4 * g) =
+                    make_float4(oacc[mb][4 * rb] * inv, oacc[mb][4 * rb + 1] * inv,
+                                oacc[mb][4 * rb + 2] * inv, oacc[mb][4 * rb + 3] * inv);
+        if (g == 0) LSEpart[pidx] = (l_tot > 0.f) ? m_ref * kLn2 + __logf(l_tot) : -INFINITY;
     }
 }
 
@@ -787,13 +773,15 @@ hipError_t launch_d(const DecodeArgs& a) {
     const int BH = a.B * a.H;
     const int G = a.H / a.Hkv;
     hipStream_t st = (hipStream_t)a.stream;
-    // With one split each partial already is the final row: the kernels
-    // write O (bf16) and the LSE themselves -- the same values the merge
-    // would (its weight for the only split is e^0 = 1) -- and the merge
-    // launch is skipped.
-    const bool one = a.splits == 1;
-    __bf16* ofin = one ? (__bf16*)a.o : nullptr;
-    float* lfin = one ? a.lse : nullptr;
+    // With one split each partial already is the final row: the per-head
+    // and small-group kernels then write O (bf16) and the LSE themselves --
+    // the same values the merge would (its weight for the only split is
+    // e^0 = 1) -- and the merge launch is skipped.  The MFMA grouped kernel,
+    // which serves small batches with many splits, always writes partials
+    // (a direct-store path there measured 3% slower at batch 1).
+    bool direct = a.splits == 1;
+    __bf16* ofin = direct ? (__bf16*)a.o : nullptr;
+    float* lfin = direct ? a.lse : nullptr;
     if (decode_small_group(a.B, a.H, a.Hkv) != 0) {
         const dim3 grid((unsigned)(a.B * a.Hkv * a.splits));
         if (G == 2) {
@@ -814,15 +802,15 @@ hipError_t launch_d(const DecodeArgs& a) {
         constexpr int WV = dg_waves<D>();
         hipLaunchKernelGGL((decode_group_kernel<D, PAGED>), dim3((unsigned)((units + WV - 1) / WV)),
                            dim3(64 * WV), 0, st, (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v,
-                           a.o_part, a.lse_part, ofin, lfin, G, a.L, a.splits, a.chunk, units, a.scale * kLog2e,
-                           a.paging);
+                           a.o_part, a.lse_part, G, a.L, a.splits, a.chunk, units, a.scale * kLog2e, a.paging);
+        direct = false;
     } else {
         hipLaunchKernelGGL((decode_split_kernel<D, PAGED>), dim3((unsigned)(BH * a.splits)), dim3(DEC_THREADS), 0,
                            st, (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, a.o_part, a.lse_part,
                            ofin, lfin, G, a.L, a.splits, a.chunk, a.scale * kLog2e, a.paging);
     }
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess || one) return e;
+    if (e != hipSuccess || direct) return e;
     hipLaunchKernelGGL((decode_merge_kernel<D>), dim3((unsigned)((BH + DEC_WAVES - 1) / DEC_WAVES)),
                        dim3(DEC_THREADS), 0, st, a.o_part, a.lse_part, (__bf16*)a.o, a.lse, BH, a.splits);
     return hipGetLastError();
