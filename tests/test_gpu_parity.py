@@ -106,6 +106,10 @@ SMALL = [
     (1, 1, 1, 64, "fp32", False),
     (1, 2, 33, 128, "fp32", True),
     (2, 1, 129, 64, "fp32", True),
+    # fp32: the four waves of a 32-row workgroup take every fourth key tile,
+    # so these give each wave two or three tiles (the prefetch path)
+    (1, 2, 300, 64, "fp32", False),
+    (1, 1, 257, 128, "fp32", False),
     (1, 1, 300, 128, "fp32", False),
     # head dim 256 (bf16 only)
     (1, 2, 300, 256, "bf16", True),
