@@ -376,6 +376,34 @@ def test_decode_split_counts_agree(L, d):
         assert np.all(np.abs(o - o0) <= np.maximum(np.abs(o), np.abs(o0)) * 2.0 ** -7 + 1e-6)
 
 
+@pytest.mark.parametrize("B,H,Hkv,L,d", [
+    (2, 4, 4, 300, 128),     # per-head kernel
+    (2, 16, 8, 500, 64),     # small-group kernel, groups of 2
+    (16, 32, 8, 700, 128),   # small-group kernel, groups of 4
+    (2, 16, 2, 600, 128),    # MFMA grouped kernel (groups of 8), which keeps the merge
+])
+def test_decode_one_split_without_lse(B, H, Hkv, L, d):
+    # With one split the per-head and small-group kernels write O and the LSE
+    # themselves (no merge launch).  A null LSE pointer must leave O as it is
+    # with an LSE, and both must meet the oracle.
+    fa = _fa()
+    q, kc, vc = W.make_gqa(B, H, Hkv, 1, d, "bf16", seed=3300 + L, Nk=L, device=DEV)
+    scale = 1 / math.sqrt(d)
+    say(f"fa_decode one split B{B} H{H} Hkv{Hkv} L{L} d{d}, with and without LSE")
+    o_ref, lse_ref = fa.decode(q, kc, vc, scale=scale, num_splits=1)
+    o = torch.full_like(o_ref, float("nan"))
+    nb = fa.fa_decode_workspace_bytes(B, H, Hkv, L, d, 1)
+    ws = torch.empty((nb,), dtype=torch.uint8, device=DEV)
+    st = fa.fa_decode(q.data_ptr(), kc.data_ptr(), vc.data_ptr(), o.data_ptr(), 0, ws.data_ptr(), nb,
+                      B, H, Hkv, L, d, fa.FA_BF16, 1, scale, torch.cuda.current_stream().cuda_stream)
+    assert st == fa.FA_OK, fa.fa_status_string(st)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_ref)
+    o64, l64 = ref_decode(to64(q), to64(kc), to64(vc), scale)
+    assert_bf16_close(to64(o_ref), o64, "O")
+    assert_lse_close(to64(lse_ref), l64, "LSE")
+
+
 def test_decode_deterministic():
     fa = _fa()
     q, kc, vc = W.make_custom(4, 8, 1, 128, "bf16", seed=3100, Nk=3000, device=DEV)
