@@ -613,6 +613,11 @@ GQA_DEC = [
     (2, 8, 1, 777, 64),
     (1, 32, 8, 4097, 128),
     (2, 6, 3, 1, 128),
+    # caches shorter than one 32-key tile: the MFMA grouped kernel (groups of
+    # 8; groups of 4 over fewer than 64 pairs) and the small-group kernel
+    (1, 8, 1, 1, 128),
+    (2, 16, 4, 31, 64),
+    (16, 32, 8, 17, 128),
     (2, 4, 4, 300, 64),
     (1, 32, 1, 2049, 128),
     (1, 64, 1, 500, 64),
