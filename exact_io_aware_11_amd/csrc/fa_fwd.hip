@@ -87,10 +87,20 @@ fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
     const float* Kh = K + kvoff;
     const float* Vh = V + kvoff;
 
+    // K-step ks of S^T = K Q^T takes dims ks (K-slot 0, lanes 0-31) and
+    // ks + D/2 (K-slot 1, lanes 32-63): each lane holds one contiguous half
+    // of its query row, loaded 16 bytes at a time
     const int qrow = q0 + l32;
     float qf[D / 2];
 #pragma unroll
-    for (int ks = 0; ks < D / 2; ++ks) qf[ks] = (qrow < N) ? Qh[(size_t)qrow * D + 2 * ks + g] : 0.f;
+    for (int j = 0; j < D / 8; ++j) {
+        float4 u = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (qrow < N) u = *reinterpret_cast<const float4*>(Qh + (size_t)qrow * D + (D / 2) * g + 4 * j);
+        qf[4 * j] = u.x;
+        qf[4 * j + 1] = u.y;
+        qf[4 * j + 2] = u.z;
+        qf[4 * j + 3] = u.w;
+    }
 
     f32x16 oacc[D / 32];
 #pragma unroll
@@ -135,7 +145,7 @@ fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
 
         f32x16 s = zero16();
 #pragma unroll
-        for (int ks = 0; ks < D / 2; ++ks) s = mfma_f32(Ks[l32 * KS + 2 * ks + g], qf[ks], s);
+        for (int ks = 0; ks < D / 2; ++ks) s = mfma_f32(Ks[l32 * KS + ks + (D / 2) * g], qf[ks], s);
 
         if ((kv0 + BC > N) || (CAUSAL && kv0 + BC - 1 > q0)) {
 #pragma unroll
