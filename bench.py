@@ -262,7 +262,7 @@ def configs_measure(torch, fa, W, dev):
                  "us_min": round(st["min_ms"] * 1e3, 2), "calls": st["calls"],
                  "tflops": round(fl / (st["median_ms"] * 1e-3) / 1e12, 3),
                  "note": "latency-bound: 4.19 MFLOP on four workgroups of 32 query rows, whose four waves take "
-                         "one 32-key tile each and merge through LDS (the kernel itself takes ~8.7 us, about 2 us "
+                         "one 32-key tile each and merge through LDS (the kernel itself takes ~6.5 us, about 2 us "
                          "of it the 64 fp32 MFMAs per wave, the rest loads, the merge and the dispatch); the fp32 "
                          f"matrix peak is {PEAK_FP32_MATRIX_TFLOPS} TFLOP/s, for information only"}
     log(f"C1 {out['C1']['workload']}: {out['C1']['us']} us")
